@@ -1,0 +1,305 @@
+"""Pins for the fp64 attention oracle.
+
+Checks form A (materialised softmax) against a library routine (torch's
+fp64 CPU scaled_dot_product_attention) and closed forms, checks form B
+(online, blockwise, any block order) against form A, and checks the ring
+share and the sink + window decode against brute-force masked attention.
+"""
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import attention as A
+from oracle import rope as R
+from yarn_rope_blockwise_amd import synth
+from yarn_rope_blockwise_amd import workloads as W
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_full_matches_torch_sdpa_fp64():
+    # Library routine: softmax(QK^T * scale) V with a causal mask.
+    S, D = 97, 64
+    q, k, v = _rand((S, D), 1), _rand((S, D), 2), _rand((S, D), 3)
+    scale = 0.37
+    pos = np.arange(S)
+    for causal in (True, False):
+        vis = A.causal_visible if causal else A.all_visible
+        o = A.attention_full(q, k, v, scale, pos, pos, vis, row_chunk=13)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+            is_causal=causal, scale=scale)[0].numpy()
+        np.testing.assert_allclose(o, ref, atol=1e-13)
+
+
+def test_full_with_offsets_matches_sdpa_bool_mask():
+    Sq, Sk, D = 40, 70, 32
+    q, k, v = _rand((Sq, D), 4), _rand((Sk, D), 5), _rand((Sk, D), 6)
+    q_pos = 50 + np.arange(Sq)
+    k_pos = 20 + np.arange(Sk)
+    o = A.attention_full(q, k, v, 0.2, q_pos, k_pos)
+    mask = torch.from_numpy(k_pos[None, :] <= q_pos[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=mask[None], scale=0.2)[0].numpy()
+    np.testing.assert_allclose(o, ref, atol=1e-13)
+
+
+def test_first_row_returns_first_value():
+    q, k, v = _rand((16, 64), 7), _rand((16, 64), 8), _rand((16, 64), 9)
+    o = A.attention_full(q, k, v, 0.125, np.arange(16), np.arange(16))
+    assert np.array_equal(o[0], v[0])
+
+
+def test_zero_query_is_mean_of_visible_values():
+    k, v = _rand((30, 64), 10), _rand((30, 64), 11)
+    q = np.zeros((30, 64))
+    o = A.attention_full(q, k, v, 0.125, np.arange(30), np.arange(30))
+    expect = np.cumsum(v, axis=0) / np.arange(1, 31)[:, None]
+    np.testing.assert_allclose(o, expect, atol=1e-14)
+
+
+def test_fully_masked_row_is_zero():
+    q, k, v = _rand((4, 8), 1), _rand((4, 8), 2), _rand((4, 8), 3)
+    o, m, l = A.attention_full(q, k, v, 1.0, np.arange(4), 10 + np.arange(4), return_state=True)
+    assert np.all(o == 0) and np.all(np.isneginf(m)) and np.all(l == 0)
+    ob, mb, lb = A.attention_online(q, k, v, 1.0, np.arange(4), 10 + np.arange(4), block=2,
+                                    return_state=True)
+    assert np.all(ob == 0) and np.all(np.isneginf(mb)) and np.all(lb == 0)
+
+
+@settings(max_examples=30, deadline=None)
+@given(S=st.integers(1, 200), block=st.integers(1, 80), causal=st.booleans(),
+       seed=st.integers(0, 1000), shuffle=st.booleans())
+def test_online_equals_full(S, block, causal, seed, shuffle):
+    q, k, v = _rand((S, 32), seed), _rand((S, 32), seed + 1), _rand((S, 32), seed + 2)
+    pos = np.arange(S)
+    vis = A.causal_visible if causal else A.all_visible
+    oa, ma, la = A.attention_full(q, k, v, 0.3, pos, pos, vis, return_state=True)
+    nb = (S + block - 1) // block
+    order = np.random.default_rng(seed).permutation(nb) if shuffle else None
+    ob, mb, lb = A.attention_online(q, k, v, 0.3, pos, pos, block, order, vis, return_state=True)
+    np.testing.assert_allclose(ob, oa, atol=1e-12)
+    np.testing.assert_allclose(mb, ma, atol=1e-12)
+    np.testing.assert_allclose(lb, la, rtol=1e-12)
+
+
+def test_tiny_config_blockwise():
+    # The tiny fp32 workload: YaRN s=4 from 128, d=64, S=512, KV block 64.
+    w = W.TINY
+    (qf, _), (kf, _), (vf, _) = synth.qkv((1, w.seq, 1, w.head_dim), (1, w.seq, 1, w.head_dim), "f32")
+    th = R.inv_freq(w.rope.kind, w.rope.head_dim, w.rope.base, w.rope.scale, w.rope.orig_ctx)
+    sc = R.softmax_scale(w.rope.kind, w.rope.scale, w.head_dim)
+    o_full = A.prefill(qf, kf, vf, th, sc)[0, :, 0]
+    pos = np.arange(w.seq)
+    qr = R.rotate_bshd(qf, th, pos)[0, :, 0]
+    kr = R.rotate_bshd(kf, th, pos)[0, :, 0]
+    o_blk = A.attention_online(qr, kr, vf[0, :, 0], sc, pos, pos, block=w.kv_block)
+    np.testing.assert_allclose(o_blk, o_full, atol=1e-12)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    B, S, Hq, Hkv, D = 2, 33, 8, 2, 32
+    q = _rand((B, S, Hq, D), 20)
+    k = _rand((B, S, Hkv, D), 21)
+    v = _rand((B, S, Hkv, D), 22)
+    th = R.inv_freq(R.NTK, D, 1e4, 4.0)
+    o = A.prefill(q, k, v, th, 0.2)
+    kr = np.repeat(k, Hq // Hkv, axis=2)
+    vr = np.repeat(v, Hq // Hkv, axis=2)
+    o2 = A.prefill(q, kr, vr, th, 0.2)
+    np.testing.assert_allclose(o, o2, atol=0)
+    # the grouping is contiguous: q head h reads kv head h // 4
+    o3 = A.prefill(q[:, :, 5:6], k[:, :, 1:2], v[:, :, 1:2], th, 0.2)
+    np.testing.assert_allclose(o[:, :, 5:6], o3, atol=0)
+
+
+def _ring_inputs(n_blocks=4, blk=24, H=2, D=32, seed=30):
+    S = n_blocks * blk
+    q = _rand((1, S, H, D), seed)
+    k = _rand((1, S, H, D), seed + 1)
+    v = _rand((1, S, H, D), seed + 2)
+    return q, k, v, S
+
+
+@pytest.mark.parametrize("qi", [0, 1, 3])
+def test_ring_share_equals_causal_full(qi):
+    nb, blk = 4, 24
+    q, k, v, S = _ring_inputs(nb, blk)
+    th = R.inv_freq(R.YARN, 32, 1e4, 4.0, 24)
+    sc = 0.21
+    full = A.prefill(q, k, v, th, sc)
+    kb = [k[:, j * blk:(j + 1) * blk] for j in range(nb)]
+    vb = [v[:, j * blk:(j + 1) * blk] for j in range(nb)]
+    qb = q[:, qi * blk:(qi + 1) * blk]
+    offs = [j * blk for j in range(nb)]
+    ring_order = [(qi - t) % nb for t in range(nb)]
+    o, m, l, acc = A.ring_share(qb, kb, vb, th, sc, qi * blk, offs, order=ring_order)
+    np.testing.assert_allclose(o, full[:, qi * blk:(qi + 1) * blk], atol=1e-12)
+    # block-order invariance
+    o2, m2, l2, _ = A.ring_share(qb, kb, vb, th, sc, qi * blk, offs, order=list(range(nb)))
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(m2, m, atol=1e-12)
+    np.testing.assert_allclose(l2, l, rtol=1e-12)
+
+
+def test_ring_future_blocks_change_nothing_and_resume():
+    nb, blk = 4, 24
+    q, k, v, S = _ring_inputs(nb, blk, seed=40)
+    th = R.inv_freq(R.PI, 32, 1e4, 2.0)
+    sc = 0.19
+    kb = [k[:, j * blk:(j + 1) * blk] for j in range(nb)]
+    vb = [v[:, j * blk:(j + 1) * blk] for j in range(nb)]
+    qi = 1
+    qb = q[:, qi * blk:(qi + 1) * blk]
+    offs = [j * blk for j in range(nb)]
+    o_all, m_all, l_all, acc_all = A.ring_share(qb, kb, vb, th, sc, qi * blk, offs)
+    o_past, m_p, l_p, acc_p = A.ring_share(qb, kb, vb, th, sc, qi * blk, offs, order=[0, 1])
+    assert np.array_equal(o_all, o_past) and np.array_equal(acc_all, acc_p)
+    # resume: stop after block 1, snapshot, finish with block 0
+    _, m1, l1, a1 = A.ring_share(qb, kb, vb, th, sc, qi * blk, offs, order=[1], finalize=False)
+    snap = (m1.copy(), l1.copy(), a1.copy())
+    o_res, _, _, _ = A.ring_share(qb, kb, vb, th, sc, qi * blk, offs, order=[0], state_in=snap)
+    o_ref, _, _, _ = A.ring_share(qb, kb, vb, th, sc, qi * blk, offs, order=[1, 0])
+    np.testing.assert_allclose(o_res, o_ref, atol=0)
+
+
+def test_decode_without_eviction_is_last_prefill_row():
+    B, H, D = 3, 4, 64
+    n_sink, window = 4, 60
+    C = n_sink + window
+    th = R.inv_freq(R.PLAIN, D, 1e4)
+    sc = 1 / 8.0
+    q = _rand((B, C, H, D), 50)
+    k = _rand((B, C, H, D), 51)
+    v = _rand((B, C, H, D), 52)
+    lens = np.array([C, 37, 1])
+    kc = np.zeros((B, H, C, D))
+    vc = np.zeros((B, H, C, D))
+    for b in range(B):
+        kc[b] = k[b].transpose(1, 0, 2)
+        vc[b] = v[b].transpose(1, 0, 2)
+    o = A.decode_sink_window(np.stack([q[b, lens[b] - 1] for b in range(B)]), kc, vc, th, sc,
+                             n_sink, window, lens)
+    for b in range(B):
+        L = lens[b]
+        ref = A.prefill(q[b:b + 1, :L], k[b:b + 1, :L], v[b:b + 1, :L], th, sc, rows=[L - 1])
+        np.testing.assert_allclose(o[b], ref[0, 0], atol=1e-12)
+
+
+def _stream_into_cache(k_seq, v_seq, n_sink, window):
+    """Insert tokens 0..T-1 one by one into a sink + ring-buffer window cache."""
+    T, H, D = k_seq.shape
+    C = n_sink + window
+    kc = np.zeros((H, C, D))
+    vc = np.zeros((H, C, D))
+    for t in range(T):
+        slot = t if t < n_sink else n_sink + (t - n_sink) % window
+        kc[:, slot] = k_seq[t]
+        vc[:, slot] = v_seq[t]
+    length = min(T, C)
+    ring_head = 0 if T <= C else (T - n_sink) % window
+    return kc, vc, length, ring_head
+
+
+@pytest.mark.parametrize("T", [5, 40, 64, 65, 100, 203])
+def test_decode_with_eviction_equals_masked_attention(T):
+    # 14cs17 "Sliding Window + Attention Sinks": the cache is the first s
+    # tokens plus the last w; positions are re-indexed inside the cache.
+    n_sink, window, H, D = 4, 60, 2, 32
+    k_seq = _rand((T, H, D), 60 + T)
+    v_seq = _rand((T, H, D), 61 + T)
+    qv = _rand((H, D), 62 + T)
+    kc, vc, L, rh = _stream_into_cache(k_seq, v_seq, n_sink, window)
+    th = R.inv_freq(R.YARN, D, 1e4, 4.0, 16)
+    sc = 0.17
+    o = A.decode_sink_window(qv[None], kc[None], vc[None], th, sc, n_sink, window, [L], [rh])[0]
+    # brute force over the logical sequence
+    t = T - 1
+    logical = np.arange(T)
+    keep = A.sink_window_visible(n_sink, window)(np.array([t]), logical)[0]
+    kept = logical[keep]
+    assert len(kept) == L
+    new_pos = np.arange(len(kept))           # re-indexed: sinks 0..s-1, window after
+    ck, sk = R.tables(th, new_pos)
+    cq, sq = R.tables(th, [len(kept) - 1])
+    for h in range(H):
+        kk = R.rotate_half(k_seq[kept, h], ck, sk)
+        qq = R.rotate_half(qv[h][None], cq, sq)
+        lg = sc * (qq @ kk.T)[0]
+        p = np.exp(lg - lg.max())
+        ref = (p / p.sum()) @ v_seq[kept, h]
+        np.testing.assert_allclose(o[h], ref, atol=1e-12)
+
+
+def test_decode_ring_head_equals_contiguous_layout():
+    n_sink, window, H, D = 4, 16, 2, 16
+    C = n_sink + window
+    kc = _rand((1, H, C, D), 70)
+    vc = _rand((1, H, C, D), 71)
+    qv = _rand((1, H, D), 72)
+    th = R.inv_freq(R.PLAIN, D, 1e4)
+    for rh in (0, 3, 15):
+        o = A.decode_sink_window(qv, kc, vc, th, 0.3, n_sink, window, [C], [rh])
+        perm = [A.cache_slot(e, n_sink, window, rh) for e in range(C)]
+        o_lin = A.decode_sink_window(qv, kc[:, :, perm], vc[:, :, perm], th, 0.3, n_sink,
+                                     window, [C], [0])
+        np.testing.assert_allclose(o, o_lin, atol=0)
+
+
+def test_decode_empty_cache_is_zero():
+    kc = _rand((2, 1, 8, 16), 1)
+    o = A.decode_sink_window(_rand((2, 1, 16), 2), kc, kc, R.base_inv_freq(16, 1e4), 0.2, 2, 6,
+                             [0, 0])
+    assert np.all(o == 0)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes (on the CPU, in a copy of the oracle's arithmetic): each
+# plausible slip must fail one of the pins above.
+# ---------------------------------------------------------------------------
+
+def test_planted_sign_slip_fails_complex_pin(monkeypatch):
+    def bad_rotate(x, cos, sin):
+        x = np.asarray(x, np.float64)
+        h = x.shape[-1] // 2
+        a, b = x[..., :h], x[..., h:]
+        return np.concatenate([a * cos + b * sin, a * sin + b * cos], axis=-1)
+    x = _rand((3, 16), 1)
+    th = R.base_inv_freq(16, 1e4)
+    pos = np.array([1, 2, 3])
+    c, s = R.tables(th, pos)
+    z = (x[:, :8] + 1j * x[:, 8:]) * np.exp(1j * np.outer(pos, th))
+    assert not np.allclose(bad_rotate(x, c, s)[:, :8], z.real, atol=1e-6)
+
+
+def test_planted_missing_rescale_fails_online_pin(monkeypatch):
+    orig = A.online_update
+
+    def no_alpha(state, q, kb, vb, scale, qp, kp, visible=A.causal_visible):
+        m, l, acc = state
+        mn, ln, an = orig((m, l, acc), q, kb, vb, scale, qp, kp, visible)
+        # forget to rescale the accumulator by alpha
+        s = scale * (q @ kb.T)
+        s = np.where(visible(qp, kp), s, -np.inf)
+        p = np.where(np.isfinite(mn)[:, None], np.exp(s - mn[:, None]), 0)
+        return mn, ln, acc + p @ vb
+    monkeypatch.setattr(A, "online_update", no_alpha)
+    q, k, v = _rand((50, 16), 1), _rand((50, 16), 2), _rand((50, 16), 3)
+    pos = np.arange(50)
+    ob = A.attention_online(q, k, v, 0.5, pos, pos, block=7)
+    monkeypatch.undo()
+    oa = A.attention_full(q, k, v, 0.5, pos, pos)
+    assert not np.allclose(ob, oa, atol=1e-6)
+
+
+def test_planted_gqa_mapping_slip_fails_pin(monkeypatch):
+    monkeypatch.setattr(A, "kv_head", lambda h, hq, hkv: h % hkv)
+    B, S, Hq, Hkv, D = 1, 9, 4, 2, 8
+    q, k, v = _rand((B, S, Hq, D), 1), _rand((B, S, Hkv, D), 2), _rand((B, S, Hkv, D), 3)
+    o = A.prefill(q, k, v, None, 0.3)
+    o3 = A.prefill(q[:, :, 1:2], k[:, :, 0:1], v[:, :, 0:1], None, 0.3)
+    assert not np.allclose(o[:, :, 1:2], o3)
