@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of the YaRN-RoPE blockwise attention path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
+
+One step is the whole prefill path on the Llama-7B-like 16k workload
+(batch 1, 32 heads, d=128, 16384 tokens, bf16, YaRN s=4 from 4096):
+  rope_tables_build (16384 rows)  ->  rope_apply (K, once)  ->
+  attn_prefill_blockwise (Q rotated on load, causal, online softmax).
+``value`` is algorithmic TFLOP/s of the step (4*d flop per visible
+(query, key) pair, masked pairs not counted) with inputs resident in HBM.
+
+Also measured in the same run: the sink + window decode (64 sequences x 32
+heads, cache 4 + 4096, HBM GB/s), one ring device's share (8 heads, 8 key
+blocks of 32768 at query block 7), and the fp64 oracle on the host cores
+over a bounded sample (``cpu_baseline``).  Per-kernel durations come from
+HIP events recorded on the stream the library launches on.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HBM GB/s"
+
+
+def causal_flops(seq: int, heads: int, d: int, batch: int = 1) -> float:
+    """4*d flop per visible (query, key) pair: QK^T and PV, 2 flop per MAC."""
+    return 4.0 * d * heads * batch * seq * (seq + 1) / 2.0
+
+
+def ring_flops(block: int, heads: int, d: int, full_blocks: int) -> float:
+    return 4.0 * d * heads * (full_blocks * block * block + block * (block + 1) / 2.0)
+
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _upload(shape, seed):
+    import torch
+    from yarn_rope_blockwise_amd import synth
+    _, bits = synth.normal(shape, seed, "bf16")
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def run_prefill(steps: int, warmup: int):
+    import torch
+    from yarn_rope_blockwise_amd import api
+    from yarn_rope_blockwise_amd import workloads as W
+    w = W.LLAMA_16K
+    B, S, H, D = w.batch, w.seq, w.n_q_heads, w.head_dim
+    q = _upload((B, S, H, D), 0)
+    k = _upload((B, S, w.n_kv_heads, D), 1)
+    v = _upload((B, S, w.n_kv_heads, D), 2)
+    cfg = api.RopeConfig.of(w.rope)
+    tab = torch.empty((S, D // 2, 2), dtype=torch.float32, device="cuda")
+    k_rot = torch.empty_like(k)
+    out = torch.empty_like(q)
+    _, _, af = api.rope_tables_build(cfg, S, out=tab)
+    scale = af / np.sqrt(D)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        api.rope_tables_build(cfg, S, out=tab)
+        if ev is not None:
+            ev[1].record()
+        api.rope_apply(k, tab, out=k_rot)
+        if ev is not None:
+            ev[2].record()
+        api.attn_prefill_blockwise(q, k_rot, v, scale, cos_sin=tab, out=out)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(4) for _ in range(steps)]
+    t0, t1 = _events(2)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        step(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    tab_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    rope_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    flops = causal_flops(S, H, D, B)
+    return dict(total_ms=total_ms, ms_per_step=total_ms / steps, tables_ms=tab_ms,
+                rope_k_ms=rope_ms, attn_ms=attn_ms, flops=flops,
+                k_bytes=2 * k.numel() * 2 + S * D * 4)
+
+
+def run_decode(steps: int, warmup: int):
+    import torch
+    from yarn_rope_blockwise_amd import api, synth
+    from yarn_rope_blockwise_amd import workloads as W
+    w = W.SINK_DECODE
+    C = w.n_sink + w.window
+    q = _upload((w.batch, w.n_q_heads, w.head_dim), 0)
+    kc = _upload((w.batch, w.n_kv_heads, C, w.head_dim), 1)
+    vc = _upload((w.batch, w.n_kv_heads, C, w.head_dim), 2)
+    lens = torch.full((w.batch,), C, dtype=torch.int32, device="cuda")
+    rh = torch.from_numpy(synth.ring_heads(w.batch, w.window)).cuda()
+    tab, _, af = api.rope_tables_build(api.RopeConfig.of(w.rope), C)
+    scale = af / np.sqrt(w.head_dim)
+    out = torch.empty_like(q)
+    for _ in range(warmup):
+        api.attn_decode_sink_window(q, kc, vc, lens, w.n_sink, w.window, tab, scale, rh, out)
+    torch.cuda.synchronize()
+    evs = [_events(2) for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        api.attn_decode_sink_window(q, kc, vc, lens, w.n_sink, w.window, tab, scale, rh, out)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    kv_bytes = 2 * kc.numel() * 2
+    other = q.numel() * 2 * 2 + lens.numel() * 4 * 2
+    return dict(ms=ms, bytes=kv_bytes + other, kv_bytes=kv_bytes)
+
+
+def run_ring(steps: int, warmup: int):
+    import torch
+    from yarn_rope_blockwise_amd import api
+    from yarn_rope_blockwise_amd import workloads as W
+    w = W.RING_SHARE
+    blk, nb, H, D = w.block, w.n_blocks, w.n_q_heads, w.head_dim
+    S = blk * nb
+    q = _upload((1, blk, H, D), 0)
+    k = _upload((1, S, w.n_kv_heads, D), 1)
+    v = _upload((1, S, w.n_kv_heads, D), 2)
+    tab, _, af = api.rope_tables_build(api.RopeConfig.of(w.rope), S)
+    scale = af / np.sqrt(D)
+    k = api.rope_apply(k, tab)              # every block rotated once by its owner
+    st = api.AccState.empty(1, blk, H, D)
+    out = torch.empty_like(q)
+    order = W.ring_order(w)
+    qoff = w.q_block_index * blk
+
+    def step(ev=None):
+        for t, j in enumerate(order):
+            if ev is not None:
+                ev[t].record()
+            api.attn_block_accumulate(q, k[:, j * blk:(j + 1) * blk], v[:, j * blk:(j + 1) * blk],
+                                      st, qoff, j * blk, scale, cos_sin=tab, first=(t == 0),
+                                      finalize=(t == nb - 1), out=out)
+        if ev is not None:
+            ev[nb].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(nb + 1) for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    per_call = np.array([[e[t].elapsed_time(e[t + 1]) for t in range(nb)] for e in evs]).mean(0)
+    full = sum(1 for j in order if j < w.q_block_index)
+    return dict(ms=float(per_call.sum()), per_call_ms=[round(float(x), 4) for x in per_call],
+                flops=ring_flops(blk, H, D, full))
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """The fp64 oracle as it stands, on the 16k workload, head by head."""
+    from oracle import attention as A
+    from oracle import rope as R
+    from yarn_rope_blockwise_amd import synth
+    from yarn_rope_blockwise_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = W.LLAMA_16K
+    S, D = w.seq, w.head_dim
+    th = R.inv_freq(w.rope.kind, D, w.rope.base, w.rope.scale, w.rope.orig_ctx)
+    sc = R.softmax_scale(w.rope.kind, w.rope.scale, D)
+    done = 0
+    t0 = time.perf_counter()
+    while done < w.n_q_heads and time.perf_counter() - t0 < budget_s:
+        qv, _ = synth.normal((1, S, 1, D), 1000 + done, "bf16")
+        kv, _ = synth.normal((1, S, 1, D), 2000 + done, "bf16")
+        vv, _ = synth.normal((1, S, 1, D), 3000 + done, "bf16")
+        A.prefill(qv, kv, vv, th, sc)
+        done += 1
+    el = time.perf_counter() - t0
+    flops = causal_flops(S, done, D)
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {w.n_q_heads} heads of the 16k prefill (all 16384 causal rows "
+                      f"each, fp64 numpy), {el:.1f} s wall incl. input generation"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip decode and ring share")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    pre = run_prefill(args.steps, args.warmup)
+    value = pre["flops"] / (pre["ms_per_step"] * 1e-3) / 1e12
+    attn_tflops = pre["flops"] / (pre["attn_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama7b_prefill_16k_yarn4", "batch": 1, "seq": 16384,
+                   "q_heads": 32, "kv_heads": 32, "head_dim": 128, "causal": True,
+                   "rope": "yarn s=4 (4096->16384), base 1e4, alpha 1, beta 32",
+                   "step": "rope_tables_build + rope_apply(K) + attn_prefill_blockwise"},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel", "kernel_ms": round(pre["attn_ms"], 4),
+                     "flops_per_launch": pre["flops"]},
+        "step_breakdown_ms": {"rope_tables_build": round(pre["tables_ms"], 4),
+                              "rope_apply_k": round(pre["rope_k_ms"], 4),
+                              "attn_prefill_blockwise": round(pre["attn_ms"], 4)},
+    }
+    if not args.no_extras:
+        dec = run_decode(max(args.steps, 10), args.warmup)
+        gbs = dec["bytes"] / (dec["ms"] * 1e-3) / 1e9
+        line["decode"] = {"workload": "sink_decode_b64_h32_4p4096", "ms": round(dec["ms"], 4),
+                          "GB/s": round(gbs, 1),
+                          "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                       "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                       "kernel": "decode_bf16_kernel",
+                                       "bytes_per_launch": dec["bytes"]}}
+        ring = run_ring(max(2, args.steps // 5), 1)
+        line["ring_share"] = {"workload": "ring_share_h8_8x32768_yarn8_qblock7",
+                              "ms": round(ring["ms"], 3),
+                              "TFLOP/s": round(ring["flops"] / (ring["ms"] * 1e-3) / 1e12, 2),
+                              "per_call_ms": ring["per_call_ms"]}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+/*
+ * yrb.h -- C ABI of libyrb.so: RoPE under a context-extension rescale, fused
+ * into exact blockwise causal attention, for AMD Instinct MI355X (gfx950).
+ *
+ * Five calls make up the path:
+ *   rope_tables_build        frequencies theta'_i and fp32 cos/sin tables
+ *   rope_apply               rotate half-split pairs of Q or K
+ *   attn_prefill_blockwise   causal softmax attention with RoPE on load
+ *   attn_block_accumulate    fold one external key/value block into a
+ *                            query block's online-softmax state (one ring step)
+ *   attn_decode_sink_window  one query per sequence over a sink + sliding
+ *                            window cache, keys rotated on load
+ *
+ * Conventions shared by every call
+ *  - Every device buffer is owned by the caller.  The library allocates no
+ *    memory, never synchronises and keeps no mutable global state; calls are
+ *    thread-safe.
+ *  - Work is queued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and completes asynchronously.  A kernel fault surfaces at the caller's
+ *    next synchronisation.
+ *  - Arguments are validated on the host before anything is queued: a
+ *    negative return means nothing was launched and nothing was written.
+ *  - Tensors are token-major [batch][token][head][dim] with the dim stride
+ *    equal to 1; the other strides are given in elements.  Base pointers
+ *    must be 16-byte aligned and strides multiples of 16 bytes.
+ *  - dtype: YRB_BF16 (bfloat16 storage, fp32 arithmetic, bf16 MFMA for the
+ *    products) or YRB_F32 (fp32 storage and arithmetic).
+ *  - head_dim must be 64 or 128.
+ *  - Cos/sin tables hold row r for position r (rows start at position 0),
+ *    each row [head_dim/2][2] floats = (cos, sin) of pair i.  `n_table_rows`
+ *    is the number of rows the caller allocated; every position a call uses
+ *    must be below it.
+ *
+ * Sources (cited by page title and section):
+ *  [T] "Context Window Scaling: YaRN, LongRoPE, and RingAttention
+ *      Architectures" (tecvarsity)
+ *  [C] "Context Length Extension" (14cs17 notes)
+ *  [R] "Long-context extension: stretching attention past its training
+ *      window" (root18d)
+ *  [J] jovanaeducation guide a2-tli-4 (sections "YaRN: rescale the
+ *      frequencies", "Attention sinks", "Ring attention")
+ */
+#ifndef YRB_H
+#define YRB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define YRB_OK            0
+#define YRB_EINVAL       -1   /* bad size, pointer, flag or position range */
+#define YRB_EUNSUPPORTED -2   /* head_dim or dtype the kernels do not build */
+#define YRB_EALIGN       -3   /* base pointer or stride not 16-byte aligned */
+#define YRB_EHIP         -4   /* the HIP runtime reported a launch error */
+
+/* Rescale methods. */
+#define YRB_ROPE_PLAIN 0      /* theta_i = base^(-2i/d)                 [T] Sec. 2 */
+#define YRB_ROPE_PI    1      /* theta_i / s  (position m -> m/s)       [T] Sec. 2, [C] "Position Interpolation" */
+#define YRB_ROPE_NTK   2      /* base -> base * s^(d/(d-2))             [C] "NTK-Aware Scaling" (formula not printed; this reading) */
+#define YRB_ROPE_YARN  3      /* per-pair ramp between theta and theta/s, plus temperature  [R], [T] Sec. 3 */
+
+/* Storage types. */
+#define YRB_BF16 0
+#define YRB_F32  1
+
+/* attn_block_accumulate flags. */
+#define YRB_ACC_FIRST    1    /* ignore the incoming state: start from m=-inf, l=0, acc=0 */
+#define YRB_ACC_FINALIZE 2    /* after folding the block, write o = acc / l */
+
+typedef struct yrb_rope_config {
+  int32_t kind;      /* YRB_ROPE_* */
+  int32_t head_dim;  /* d: 64 or 128 */
+  double  base;      /* b > 1 (10000 in the pages' examples) */
+  double  scale;     /* s = L_target / L_train > 0 */
+  int64_t orig_ctx;  /* L_train > 0; used by YaRN's ramp */
+  double  alpha;     /* YaRN ramp: below alpha turns per training window -> full interpolation (1) */
+  double  beta;      /* YaRN ramp: above beta turns -> untouched (32); alpha < beta */
+} yrb_rope_config;
+
+/*
+ * rope_tables_build -- frequencies and cos/sin tables of one rescale.
+ *
+ * theta_i = base^(-2i/d) [T] Sec. 2; theta'_i per method:
+ *   PLAIN theta; PI theta/s; NTK (base*s^(d/(d-2)))^(-2i/d);
+ *   YARN  (1-g_i) theta_i/s + g_i theta_i with r_i = L_train*theta_i/(2 pi),
+ *         g_i = clamp((r_i - alpha)/(beta - alpha), 0, 1)   [R], [T] Sec. 3.
+ * attn_factor = (0.1 ln s + 1)^2 for YARN with s > 1, else 1 ([T] Sec. 3
+ * temperature; the square because both q and k carry the factor).  The
+ * caller folds it into softmax_scale = attn_factor / sqrt(d); the tables
+ * themselves stay unit-norm.
+ *
+ *   cfg            host; validated (kind, head_dim in {64,128}, base > 1,
+ *                  scale > 0, orig_ctx > 0, alpha < beta).
+ *   pos0, n_pos    rows written are positions pos0 .. pos0+n_pos-1, row r
+ *                  holding position pos0+r.  pos0 >= 0, n_pos >= 0.
+ *   cos_sin        device [n_pos][d/2][2] fp32, cos then sin of pos*theta'_i,
+ *                  with the angle formed and reduced in fp64.  May be NULL
+ *                  only when n_pos == 0 (frequencies only, no launch).
+ *   inv_freq_out   host [d/2] fp64 theta'_i, or NULL.
+ *   attn_factor_out host fp64, or NULL.
+ */
+int rope_tables_build(const yrb_rope_config* cfg, int64_t pos0, int64_t n_pos,
+                      float* cos_sin, double* inv_freq_out, double* attn_factor_out,
+                      void* stream);
+
+/*
+ * rope_apply -- rotate every half-split pair (x_i, x_{i+d/2}) of x by the
+ * angle of its token's position ([T] Sec. 2 rotation matrix
+ * [[cos, -sin], [sin, cos]]):
+ *   y_i = x_i c - x_{i+d/2} s,   y_{i+d/2} = x_i s + x_{i+d/2} c.
+ *
+ *   x, y           device [B][S][H][D] of dtype, strides x_strides / y_strides
+ *                  (b, s, h; elements).  y may equal x (in place).
+ *   cos_sin        device table (see conventions), n_table_rows rows.
+ *   pos_ids        device int32 [B][S] (contiguous) giving each token's
+ *                  position, or NULL: token s of every sequence sits at
+ *                  pos_offset + s (then pos_offset + S <= n_table_rows is
+ *                  checked on the host).  With pos_ids, a position outside
+ *                  [0, n_table_rows) is not read: that token's output is NaN.
+ * Arithmetic is fp32; bf16 results are rounded to nearest even.
+ */
+int rope_apply(const void* x, void* y, int32_t dtype,
+               int64_t B, int64_t S, int64_t H, int64_t D,
+               const int64_t x_strides[3], const int64_t y_strides[3],
+               const float* cos_sin, int64_t n_table_rows,
+               int64_t pos_offset, const int32_t* pos_ids, void* stream);
+
+/*
+ * attn_prefill_blockwise -- o = softmax(scale * Q' K'^T + causal mask) V per
+ * (batch, query head), computed blockwise with a running row max and sum so
+ * that the S x S score matrix never exists ([T] Sec. 1 MHSA relation;
+ * [J] "Ring attention" / [C] "Ring Attention": the online softmax of
+ * FlashAttention-style kernels).  Causal: key position <= query position
+ * ([T] FAQ 2); key tiles wholly in a query tile's future are skipped.
+ *
+ *   q              device [B][S][Hq][D], strides[0] = (b, s, h) elements
+ *   k, v           device [B][S][Hkv][D], strides[1], strides[2]
+ *   o              device [B][S][Hq][D], strides[3]; written in dtype
+ *   Hq % Hkv == 0; query head h reads key/value head h / (Hq/Hkv).
+ *   cos_sin        NULL: q is already rotated.  Otherwise q is rotated on load
+ *                  at positions 0..S-1 (S <= n_table_rows).  k must already
+ *                  be rotated (rope_apply at the same positions): keys are
+ *                  reused by every query tile, so they are rotated once, not
+ *                  on every load.
+ *   softmax_scale  multiplier of q.k (attn_factor / sqrt(d)); finite, > 0.
+ *   causal         0 or 1.
+ *   lse            device [B][Hq][S] fp32 or NULL: ln sum_j exp(scale q.k_j)
+ *                  per row (-inf for a row that sees no key).
+ * bf16: products on bf16 MFMA with fp32 accumulation; probabilities are
+ * rounded to bf16 before the P V product; output rounded to nearest even.
+ */
+int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o,
+                           int32_t dtype, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                           int64_t D, const int64_t strides[4][3],
+                           const float* cos_sin, int64_t n_table_rows,
+                           float softmax_scale, int32_t causal, float* lse, void* stream);
+
+/*
+ * attn_block_accumulate -- one ring-attention step on one device: fold the
+ * key/value block that just arrived into the local query block's state
+ * ([J] "Ring attention": each device accumulates its block's contribution
+ * as blocks rotate; [T] Sec. 5; [C] "Ring Attention": combined with online
+ * softmax).
+ *
+ *   q              device [B][Sq][Hq][D]   strides[0], positions q_offset + s
+ *   k_blk, v_blk   device [B][Sk][Hkv][D]  strides[1], strides[2],
+ *                  positions k_offset + t
+ *   k_blk must already be rotated at its positions (a ring device rotates
+ *                  its own block once, before it travels around the ring).
+ *   cos_sin        NULL (q already rotated) or a table covering q_offset+Sq
+ *                  rows: q is then rotated on load.
+ *   o_acc          device [B][Sq][Hq][D] fp32 contiguous: unnormalised sum of
+ *                  exp(scaled logit - m) * v
+ *   m, l           device [B][Hq][Sq] fp32 contiguous: running max of the
+ *                  scaled logits and running sum of exp(logit - m) (natural
+ *                  exp).  A row that has seen no key holds m = -inf, l = 0.
+ *   flags          YRB_ACC_FIRST and/or YRB_ACC_FINALIZE.
+ *   o_out          device [B][Sq][Hq][D] of dtype, o_strides; required iff
+ *                  FINALIZE; rows with l = 0 are written as 0.
+ * With causal = 1 a block wholly in the future of every local query
+ * (k_offset > q_offset + Sq - 1) contributes nothing ([T] FAQ 2); the call
+ * still initialises (FIRST) and finalises (FINALIZE) as asked.  Folding the
+ * blocks in any order gives the same result up to rounding.
+ */
+int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk,
+                          int32_t dtype, int64_t B, int64_t Sq, int64_t Sk,
+                          int64_t Hq, int64_t Hkv, int64_t D,
+                          const int64_t strides[3][3], int64_t q_offset, int64_t k_offset,
+                          const float* cos_sin, int64_t n_table_rows,
+                          float softmax_scale, int32_t causal,
+                          float* o_acc, float* m, float* l, int32_t flags,
+                          void* o_out, const int64_t o_strides[3], void* stream);
+
+/*
+ * attn_decode_sink_window -- one new query per sequence against a cache of
+ * n_sink attention-sink entries plus a sliding window of `window` entries
+ * ([C] "Sliding Window + Attention Sinks": the cache is the first s tokens
+ * and the last w tokens; [J] "Attention sinks").
+ *
+ *   q              device [B][Hq][D], q_strides (b, h)
+ *   k_cache,
+ *   v_cache        device [B][Hkv][C][D], C = n_sink + window, cache_strides
+ *                  (b, h, slot); keys are stored un-rotated.
+ *   o              device [B][Hq][D], o_strides (b, h)
+ *   cache_len      device int32 [B]: entries present, 0 <= len <= C.
+ *   ring_head      device int32 [B] or NULL (= 0): 0 <= head < window.
+ * Entry e < len sits at position e (positions re-indexed inside the cache);
+ * entry e < n_sink is in slot e, a window entry in slot
+ * n_sink + (ring_head + e - n_sink) mod window.  The query sits at position
+ * len - 1 (its own key/value were stored first) and sees every entry.
+ * len = 0 gives o = 0; a len or ring_head out of range gives o = NaN for
+ * that sequence (nothing out of range is read).  Needs n_table_rows >= C.
+ */
+int attn_decode_sink_window(const void* q, const void* k_cache, const void* v_cache, void* o,
+                            int32_t dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                            int64_t n_sink, int64_t window,
+                            const int64_t q_strides[2], const int64_t cache_strides[3],
+                            const int64_t o_strides[2],
+                            const int32_t* cache_len, const int32_t* ring_head,
+                            const float* cos_sin, int64_t n_table_rows,
+                            float softmax_scale, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* yrb_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* YRB_H */

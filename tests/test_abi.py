@@ -1,0 +1,202 @@
+"""Host-side checks of libyrb.so that need no GPU.
+
+* the library loads and exports every function include/yrb.h declares;
+* the fp64 frequencies and temperature computed on the host by the library
+  match the oracle;
+* invalid arguments are rejected with the documented status before anything
+  is launched (these calls never reach the HIP runtime).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import rope as R
+from yarn_rope_blockwise_amd import api
+from yarn_rope_blockwise_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "yrb.h")
+
+OK, EINVAL, EUNSUP, EALIGN = 0, -1, -2, -3
+FAKE = 0x10000          # 16-byte aligned non-null address; never dereferenced
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("rope_tables_build", "rope_apply", "attn_prefill_blockwise",
+              "attn_block_accumulate", "attn_decode_sink_window", "yrb_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = api.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert L.yrb_status_str(0) == b"ok"
+    assert L.yrb_status_str(-2).startswith(b"unsupported")
+
+
+@pytest.mark.parametrize("kind", [R.PLAIN, R.PI, R.NTK, R.YARN])
+@pytest.mark.parametrize("w", [W.TINY.rope, W.LLAMA_16K.rope, W.GQA_32K[W.YARN].rope,
+                               W.RING_SHARE.rope], ids=["tiny", "llama16k", "gqa32k", "ring"])
+def test_host_frequencies_match_oracle(kind, w):
+    cfg = api.RopeConfig(kind, w.head_dim, w.base, w.scale, w.orig_ctx, w.alpha, w.beta)
+    th, af = api.rope_frequencies(cfg)
+    ref = R.inv_freq(kind, w.head_dim, w.base, w.scale, w.orig_ctx, w.alpha, w.beta)
+    np.testing.assert_allclose(th, ref, rtol=1e-14, atol=0)
+    assert af == pytest.approx(R.attn_factor(kind, w.scale), rel=1e-15)
+
+
+def _tables(cfg_kw, **over):
+    kw = dict(kind=3, head_dim=128, base=1e4, scale=4.0, orig_ctx=4096, alpha=1.0, beta=32.0)
+    kw.update(cfg_kw)
+    c = api.YrbRopeConfig(**kw)
+    a = dict(pos0=0, n_pos=0, cos_sin=None)
+    a.update(over)
+    return api.lib().rope_tables_build(ctypes.byref(c), a["pos0"], a["n_pos"], a["cos_sin"],
+                                       None, None, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({}, OK),
+    ({"kind": 7}, EINVAL),
+    ({"head_dim": 96}, EUNSUP),
+    ({"head_dim": 130}, EUNSUP),
+    ({"base": 1.0}, EINVAL),
+    ({"scale": 0.0}, EINVAL),
+    ({"scale": -2.0}, EINVAL),
+    ({"alpha": 32.0, "beta": 1.0}, EINVAL),
+    ({"orig_ctx": 0}, EINVAL),
+])
+def test_rope_tables_config_validation(kw, expect):
+    assert _tables(kw) == expect
+
+
+def test_rope_tables_pointer_validation():
+    assert _tables({}, n_pos=4, cos_sin=None) == EINVAL
+    assert _tables({}, n_pos=4, cos_sin=MISALIGNED) == EALIGN
+    assert _tables({}, n_pos=-1) == EINVAL
+    assert _tables({}, pos0=-5) == EINVAL
+
+
+def _strides(*v):
+    return api._arr(v)
+
+
+def test_rope_apply_validation():
+    L = api.lib()
+    s = _strides(8 * 128 * 32, 128 * 32, 128)
+    args = dict(x=FAKE, y=FAKE, dtype=0, B=1, S=8, H=32, D=128, xs=s, ys=s, cs=FAKE, rows=8,
+                off=0, pos=None, st=None)
+
+    def call(**over):
+        a = dict(args)
+        a.update(over)
+        return L.rope_apply(a["x"], a["y"], a["dtype"], a["B"], a["S"], a["H"], a["D"], a["xs"],
+                            a["ys"], a["cs"], a["rows"], a["off"], a["pos"], a["st"])
+    assert call(D=80) == EUNSUP
+    assert call(dtype=5) == EUNSUP
+    assert call(x=None) == EINVAL
+    assert call(cs=None) == EINVAL
+    assert call(x=MISALIGNED) == EALIGN
+    assert call(xs=_strides(8 * 128 * 32, 128 * 32, 132)) == EALIGN     # 264-byte head stride
+    assert call(rows=7) == EINVAL                                        # table too short
+    assert call(off=1) == EINVAL                                         # off + S > rows
+    assert call(B=-1) == EINVAL
+    assert call(B=0) == OK                                               # nothing to do
+
+
+def _prefill(**over):
+    L = api.lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=0, B=1, S=64, Hq=4, Hkv=2, D=128,
+             strides=_strides(*([64 * 4 * 128, 4 * 128, 128] * 4)), cs=FAKE, rows=64,
+             scale=0.1, causal=1, lse=None)
+    a.update(over)
+    return L.attn_prefill_blockwise(a["q"], a["k"], a["v"], a["o"], a["dtype"], a["B"], a["S"],
+                                    a["Hq"], a["Hkv"], a["D"], a["strides"], a["cs"], a["rows"],
+                                    ctypes.c_float(a["scale"]), a["causal"], a["lse"], None)
+
+
+def test_prefill_validation():
+    assert _prefill(Hq=3) == EINVAL            # Hq % Hkv
+    assert _prefill(Hkv=0) == EINVAL
+    assert _prefill(D=32) == EUNSUP
+    assert _prefill(causal=2) == EINVAL
+    assert _prefill(scale=0.0) == EINVAL
+    assert _prefill(scale=float("nan")) == EINVAL
+    assert _prefill(q=None) == EINVAL
+    assert _prefill(cs=MISALIGNED) == EALIGN
+    assert _prefill(rows=63) == EINVAL         # table shorter than S
+    assert _prefill(o=MISALIGNED) == EALIGN
+    assert _prefill(lse=MISALIGNED) == EALIGN
+    assert _prefill(S=0) == OK
+    assert _prefill(B=0) == OK
+
+
+def _accum(**over):
+    L = api.lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=0, B=1, Sq=64, Sk=64, Hq=2, Hkv=2, D=64,
+             strides=_strides(*([64 * 2 * 64, 2 * 64, 64] * 3)), qo=64, ko=0, cs=FAKE, rows=128,
+             scale=0.1, causal=1, acc=FAKE, m=FAKE, l=FAKE, flags=1, out=None, os=None)
+    a.update(over)
+    return L.attn_block_accumulate(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["Sq"], a["Sk"],
+                                   a["Hq"], a["Hkv"], a["D"], a["strides"], a["qo"], a["ko"],
+                                   a["cs"], a["rows"], ctypes.c_float(a["scale"]),
+                                   a["causal"], a["acc"], a["m"], a["l"], a["flags"], a["out"],
+                                   a["os"], None)
+
+
+def test_accumulate_validation():
+    assert _accum(flags=4) == EINVAL
+    assert _accum(flags=2) == EINVAL            # FINALIZE without output / strides
+    assert _accum(flags=2, out=FAKE) == EINVAL  # no output strides
+    assert _accum(qo=-1) == EINVAL
+    assert _accum(rows=127) == EINVAL           # q_offset + Sq > rows
+    assert _accum(qo=2 ** 31 - 10) == EINVAL    # positions must fit 31 bits
+    assert _accum(m=None) == EINVAL
+    assert _accum(acc=MISALIGNED) == EALIGN
+    assert _accum(cs=MISALIGNED) == EALIGN
+    assert _accum(dtype=2) == EUNSUP
+    assert _accum(Sq=0) == OK
+
+
+def _decode(**over):
+    L = api.lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=0, B=2, Hq=4, Hkv=4, D=128, sink=4, win=60,
+             qs=_strides(512, 128), cs=_strides(4 * 64 * 128, 64 * 128, 128),
+             os=_strides(512, 128), len=FAKE, rh=None, tab=FAKE, rows=64, scale=0.1)
+    a.update(over)
+    return L.attn_decode_sink_window(a["q"], a["k"], a["v"], a["o"], a["dtype"], a["B"], a["Hq"],
+                                     a["Hkv"], a["D"], a["sink"], a["win"], a["qs"], a["cs"],
+                                     a["os"], a["len"], a["rh"], a["tab"], a["rows"],
+                                     ctypes.c_float(a["scale"]), None)
+
+
+def test_decode_validation():
+    assert _decode(dtype=1) == EUNSUP           # the decode path is bf16
+    assert _decode(Hq=12, Hkv=4) == EUNSUP      # group of 3 query heads
+    assert _decode(Hq=6, Hkv=4) == EINVAL
+    assert _decode(win=0) == EINVAL
+    assert _decode(sink=-1) == EINVAL
+    assert _decode(rows=63) == EINVAL           # table shorter than the cache
+    assert _decode(len=None) == EINVAL
+    assert _decode(k=MISALIGNED) == EALIGN
+    assert _decode(cs=_strides(4 * 64 * 128, 64 * 128, 100)) == EALIGN
+    assert _decode(B=0) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(api, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(api, "_lib", None)
+    with pytest.raises(ImportError):
+        api.lib()

@@ -1,0 +1,267 @@
+"""GPU parity: blockwise prefill and the ring-step accumulate against the fp64 oracle.
+
+Small cases compare every output element; the full-size workloads (the
+launch configurations the bench times) compare seeded samples of query
+rows, each of which the oracle computes on its own.
+"""
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import rope as R
+from yarn_rope_blockwise_amd import api, synth
+from yarn_rope_blockwise_amd import workloads as W
+from tests.gpu_helpers import BF16_TOL, F32_TOL, draw, host, max_abs, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(B, S, Hq, Hkv, D, dtype, rope, seed_base=0, n_rows=None):
+    tab, th, af = api.rope_tables_build(api.RopeConfig.of(rope), n_rows or S)
+    qv, q = draw((B, S, Hq, D), seed_base + 0, dtype)
+    kv, k = draw((B, S, Hkv, D), seed_base + 1, dtype)
+    vv, v = draw((B, S, Hkv, D), seed_base + 2, dtype)
+    scale = R.softmax_scale(rope.kind, rope.scale, D)
+    return tab, th, scale, (qv, kv, vv), (q, k, v)
+
+
+def test_prefill_tiny_fp32():
+    # 1 x 1 head x d=64, S=512, fp32, YaRN s=4 from 128.
+    require_gpu()
+    import torch
+    w = W.TINY
+    tab, th, scale, (qv, kv, vv), (q, k, v) = _setup(1, w.seq, 1, 1, w.head_dim, "f32", w.rope)
+    say("attn_prefill_blockwise tiny fp32 S=512 d=64")
+    kr = api.rope_apply(k, tab)
+    o = api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab)
+    torch.cuda.synchronize()
+    ref = A.prefill(qv, kv, vv, th, scale)
+    err = max_abs(host(o), ref)
+    assert err <= F32_TOL, err
+
+
+CASES = [
+    # B, S, Hq, Hkv, D, causal, kind
+    (1, 1, 1, 1, 128, True, W.YARN),
+    (1, 63, 2, 2, 128, True, W.YARN),
+    (1, 64, 2, 1, 128, True, W.PI),
+    (2, 257, 4, 2, 128, True, W.NTK),
+    (1, 1000, 2, 2, 128, True, W.YARN),
+    (1, 1000, 2, 2, 128, False, W.YARN),
+    (1, 700, 8, 2, 64, True, W.YARN),
+    (1, 513, 2, 2, 64, False, W.PLAIN),
+]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,causal,kind", CASES)
+def test_prefill_bf16_small(B, S, Hq, Hkv, D, causal, kind):
+    require_gpu()
+    import torch
+    rope = W.Rope(kind, D, 1e4, 4.0, 128)
+    tab, th, scale, (qv, kv, vv), (q, k, v) = _setup(B, S, Hq, Hkv, D, "bf16", rope, seed_base=S)
+    say(f"attn_prefill_blockwise bf16 B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} causal={causal}")
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    kr = api.rope_apply(k, tab)
+    o = api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab, causal=causal, lse=lse)
+    torch.cuda.synchronize()
+    ref = A.prefill(qv, kv, vv, th, scale, causal=causal)
+    err = max_abs(host(o), ref)
+    assert err <= BF16_TOL, err
+    # log-sum-exp per row against the oracle's (m, l)
+    qr = R.rotate_bshd(qv, th, np.arange(S))
+    krr = R.rotate_bshd(kv, th, np.arange(S))
+    vis = A.causal_visible if causal else A.all_visible
+    lse_h = host(lse)
+    for b in range(B):
+        for h in range(Hq):
+            g = A.kv_head(h, Hq, Hkv)
+            _, m, l = A.attention_full(qr[b, :, h], krr[b, :, g], vv[b, :, g], scale,
+                                       np.arange(S), np.arange(S), vis, return_state=True)
+            assert max_abs(lse_h[b, h], m + np.log(l)) <= 1e-2
+
+
+def test_prefill_prerotated_and_strided():
+    # cos_sin = NULL: Q and K are taken as already rotated; inputs are views
+    # into a packed [B, S, 3, H, D] buffer (strided tokens and heads).
+    require_gpu()
+    import torch
+    B, S, H, D = 1, 300, 2, 128
+    qkv_v, qkv = draw((B, S, 3, H, D), 77, "bf16")
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    say("attn_prefill_blockwise prerotated strided S=300")
+    o = api.attn_prefill_blockwise(q, k, v, 0.1)
+    torch.cuda.synchronize()
+    ref = A.prefill(qkv_v[:, :, 0], qkv_v[:, :, 1], qkv_v[:, :, 2], None, 0.1)
+    assert max_abs(host(o), ref) <= BF16_TOL
+
+
+def test_prefill_deterministic():
+    require_gpu()
+    import torch
+    rope = W.Rope(W.YARN, 128, 1e4, 4.0, 128)
+    tab, th, scale, _, (q, k, v) = _setup(1, 2000, 4, 4, 128, "bf16", rope, seed_base=5)
+    say("attn_prefill_blockwise determinism S=2000")
+    kr = api.rope_apply(k, tab)
+    o1 = api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab)
+    o2 = api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def _sample_rows(S, seed, count=40):
+    edges = [0, 1, 2, 63, 64, 127, 128, 255, 256, 257, S // 2, S - 257, S - 256, S - 2, S - 1]
+    return synth.sample_rows(S, count, seed, must=edges)
+
+
+def _check_prefill_rows(w, heads, rows_per_head=40):
+    import torch
+    tab, th, scale, (qv, kv, vv), (q, k, v) = _setup(w.batch, w.seq, w.n_q_heads, w.n_kv_heads,
+                                                     w.head_dim, "bf16", w.rope)
+    say(f"attn_prefill_blockwise {w.name} full size")
+    kr = api.rope_apply(k, tab)
+    del k
+    o = api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for h in heads:
+        rows = _sample_rows(w.seq, 1000 + h, rows_per_head)
+        got = host(o[0, rows, h])
+        ref = A.prefill(qv, kv, vv, th, scale, rows=rows, heads=[h])[0, :, 0]
+        worst = max(worst, max_abs(got, ref))
+    assert worst <= BF16_TOL, worst
+    return worst
+
+
+def test_prefill_full_llama16k():
+    require_gpu()
+    _check_prefill_rows(W.LLAMA_16K, heads=[0, 13, 31])
+
+
+@pytest.mark.parametrize("kind", [W.PI, W.NTK, W.YARN], ids=["pi", "ntk", "yarn"])
+def test_prefill_full_gqa32k(kind):
+    require_gpu()
+    _check_prefill_rows(W.GQA_32K[kind], heads=[0, 5, 30], rows_per_head=24)
+
+
+# ---------------------------------------------------------------------------
+# attn_block_accumulate (one ring device's share)
+# ---------------------------------------------------------------------------
+
+def _ring(w_blocks, blk, Hq, Hkv, D, dtype, rope, qi, seed_base=0):
+    S = w_blocks * blk
+    tab, th, _ = api.rope_tables_build(api.RopeConfig.of(rope), S)
+    qv, q = draw((1, blk, Hq, D), seed_base + 0, dtype)        # the local query block
+    kv, k = draw((1, S, Hkv, D), seed_base + 1, dtype)         # the whole key sequence
+    vv, v = draw((1, S, Hkv, D), seed_base + 2, dtype)
+    k = api.rope_apply(k, tab)          # each block rotated once at its own positions
+    kb = [k[:, j * blk:(j + 1) * blk] for j in range(w_blocks)]
+    vb = [v[:, j * blk:(j + 1) * blk] for j in range(w_blocks)]
+    kbv = [kv[:, j * blk:(j + 1) * blk] for j in range(w_blocks)]
+    vbv = [vv[:, j * blk:(j + 1) * blk] for j in range(w_blocks)]
+    return tab, th, q, qv, kb, vb, kbv, vbv
+
+
+def _run_ring(q, kb, vb, tab, scale, qi, blk, order, state=None, finalize=True):
+    out = None
+    for t, j in enumerate(order):
+        last = t == len(order) - 1
+        out = api.attn_block_accumulate(q, kb[j], vb[j], state, qi * blk, j * blk, scale,
+                                        cos_sin=tab, first=(t == 0), finalize=finalize and last)
+    return out
+
+
+def test_accumulate_tiny_ring_fp32():
+    # The tiny fp32 problem fed as 8 blocks of 64 (query block 7, ring order).
+    require_gpu()
+    import torch
+    w = W.TINY_RING
+    tab, th, q, qv, kb, vb, kbv, vbv = _ring(w.n_blocks, w.block, 1, 1, w.head_dim, "f32",
+                                             w.rope, w.q_block_index)
+    scale = R.softmax_scale(w.rope.kind, w.rope.scale, w.head_dim)
+    st = api.AccState.empty(1, w.block, 1, w.head_dim)
+    order = W.ring_order(w)
+    say("attn_block_accumulate tiny fp32 ring 8x64")
+    o = _run_ring(q, kb, vb, tab, scale, w.q_block_index, w.block, order, st)
+    torch.cuda.synchronize()
+    offs = [j * w.block for j in range(w.n_blocks)]
+    o_ref, m_ref, l_ref, acc_ref = A.ring_share(qv, kbv, vbv, th, scale,
+                                                w.q_block_index * w.block, offs, order=order)
+    assert max_abs(host(o), o_ref) <= F32_TOL
+    np.testing.assert_allclose(host(st.m), m_ref, atol=1e-5)
+    np.testing.assert_allclose(host(st.l), l_ref, rtol=1e-5)
+    np.testing.assert_allclose(host(st.o_acc), acc_ref, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("qi", [0, 2, 3])
+def test_accumulate_bf16_ring_small(qi):
+    require_gpu()
+    import torch
+    nb, blk, Hq, Hkv, D = 4, 300, 4, 2, 128
+    rope = W.Rope(W.YARN, D, 1e4, 8.0, 300)
+    tab, th, q, qv, kb, vb, kbv, vbv = _ring(nb, blk, Hq, Hkv, D, "bf16", rope, qi, seed_base=9)
+    scale = R.softmax_scale(rope.kind, rope.scale, D)
+    offs = [j * blk for j in range(nb)]
+    order = [(qi - t) % nb for t in range(nb)]       # includes future blocks: no-ops
+    st = api.AccState.empty(1, blk, Hq, D)
+    say(f"attn_block_accumulate bf16 ring 4x300 qi={qi}")
+    o = _run_ring(q, kb, vb, tab, scale, qi, blk, order, st)
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref, acc_ref = A.ring_share(qv, kbv, vbv, th, scale, qi * blk, offs,
+                                                order=order)
+    assert max_abs(host(o), o_ref) <= BF16_TOL
+    np.testing.assert_allclose(host(st.m), m_ref, atol=2e-2)
+    # order invariance on the GPU: ascending block order
+    st2 = api.AccState.empty(1, blk, Hq, D)
+    o2 = _run_ring(q, kb, vb, tab, scale, qi, blk, list(range(nb)), st2)
+    torch.cuda.synchronize()
+    assert max_abs(host(o2), o_ref) <= BF16_TOL
+
+
+def test_accumulate_resume_from_host_snapshot():
+    require_gpu()
+    import torch
+    nb, blk, Hq, Hkv, D = 4, 256, 2, 2, 128
+    rope = W.Rope(W.PI, D, 1e4, 4.0)
+    qi = 3
+    tab, th, q, qv, kb, vb, kbv, vbv = _ring(nb, blk, Hq, Hkv, D, "bf16", rope, qi, seed_base=21)
+    scale = R.softmax_scale(rope.kind, rope.scale, D)
+    order = [3, 2, 1, 0]
+    st = api.AccState.empty(1, blk, Hq, D)
+    say("attn_block_accumulate resume")
+    o_ref = _run_ring(q, kb, vb, tab, scale, qi, blk, order, st)
+    st2 = api.AccState.empty(1, blk, Hq, D)
+    _run_ring(q, kb, vb, tab, scale, qi, blk, order[:2], st2, finalize=False)
+    torch.cuda.synchronize()
+    snap = [host(x) for x in (st2.o_acc, st2.m, st2.l)]
+    st3 = api.AccState(*[torch.from_numpy(x.astype(np.float32)).cuda() for x in snap])
+    o_res = None
+    for t, j in enumerate(order[2:]):
+        o_res = api.attn_block_accumulate(q, kb[j], vb[j], st3, qi * blk, j * blk, scale,
+                                          cos_sin=tab, finalize=(t == 1))
+    torch.cuda.synchronize()
+    assert torch.equal(o_res, o_ref)
+
+
+def test_accumulate_full_ring_share():
+    # 8 heads, query block 7 of 8 blocks of 32768 tokens (positions up to
+    # 262143), YaRN s=8 from 32768, fed in ring order 7, 6, ..., 0.
+    require_gpu()
+    import torch
+    w = W.RING_SHARE
+    tab, th, q, qv, kb, vb, kbv, vbv = _ring(w.n_blocks, w.block, w.n_q_heads, w.n_kv_heads,
+                                             w.head_dim, "bf16", w.rope, w.q_block_index)
+    scale = R.softmax_scale(w.rope.kind, w.rope.scale, w.head_dim)
+    st = api.AccState.empty(1, w.block, w.n_q_heads, w.head_dim)
+    order = W.ring_order(w)
+    say("attn_block_accumulate ring share 8x32768 full size")
+    o = _run_ring(q, kb, vb, tab, scale, w.q_block_index, w.block, order, st)
+    torch.cuda.synchronize()
+    offs = [j * w.block for j in range(w.n_blocks)]
+    worst = 0.0
+    for h in (0, 7):
+        rows = _sample_rows(w.block, 50 + h, 12)
+        o_ref, m_ref, _, _ = A.ring_share(qv, kbv, vbv, th, scale, w.q_block_index * w.block,
+                                          offs, order=order, rows=rows, heads=[h])
+        worst = max(worst, max_abs(host(o[0, rows, h]), o_ref[0, :, 0]))
+        assert max_abs(host(st.m[0, h, rows]), m_ref[0, 0]) <= 2e-2
+    assert worst <= BF16_TOL, worst

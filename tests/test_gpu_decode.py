@@ -1,0 +1,120 @@
+"""GPU parity: attention-sink + sliding-window decode against the fp64 oracle."""
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import rope as R
+from yarn_rope_blockwise_amd import api, synth
+from yarn_rope_blockwise_amd import workloads as W
+from tests.gpu_helpers import BF16_TOL, draw, host, max_abs, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(B, Hq, Hkv, D, n_sink, window, lens, ring_heads, rope, seed=0):
+    import torch
+    C = n_sink + window
+    tab, th, _ = api.rope_tables_build(api.RopeConfig.of(rope), C)
+    qv, q = draw((B, Hq, D), seed + 0, "bf16")
+    kv, k = draw((B, Hkv, C, D), seed + 1, "bf16")
+    vv, v = draw((B, Hkv, C, D), seed + 2, "bf16")
+    lens_t = torch.tensor(np.asarray(lens, np.int32), device="cuda")
+    rh_t = None if ring_heads is None else torch.tensor(np.asarray(ring_heads, np.int32),
+                                                         device="cuda")
+    scale = R.softmax_scale(rope.kind, rope.scale, D)
+    return tab, th, scale, (qv, kv, vv), (q, k, v), lens_t, rh_t
+
+
+def test_decode_full_sink_config():
+    # 64 sequences x 32 heads, d=128, 4 sinks + 4096 window (cache full),
+    # ring heads seeded, plain RoPE.
+    require_gpu()
+    import torch
+    w = W.SINK_DECODE
+    C = w.n_sink + w.window
+    rh = synth.ring_heads(w.batch, w.window)
+    tab, th, scale, (qv, kv, vv), (q, k, v), lens, rht = _case(
+        w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_sink, w.window, [C] * w.batch, rh,
+        w.rope)
+    say("attn_decode_sink_window B=64 H=32 C=4100 full size")
+    o = api.attn_decode_sink_window(q, k, v, lens, w.n_sink, w.window, tab, scale, ring_head=rht)
+    torch.cuda.synchronize()
+    got = host(o)
+    bs = synth.sample_rows(w.batch, 6, 123, must=[0, w.batch - 1])
+    ref = A.decode_sink_window(qv[bs], kv[bs], vv[bs], th, scale, w.n_sink, w.window,
+                               [C] * len(bs), rh[bs])
+    err = max_abs(got[bs], ref)
+    assert err <= BF16_TOL, err
+
+
+@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_edge_cases(G, D):
+    # len 0, len inside the sinks, a partly filled window, a full window with
+    # ring heads at 0 / middle / last slot, and invalid len / ring head.
+    require_gpu()
+    import torch
+    n_sink, window = 4, 300
+    C = n_sink + window
+    lens = [0, 1, 3, 4, 5, 150, C, C, C, C + 1, C]
+    heads = [0, 0, 0, 0, 0, 7, 0, 123, window - 1, 0, window]
+    B = len(lens)
+    Hkv = 2
+    rope = W.Rope(W.YARN, D, 1e4, 4.0, 128)
+    tab, th, scale, (qv, kv, vv), (q, k, v), lens_t, rh_t = _case(
+        B, Hkv * G, Hkv, D, n_sink, window, lens, heads, rope, seed=40 + G + D)
+    say(f"attn_decode_sink_window edge cases G={G} D={D}")
+    o = api.attn_decode_sink_window(q, k, v, lens_t, n_sink, window, tab, scale, ring_head=rh_t)
+    torch.cuda.synchronize()
+    got = host(o)
+    for b in range(B):
+        bad = lens[b] < 0 or lens[b] > C or heads[b] < 0 or heads[b] >= window
+        if bad:
+            assert np.isnan(got[b]).all(), b
+            continue
+        ref = A.decode_sink_window(qv[b:b + 1], kv[b:b + 1], vv[b:b + 1], th, scale, n_sink,
+                                   window, [lens[b]], [heads[b]])
+        if lens[b] == 0:
+            assert np.all(got[b] == 0)
+        assert max_abs(got[b], ref[0]) <= BF16_TOL, b
+
+
+def test_decode_streaming_equals_masked_attention():
+    # Tokens streamed through the cache (sinks kept, window evicting) give
+    # the masked attention over the logical sequence with re-indexed positions.
+    require_gpu()
+    import torch
+    n_sink, window, H, D, T = 4, 100, 4, 128, 357
+    C = n_sink + window
+    rope = W.Rope(W.PLAIN, D)
+    tab, th, _ = api.rope_tables_build(api.RopeConfig.of(rope), C)
+    kseq, _ = synth.normal((T, H, D), 91, "bf16")
+    vseq, _ = synth.normal((T, H, D), 92, "bf16")
+    qv, q = draw((1, H, D), 93, "bf16")
+    kc = np.zeros((1, H, C, D), np.float32)
+    vc = np.zeros((1, H, C, D), np.float32)
+    for t in range(T):
+        slot = t if t < n_sink else n_sink + (t - n_sink) % window
+        kc[0, :, slot] = kseq[t]
+        vc[0, :, slot] = vseq[t]
+    rh = (T - n_sink) % window
+    kdev = torch.from_numpy(synth.bf16_bits_from_f32(kc).view(np.int16)).view(torch.bfloat16).cuda()
+    vdev = torch.from_numpy(synth.bf16_bits_from_f32(vc).view(np.int16)).view(torch.bfloat16).cuda()
+    scale = R.softmax_scale(rope.kind, rope.scale, D)
+    say("attn_decode_sink_window streamed T=357")
+    o = api.attn_decode_sink_window(q, kdev, vdev, torch.tensor([C], dtype=torch.int32,
+                                                                 device="cuda"),
+                                    n_sink, window, tab, scale,
+                                    ring_head=torch.tensor([rh], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    kept = np.r_[0:n_sink, T - window:T]
+    pos = np.arange(len(kept))
+    ck, sk = R.tables(th, pos)
+    cq, sq = R.tables(th, [len(kept) - 1])
+    ref = np.zeros((H, D))
+    for h in range(H):
+        kk = R.rotate_half(kseq[kept, h].astype(np.float64), ck, sk)
+        qq = R.rotate_half(qv[0, h][None].astype(np.float64), cq, sq)
+        ref[h] = A.attention_full(qq, kk, vseq[kept, h], scale, np.array([len(kept) - 1]), pos,
+                                  A.all_visible)[0]
+    assert max_abs(host(o[0]), ref) <= BF16_TOL

@@ -1,0 +1,327 @@
+// C ABI of libyrb: argument validation on the host, then kernel launches.
+// Declarations and the contract of each call are in include/yrb.h.
+//
+// Nothing here allocates, synchronises or keeps state.  Every check runs
+// before the first launch, so an error return means nothing was queued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/yrb.h"
+#include "kernels.h"
+
+namespace {
+
+using yrb::kBF16;
+using yrb::kF32;
+
+constexpr double kPi = 3.14159265358979323846;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int32_t dtype) { return dtype == YRB_BF16 ? 2 : 4; }
+
+bool dtype_ok(int32_t dtype) { return dtype == YRB_BF16 || dtype == YRB_F32; }
+bool dim_ok(int64_t d) { return d == 64 || d == 128; }
+
+// Strides (elements) must keep every row start 16-byte aligned.
+bool strides_aligned(const int64_t* s, int n, int32_t dtype) {
+  const int64_t q = 16 / elem_size(dtype);
+  for (int i = 0; i < n; ++i)
+    if (s[i] % q != 0) return false;
+  return true;
+}
+bool strides_nonneg(const int64_t* s, int n) {
+  for (int i = 0; i < n; ++i)
+    if (s[i] < 0) return false;
+  return true;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? YRB_OK : YRB_EHIP; }
+
+int check_config(const yrb_rope_config* c) {
+  if (!c) return YRB_EINVAL;
+  if (c->kind < YRB_ROPE_PLAIN || c->kind > YRB_ROPE_YARN) return YRB_EINVAL;
+  if (!dim_ok(c->head_dim)) return YRB_EUNSUPPORTED;
+  if (!(c->base > 1.0) || !std::isfinite(c->base)) return YRB_EINVAL;
+  if (!(c->scale > 0.0) || !std::isfinite(c->scale)) return YRB_EINVAL;
+  if (c->kind == YRB_ROPE_YARN) {
+    if (c->orig_ctx <= 0) return YRB_EINVAL;
+    if (!(c->alpha < c->beta) || !std::isfinite(c->alpha) || !std::isfinite(c->beta))
+      return YRB_EINVAL;
+  }
+  return YRB_OK;
+}
+
+// theta'_i of one rescale, in fp64.
+//  base frequencies theta_i = b^(-2i/d)        (tecvarsity Sec. 2)
+//  PI   theta_i / s                             (tecvarsity Sec. 2; 14cs17 "Position Interpolation")
+//  NTK  (b s^(d/(d-2)))^(-2i/d)                 (14cs17 "NTK-Aware Scaling"; the base change that
+//                                                keeps pair 0 and scales the slowest pair by 1/s)
+//  YARN r_i = L_train theta_i / (2 pi) turns per training window; g_i = clamp((r_i-alpha)/(beta-alpha));
+//       theta'_i = (1-g_i) theta_i / s + g_i theta_i   (root18d "Not every RoPE dimension ...";
+//                                                       tecvarsity Sec. 3)
+void compute_theta(const yrb_rope_config* c, double* th) {
+  const int half = c->head_dim / 2;
+  const double d = c->head_dim;
+  double base = c->base;
+  if (c->kind == YRB_ROPE_NTK) base = c->base * std::pow(c->scale, d / (d - 2.0));
+  for (int i = 0; i < half; ++i) {
+    const double t = std::pow(base, -2.0 * i / d);
+    double tp = t;
+    if (c->kind == YRB_ROPE_PI) {
+      tp = t / c->scale;
+    } else if (c->kind == YRB_ROPE_YARN) {
+      const double turns = (double)c->orig_ctx * t / (2.0 * kPi);
+      double g = (turns - c->alpha) / (c->beta - c->alpha);
+      g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+      tp = (1.0 - g) * (t / c->scale) + g * t;
+    }
+    th[i] = tp;
+  }
+}
+
+// Logit multiplier (0.1 ln s + 1)^2 for YaRN with s > 1 (tecvarsity Sec. 3 temperature;
+// the square because the factor sits on both the query and the key rotation).
+double attn_factor_of(const yrb_rope_config* c) {
+  if (c->kind != YRB_ROPE_YARN || c->scale <= 1.0) return 1.0;
+  const double ms = 0.1 * std::log(c->scale) + 1.0;
+  return ms * ms;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* yrb_status_str(int status) {
+  switch (status) {
+    case YRB_OK: return "ok";
+    case YRB_EINVAL: return "invalid argument";
+    case YRB_EUNSUPPORTED: return "unsupported head_dim or dtype";
+    case YRB_EALIGN: return "pointer or stride not 16-byte aligned";
+    case YRB_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int rope_tables_build(const yrb_rope_config* cfg, int64_t pos0, int64_t n_pos, float* cos_sin,
+                      double* inv_freq_out, double* attn_factor_out, void* stream) {
+  int st = check_config(cfg);
+  if (st) return st;
+  if (pos0 < 0 || n_pos < 0) return YRB_EINVAL;
+  if (n_pos > 0 && !cos_sin) return YRB_EINVAL;
+  if (n_pos > 0 && !aligned16(cos_sin)) return YRB_EALIGN;
+  if (n_pos > (int64_t(1) << 40) || pos0 > (int64_t(1) << 50)) return YRB_EINVAL;
+  double th[64];
+  compute_theta(cfg, th);
+  const int half = cfg->head_dim / 2;
+  if (inv_freq_out)
+    for (int i = 0; i < half; ++i) inv_freq_out[i] = th[i];
+  if (attn_factor_out) *attn_factor_out = attn_factor_of(cfg);
+  if (n_pos == 0) return YRB_OK;
+  return hip_status(
+      yrb::launch_rope_tables(th, half, pos0, n_pos, cos_sin, static_cast<hipStream_t>(stream)));
+}
+
+int rope_apply(const void* x, void* y, int32_t dtype, int64_t B, int64_t S, int64_t H, int64_t D,
+               const int64_t x_strides[3], const int64_t y_strides[3], const float* cos_sin,
+               int64_t n_table_rows, int64_t pos_offset, const int32_t* pos_ids, void* stream) {
+  if (!dtype_ok(dtype)) return YRB_EUNSUPPORTED;
+  if (!dim_ok(D)) return YRB_EUNSUPPORTED;
+  if (B < 0 || S < 0 || H < 0 || n_table_rows < 0 || pos_offset < 0) return YRB_EINVAL;
+  if (!x_strides || !y_strides) return YRB_EINVAL;
+  if (B * S * H == 0) return YRB_OK;
+  if (!x || !y || !cos_sin) return YRB_EINVAL;
+  if (!strides_nonneg(x_strides, 3) || !strides_nonneg(y_strides, 3)) return YRB_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(cos_sin)) return YRB_EALIGN;
+  if (!strides_aligned(x_strides, 3, dtype) || !strides_aligned(y_strides, 3, dtype))
+    return YRB_EALIGN;
+  if (!pos_ids && pos_offset + S > n_table_rows) return YRB_EINVAL;
+  yrb::RopeArgs r{};
+  r.x = x;
+  r.y = y;
+  for (int i = 0; i < 3; ++i) {
+    r.xs[i] = x_strides[i];
+    r.ys[i] = y_strides[i];
+  }
+  r.B = B;
+  r.S = S;
+  r.H = H;
+  r.cos_sin = cos_sin;
+  r.n_rows = n_table_rows;
+  r.pos_offset = pos_offset;
+  r.pos_ids = pos_ids;
+  return hip_status(yrb::launch_rope_apply(dtype, (int)D, r, static_cast<hipStream_t>(stream)));
+}
+
+int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                           int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                           const int64_t strides[4][3], const float* cos_sin,
+                           int64_t n_table_rows, float softmax_scale, int32_t causal, float* lse,
+                           void* stream) {
+  if (!dtype_ok(dtype)) return YRB_EUNSUPPORTED;
+  if (!dim_ok(D)) return YRB_EUNSUPPORTED;
+  if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return YRB_EINVAL;
+  if (causal != 0 && causal != 1) return YRB_EINVAL;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return YRB_EINVAL;
+  if (!strides) return YRB_EINVAL;
+  if (B * S == 0) return YRB_OK;
+  if (!q || !k || !v || !o) return YRB_EINVAL;
+  for (int t = 0; t < 4; ++t) {
+    if (!strides_nonneg(strides[t], 3)) return YRB_EINVAL;
+    if (!strides_aligned(strides[t], 3, dtype)) return YRB_EALIGN;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return YRB_EALIGN;
+  if (S >= (int64_t(1) << 31)) return YRB_EINVAL;
+  if (cos_sin) {
+    if (!aligned16(cos_sin)) return YRB_EALIGN;
+    if (S > n_table_rows) return YRB_EINVAL;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  yrb::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = strides[0][i];
+    a.ks[i] = strides[1][i];
+    a.vs[i] = strides[2][i];
+    a.os[i] = strides[3][i];
+  }
+  a.o = o;
+  a.lse = lse;
+  a.cos_sin = cos_sin;
+  a.B = B;
+  a.Sq = S;
+  a.Sk = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.q_offset = 0;
+  a.k_offset = 0;
+  a.softmax_scale = softmax_scale;
+  a.causal = causal;
+  a.load_state = 0;
+  a.store_state = 0;
+  a.finalize = 1;
+  return hip_status(yrb::launch_attention(dtype, (int)D, a, s));
+}
+
+int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk, int32_t dtype,
+                          int64_t B, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv, int64_t D,
+                          const int64_t strides[3][3], int64_t q_offset, int64_t k_offset,
+                          const float* cos_sin, int64_t n_table_rows, float softmax_scale,
+                          int32_t causal, float* o_acc, float* m, float* l,
+                          int32_t flags, void* o_out, const int64_t o_strides[3], void* stream) {
+  if (!dtype_ok(dtype)) return YRB_EUNSUPPORTED;
+  if (!dim_ok(D)) return YRB_EUNSUPPORTED;
+  if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return YRB_EINVAL;
+  if (q_offset < 0 || k_offset < 0) return YRB_EINVAL;
+  if (causal != 0 && causal != 1) return YRB_EINVAL;
+  if (flags & ~(YRB_ACC_FIRST | YRB_ACC_FINALIZE)) return YRB_EINVAL;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return YRB_EINVAL;
+  if (!strides) return YRB_EINVAL;
+  const bool fin = (flags & YRB_ACC_FINALIZE) != 0;
+  if (fin && !o_strides) return YRB_EINVAL;
+  if (B * Sq == 0) return YRB_OK;
+  if (!q || !o_acc || !m || !l) return YRB_EINVAL;
+  if (Sk > 0 && (!k_blk || !v_blk)) return YRB_EINVAL;
+  if (fin && !o_out) return YRB_EINVAL;
+  for (int t = 0; t < 3; ++t) {
+    if (!strides_nonneg(strides[t], 3)) return YRB_EINVAL;
+    if (!strides_aligned(strides[t], 3, dtype)) return YRB_EALIGN;
+  }
+  if (fin && (!strides_nonneg(o_strides, 3))) return YRB_EINVAL;
+  if (fin && !strides_aligned(o_strides, 3, dtype)) return YRB_EALIGN;
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o_acc) ||
+      !aligned16(o_out))
+    return YRB_EALIGN;
+  const int64_t lim = int64_t(1) << 31;
+  if (q_offset + Sq >= lim || k_offset + Sk >= lim) return YRB_EINVAL;
+  const bool future = causal && k_offset > q_offset + Sq - 1;
+  if (cos_sin) {
+    if (!aligned16(cos_sin)) return YRB_EALIGN;
+    if (q_offset + Sq > n_table_rows) return YRB_EINVAL;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  yrb::AttnArgs a{};
+  a.q = q;
+  a.k = k_blk;
+  a.v = v_blk;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = strides[0][i];
+    a.ks[i] = strides[1][i];
+    a.vs[i] = strides[2][i];
+    a.os[i] = fin ? o_strides[i] : 0;
+  }
+  a.o = fin ? o_out : nullptr;
+  a.lse = nullptr;
+  a.o_acc = o_acc;
+  a.m = m;
+  a.l = l;
+  a.cos_sin = cos_sin;
+  a.B = B;
+  a.Sq = Sq;
+  a.Sk = future ? 0 : Sk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.q_offset = q_offset;
+  a.k_offset = k_offset;
+  a.softmax_scale = softmax_scale;
+  a.causal = causal;
+  a.load_state = (flags & YRB_ACC_FIRST) ? 0 : 1;
+  a.store_state = 1;
+  a.finalize = fin ? 1 : 0;
+  return hip_status(yrb::launch_attention(dtype, (int)D, a, s));
+}
+
+int attn_decode_sink_window(const void* q, const void* k_cache, const void* v_cache, void* o,
+                            int32_t dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                            int64_t n_sink, int64_t window, const int64_t q_strides[2],
+                            const int64_t cache_strides[3], const int64_t o_strides[2],
+                            const int32_t* cache_len, const int32_t* ring_head,
+                            const float* cos_sin, int64_t n_table_rows, float softmax_scale,
+                            void* stream) {
+  if (dtype != YRB_BF16) return YRB_EUNSUPPORTED;
+  if (!dim_ok(D)) return YRB_EUNSUPPORTED;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return YRB_EINVAL;
+  const int64_t g = Hq / Hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return YRB_EUNSUPPORTED;
+  if (n_sink < 0 || window < 1) return YRB_EINVAL;
+  if (n_sink + window > (int64_t(1) << 31) - 1) return YRB_EINVAL;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return YRB_EINVAL;
+  if (!q_strides || !cache_strides || !o_strides) return YRB_EINVAL;
+  if (B == 0) return YRB_OK;
+  if (!q || !k_cache || !v_cache || !o || !cache_len || !cos_sin) return YRB_EINVAL;
+  if (!strides_nonneg(q_strides, 2) || !strides_nonneg(cache_strides, 3) ||
+      !strides_nonneg(o_strides, 2))
+    return YRB_EINVAL;
+  if (!strides_aligned(q_strides, 2, dtype) || !strides_aligned(cache_strides, 3, dtype))
+    return YRB_EALIGN;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(cos_sin))
+    return YRB_EALIGN;
+  if (n_table_rows < n_sink + window) return YRB_EINVAL;
+  yrb::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = o;
+  a.qs[0] = q_strides[0];
+  a.qs[1] = q_strides[1];
+  for (int i = 0; i < 3; ++i) a.cs[i] = cache_strides[i];
+  a.os[0] = o_strides[0];
+  a.os[1] = o_strides[1];
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.n_sink = n_sink;
+  a.window = window;
+  a.cache_len = cache_len;
+  a.ring_head = ring_head;
+  a.cos_sin = cos_sin;
+  a.softmax_scale = softmax_scale;
+  return hip_status(yrb::launch_decode(dtype, (int)D, a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

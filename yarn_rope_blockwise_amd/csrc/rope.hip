@@ -1,0 +1,125 @@
+// RoPE cos/sin tables and the half-split pair rotation pass (gfx950).
+//
+// Tables: row r holds (cos, sin) of (pos0 + r) * theta'_i for each pair i
+// ("Context Window Scaling ..." (tecvarsity), Section 2: the 2x2 rotation by
+// m * theta_i).  The angle is formed and reduced in fp64 so that rows at
+// positions ~2^18 keep fp32 accuracy; only the final value is rounded.
+//
+// Rotation: (x_i, x_{i+d/2}) -> (x_i c - x_{i+d/2} s, x_i s + x_{i+d/2} c),
+// fp32 arithmetic, bf16 results rounded to nearest even.  HBM-bound: each
+// thread moves two 16-byte halves of one row and reads its table slice
+// (shared by all heads of a token, so it stays in L2).
+#include "common.h"
+#include "kernels.h"
+
+namespace yrb {
+
+struct ThetaPack {
+  double t[64];
+};
+
+__global__ __launch_bounds__(256) void rope_tables_kernel(ThetaPack th, int half, int64_t pos0,
+                                                          int64_t total, float2* out) {
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  int64_t r = idx / half;
+  int i = (int)(idx - r * half);
+  double a = (double)(pos0 + r) * th.t[i];
+  double s, c;
+  sincos(a, &s, &c);
+  out[idx] = make_float2((float)c, (float)s);
+}
+
+hipError_t launch_rope_tables(const double* theta, int half, int64_t pos0, int64_t n_pos,
+                              float* cos_sin, hipStream_t stream) {
+  ThetaPack th;
+  for (int i = 0; i < 64; ++i) th.t[i] = i < half ? theta[i] : 0.0;
+  int64_t total = n_pos * half;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(rope_tables_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, th, half,
+                     pos0, total, reinterpret_cast<float2*>(cos_sin));
+  return hipGetLastError();
+}
+
+// 16-byte chunk of 8 bf16 or 4 fp32 values.
+template <typename T>
+struct Vec;
+template <>
+struct Vec<__bf16> {
+  static constexpr int N = 8;
+  __device__ static void load(const __bf16* p, float* f) {
+    u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    unpack8(w, f);
+  }
+  __device__ static void store(__bf16* p, const float* f) {
+    *reinterpret_cast<u32x4*>(p) = pack8(f);
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float* f) {
+    f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    for (int i = 0; i < 4; ++i) f[i] = w[i];
+  }
+  __device__ static void store(float* p, const float* f) {
+    *reinterpret_cast<f32x4*>(p) = (f32x4){f[0], f[1], f[2], f[3]};
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t total) {
+  constexpr int N = Vec<T>::N;
+  constexpr int PER_ROW = (D / 2) / N;  // threads per (b, s, h) row
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int c = (int)(idx % PER_ROW);
+  int64_t row = idx / PER_ROW;
+  const int64_t h = row % a.H;
+  row /= a.H;
+  const int64_t s = row % a.S;
+  const int64_t b = row / a.S;
+  const int64_t pos = a.pos_ids ? (int64_t)a.pos_ids[b * a.S + s] : a.pos_offset + s;
+  const T* xr = reinterpret_cast<const T*>(a.x) + b * a.xs[0] + s * a.xs[1] + h * a.xs[2];
+  T* yr = reinterpret_cast<T*>(a.y) + b * a.ys[0] + s * a.ys[1] + h * a.ys[2];
+  const int i0 = c * N;
+  float x[N], z[N], lo[N], hi[N];
+  Vec<T>::load(xr + i0, x);
+  Vec<T>::load(xr + D / 2 + i0, z);
+  if (pos < 0 || pos >= a.n_rows) {
+    const float nan = __builtin_nanf("");
+    for (int j = 0; j < N; ++j) lo[j] = hi[j] = nan;
+  } else {
+    const f32x4* cs = reinterpret_cast<const f32x4*>(a.cos_sin + (pos * (D / 2) + i0) * 2);
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+      f32x4 t = cs[j];  // (cos, sin) of pairs i0+2j, i0+2j+1
+      lo[2 * j] = x[2 * j] * t[0] - z[2 * j] * t[1];
+      hi[2 * j] = x[2 * j] * t[1] + z[2 * j] * t[0];
+      lo[2 * j + 1] = x[2 * j + 1] * t[2] - z[2 * j + 1] * t[3];
+      hi[2 * j + 1] = x[2 * j + 1] * t[3] + z[2 * j + 1] * t[2];
+    }
+  }
+  Vec<T>::store(yr + i0, lo);
+  Vec<T>::store(yr + D / 2 + i0, hi);
+}
+
+template <typename T, int D>
+static hipError_t launch_rope_t(const RopeArgs& a, hipStream_t stream) {
+  constexpr int PER_ROW = (D / 2) / Vec<T>::N;
+  int64_t total = a.B * a.S * a.H * PER_ROW;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL((rope_apply_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
+                     total);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_apply(int dtype, int D, const RopeArgs& a, hipStream_t stream) {
+  if (dtype == kBF16) return D == 64 ? launch_rope_t<__bf16, 64>(a, stream)
+                                     : launch_rope_t<__bf16, 128>(a, stream);
+  return D == 64 ? launch_rope_t<float, 64>(a, stream) : launch_rope_t<float, 128>(a, stream);
+}
+
+}  // namespace yrb
