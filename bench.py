@@ -2,6 +2,7 @@
 """Throughput of the YaRN-RoPE blockwise attention path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
+                    [--workload all|prefill|decode|ring|copy]
 
 One step is the whole prefill path on the Llama-7B-like 16k workload
 (batch 1, 32 heads, d=128, 16384 tokens, bf16, YaRN s=4 from 4096):
@@ -43,6 +44,10 @@ def causal_flops(seq: int, heads: int, d: int, batch: int = 1) -> float:
 
 def ring_flops(block: int, heads: int, d: int, full_blocks: int) -> float:
     return 4.0 * d * heads * (full_blocks * block * block + block * (block + 1) / 2.0)
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def _events(n):
@@ -177,6 +182,18 @@ def run_ring(steps: int, warmup: int):
                 flops=ring_flops(blk, H, D, full))
 
 
+def run_copy(steps: int):
+    """A plain 1 GiB device-to-device copy: the reference for HBM byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": n, "copy_bytes_written": n, "launches": steps}
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The fp64 oracle as it stands, on the 16k workload, head by head."""
     from oracle import attention as A
@@ -215,6 +232,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip decode and ring share")
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "prefill", "decode", "ring", "copy"],
+                    help="run one workload alone (for profiling); the JSON line needs 'all'")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -226,7 +246,18 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.workload != "all":
+        only = {"prefill": lambda: run_prefill(args.steps, args.warmup),
+                "decode": lambda: run_decode(args.steps, args.warmup),
+                "ring": lambda: run_ring(args.steps, args.warmup),
+                "copy": lambda: run_copy(args.steps)}[args.workload]()
+        only.pop("per_call_ms", None)
+        print(json.dumps({"workload": args.workload, **{k: v for k, v in only.items()}}))
+        return
+
+    log("prefill 16k: uploading inputs and timing")
     pre = run_prefill(args.steps, args.warmup)
+    log(f"prefill done: {pre['ms_per_step']:.3f} ms/step, attention {pre['attn_ms']:.3f} ms")
     value = pre["flops"] / (pre["ms_per_step"] * 1e-3) / 1e12
     attn_tflops = pre["flops"] / (pre["attn_ms"] * 1e-3) / 1e12
     line = {
@@ -256,7 +287,9 @@ def main():
                               "attn_prefill_blockwise": round(pre["attn_ms"], 4)},
     }
     if not args.no_extras:
+        log("decode: uploading caches and timing")
         dec = run_decode(max(args.steps, 10), args.warmup)
+        log(f"decode done: {dec['ms']:.3f} ms")
         gbs = dec["bytes"] / (dec["ms"] * 1e-3) / 1e9
         line["decode"] = {"workload": "sink_decode_b64_h32_4p4096", "ms": round(dec["ms"], 4),
                           "GB/s": round(gbs, 1),
@@ -265,12 +298,15 @@ def main():
                                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                                        "kernel": "decode_bf16_kernel",
                                        "bytes_per_launch": dec["bytes"]}}
+        log("ring share: uploading blocks and timing")
         ring = run_ring(max(2, args.steps // 5), 1)
+        log(f"ring share done: {ring['ms']:.3f} ms")
         line["ring_share"] = {"workload": "ring_share_h8_8x32768_yarn8_qblock7",
                               "ms": round(ring["ms"], 3),
                               "TFLOP/s": round(ring["flops"] / (ring["ms"] * 1e-3) / 1e12, 2),
                               "per_call_ms": ring["per_call_ms"]}
     if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
 

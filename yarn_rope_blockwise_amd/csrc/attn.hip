@@ -41,9 +41,10 @@ namespace {
 
 constexpr float kTau = 8.0f;   // lazy-rescale threshold (log2 units)
 
-template <int D>
+template <int D, int BN_>
 struct Tile {
-  static constexpr int BN = 64;             // keys per step
+  static constexpr int BN = BN_;            // keys per barrier step (64 or 128)
+  static constexpr int NKQ = BN / 32;       // 32-key quarters per step
   static constexpr int ROWB = D * 2;        // bytes per K/V row in LDS
   static constexpr int TILEB = BN * ROWB;   // bytes per K or V tile
   static constexpr int NDS = D / 16;        // k-steps of S^T = K Q^T
@@ -70,13 +71,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// One tile (64 rows of K or V) global -> LDS.  Rows past the end are clamped
+// Workgroup barrier that no memory access may cross in either direction at
+// compile time (the LDS-DMA below is invisible to the compiler's model).
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One tile (BN rows of K or V) global -> LDS.  Rows past the end are clamped
 // to the last row: finite data, masked out of the softmax.
-template <int D, int NW, bool IS_V>
+template <int D, int BN, int NW, bool IS_V>
 __device__ __forceinline__ void load_tile(YRB_LDS char* dst, const __bf16* src, int stride, int k0,
                                           int Sk, int wave, int lane) {
-  constexpr int ROWB = Tile<D>::ROWB;
-  constexpr int PER_WAVE = Tile<D>::TILEB / 1024 / NW;
+  using T = Tile<D, BN>;
+  constexpr int ROWB = T::ROWB;
+  constexpr int PER_WAVE = T::TILEB / 1024 / NW;
+  static_assert(PER_WAVE * NW * 1024 == T::TILEB, "tile must split evenly over the waves");
 #pragma unroll
   for (int n = 0; n < PER_WAVE; ++n) {
     const int base = (wave * PER_WAVE + n) * 1024;
@@ -91,168 +102,205 @@ __device__ __forceinline__ void load_tile(YRB_LDS char* dst, const __bf16* src, 
     // of the other buffer; ordering is by the explicit vmcnt waits and
     // barriers around fold_tile.  No register outputs.
     const unsigned m0v = (unsigned)(uintptr_t)(dst + base);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved; nothing else here uses it
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(g), "s"(m0v)
                  : "memory", "m0");
+#pragma clang diagnostic pop
   }
 }
 
 template <int D, int NQT>
 struct WaveState {
-  f32x16 o[Tile<D>::NDT][NQT];
+  f32x16 o[D / 32][NQT];
   float m_use[NQT];    // max the exponentials are taken against (log2 units)
   float m_true[NQT];   // exact running max (log2 units)
   float l[NQT];        // per-lane partial row sum (this half's keys)
 };
 
-// Fold one 64-key tile (already in LDS) into the wave's state, in two
-// halves of 32 keys (kt) so that only 32 score registers per query tile are
-// live at a time.
-template <int D, int NQT>
-__device__ __forceinline__ void fold_tile(const YRB_LDS char* kt_lds, const YRB_LDS char* vt_lds,
-                                          const bf16x8 (&qf)[NQT][Tile<D>::NDS],
-                                          WaveState<D, NQT>& st, bool need_mask, int k0, int Sk,
-                                          int kpos0, int qpos_lane0, bool causal,
-                                          float scale_log2, int lane) {
-  constexpr int ROWB = Tile<D>::ROWB;
-  constexpr int NDS = Tile<D>::NDS;
-  constexpr int NDT = Tile<D>::NDT;
+// K fragments (A operand of S^T = K Q^T) of quarter kq: lane holds key
+// 32kq + l32, dims 16ds + 8hh .. +7.
+template <int D>
+__device__ __forceinline__ void read_k_quarter(const YRB_LDS char* kt_lds, int kq, int lane,
+                                               bf16x8 (&kf)[D / 16]) {
+  constexpr int ROWB = D * 2;
   const int hh = lane >> 5;
-  const int l32 = lane & 31;
+  const int r = kq * 32 + (lane & 31);
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds) {
+    const int c = 2 * ds + hh;
+    kf[ds] = *reinterpret_cast<const YRB_LDS bf16x8*>(kt_lds + r * ROWB + ((c ^ ksw<D>(r)) << 4));
+  }
+}
+
+// S^T for 32 keys against the wave's queries:
+// s[qt][j] = q(row qt*32 + l32) . k(key 32kq + 8(j/4) + 4hh + j%4).
+template <int D, int NQT>
+__device__ __forceinline__ void qk_mfma(const bf16x8 (&kf)[D / 16],
+                                        const bf16x8 (&qf)[NQT][D / 16], f32x16 (&s)[NQT]) {
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) s[qt] = (f32x16){};
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+      s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[qt][ds], s[qt], 0, 0, 0);
+}
+
+// V^T fragments (A operand of O^T += V^T P^T) of quarter kq.  Lane i
+// supplies the address of V[row][d..d+3] with row = 16ks + 8*second +
+// 4(i/32) + (i%16)/4 and d = 32dt + 16((i/16)%2) + 4(i%4);
+// ds_read_b64_tr_b16 hands lane l the column d = 32dt + l%32 over keys
+// 16ks + 8*second + 4(l/32) + 0..3, the key order the packed P uses.
+template <int D>
+__device__ __forceinline__ void read_v_quarter(const YRB_LDS char* vt_lds, int kq, int lane,
+                                               bf16x8 (&vf)[2][D / 32]) {
+  constexpr int ROWB = D * 2;
   const int g = lane >> 4;
   const int t4 = (lane & 15) >> 2;
   const int s4 = lane & 3;
-
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    // S^T = K Q^T : s[qt][j] = q(row qt*32+l32) . k(key kt*32 + 8(j/4) + 4hh + j%4)
-    f32x16 s[NQT];
+  for (int half = 0; half < 2; ++half) {
+    const int ks = 2 * kq + half;
+    const int row1 = 16 * ks + 4 * (g >> 1) + t4;
+    const int row2 = row1 + 8;
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) s[qt] = (f32x16){};
-    const int r = kt * 32 + l32;
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      const int c = 2 * ds + hh;
-      const bf16x8 kf = *reinterpret_cast<const YRB_LDS bf16x8*>(kt_lds + r * ROWB +
-                                                                 ((c ^ ksw<D>(r)) << 4));
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt)
-        s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qt][ds], s[qt], 0, 0, 0);
-    }
-
-    if (need_mask) {
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) {
-        const int qpos = qpos_lane0 + qt * 32;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int kk = kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          const bool bad = (k0 + kk >= Sk) || (causal && kpos0 + kk > qpos);
-          if (bad) s[qt][j] = -INFINITY;
-        }
-      }
-    }
-
-    // Row max (raw dot products; scale > 0 commutes with max).
-    bool grow = false;
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      float mx = s[qt][0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[qt][j]);
-      mx = pair_max(mx) * scale_log2;
-      st.m_true[qt] = fmaxf(st.m_true[qt], mx);
-      grow |= st.m_true[qt] > st.m_use[qt] + kTau;
-    }
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) {
-        const float mn = st.m_true[qt];
-        const float alpha = (st.m_use[qt] == -INFINITY) ? 0.f : fast_exp2(st.m_use[qt] - mn);
-        if (mn != -INFINITY) {
-          st.l[qt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) st.o[dt][qt] *= alpha;
-          st.m_use[qt] = mn;
-        }
-      }
-    }
-
-    // P = exp2(s * scale_log2 - m_use) packed to bf16 as the B operand of
-    // O^T += V^T P^T: k-step ks = 2kt + half takes j = 8*half .. 8*half+7.
-    bf16x8 pf[2][NQT];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      const float mu = (st.m_use[qt] == -INFINITY) ? 0.f : st.m_use[qt];
-      float acc = 0.f;
-      float p[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        p[j] = fast_exp2(__builtin_fmaf(s[qt][j], scale_log2, -mu));
-        acc += p[j];
-      }
-      st.l[qt] += acc;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 w;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          w[u] = pack_bf16x2(p[8 * half + 2 * u], p[8 * half + 2 * u + 1]);
-        pf[half][qt] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-
-    // O^T += V^T P^T.  Lane i supplies the address of V[row][d..d+3] with
-    // row = 16ks + 8*second + 4(i/32) + (i%16)/4 and d = 32dt + 16((i/16)%2)
-    // + 4(i%4); ds_read_b64_tr_b16 hands lane l the column d = 32dt + l%32
-    // over keys 16ks + 8*second + 4(l/32) + 0..3.
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int ks = 2 * kt + half;
-      const int row1 = 16 * ks + 4 * (g >> 1) + t4;
-      const int row2 = row1 + 8;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int c = dt * 4 + 2 * (g & 1) + (s4 >> 1);
-        const int boff = 8 * (s4 & 1);
-        const YRB_LDS char* a1 = vt_lds + row1 * ROWB + ((c ^ vsw<D>(row1)) << 4) + boff;
-        const YRB_LDS char* a2 = vt_lds + row2 * ROWB + ((c ^ vsw<D>(row2)) << 4) + boff;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a1);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a2);
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 vw = {lo2[0], lo2[1], hi2[0], hi2[1]};
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, vw);
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt)
-          st.o[dt][qt] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[half][qt], st.o[dt][qt], 0, 0, 0);
-      }
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int c = dt * 4 + 2 * (g & 1) + (s4 >> 1);
+      const int boff = 8 * (s4 & 1);
+      const YRB_LDS char* a1 = vt_lds + row1 * ROWB + ((c ^ vsw<D>(row1)) << 4) + boff;
+      const YRB_LDS char* a2 = vt_lds + row2 * ROWB + ((c ^ vsw<D>(row2)) << 4) + boff;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a1);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a2);
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 vw = {lo2[0], lo2[1], hi2[0], hi2[1]};
+      vf[half][dt] = __builtin_bit_cast(bf16x8, vw);
     }
   }
 }
 
-template <int D, int NQT, int NW>
+template <int D, int NQT>
+__device__ __forceinline__ void pv_mfma(const bf16x8 (&vf)[2][D / 32], const bf16x8 (&pf)[2][NQT],
+                                        WaveState<D, NQT>& st) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt)
+        st.o[dt][qt] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][dt], pf[half][qt], st.o[dt][qt], 0, 0, 0);
+}
+
+// Online-softmax update for one quarter: mask, row max, (rare) rescale,
+// P = exp2(s * scale_log2 - m_use) packed to bf16 as the B operand of
+// O^T += V^T P^T (k-step 2kq + half takes j = 8*half .. 8*half+7).
+template <int D, int NQT>
+__device__ __forceinline__ void softmax_quarter(f32x16 (&s)[NQT], WaveState<D, NQT>& st,
+                                                bool need_mask, int kk0, int Sk, int kpos_base,
+                                                int qpos_lane0, bool causal, float scale_log2,
+                                                int lane, bf16x8 (&pf)[2][NQT]) {
+  const int hh = lane >> 5;
+  if (need_mask) {
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const int qpos = qpos_lane0 + qt * 32;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kk = kk0 + 8 * (j >> 2) + 4 * hh + (j & 3);   // key index in the block
+        const bool bad = (kk >= Sk) || (causal && kpos_base + kk > qpos);
+        if (bad) s[qt][j] = -INFINITY;
+      }
+    }
+  }
+  bool grow = false;
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    float mx = s[qt][0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[qt][j]);
+    mx = pair_max(mx) * scale_log2;     // scale > 0 commutes with max
+    st.m_true[qt] = fmaxf(st.m_true[qt], mx);
+    grow |= st.m_true[qt] > st.m_use[qt] + kTau;
+  }
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const float mn = st.m_true[qt];
+      const float alpha = (st.m_use[qt] == -INFINITY) ? 0.f : fast_exp2(st.m_use[qt] - mn);
+      if (mn != -INFINITY) {
+        st.l[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) st.o[dt][qt] *= alpha;
+        st.m_use[qt] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    const float mu = (st.m_use[qt] == -INFINITY) ? 0.f : st.m_use[qt];
+    float acc = 0.f;
+    float p[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      p[j] = fast_exp2(__builtin_fmaf(s[qt][j], scale_log2, -mu));
+      acc += p[j];
+    }
+    st.l[qt] += acc;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4 w;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = pack_bf16x2(p[8 * half + 2 * u], p[8 * half + 2 * u + 1]);
+      pf[half][qt] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+}
+
+// Fold one BN-key tile (already in LDS) into the wave's state, 32 keys
+// (one quarter) at a time: S = K Q^T on the MFMA, the online-softmax update
+// on the VALU, then O^T += V^T P^T.  With two waves per SIMD the matrix
+// core of one wave's MFMAs overlaps the other wave's softmax.  (Explicitly
+// pipelining quarters inside a wave measured no faster on gfx950.)
+template <int D, int BN, int NQT>
+__device__ __forceinline__ void fold_tile(const YRB_LDS char* kt_lds, const YRB_LDS char* vt_lds,
+                                          const bf16x8 (&qf)[NQT][D / 16],
+                                          WaveState<D, NQT>& st, bool need_mask, int k0, int Sk,
+                                          int kpos0, int qpos_lane0, bool causal,
+                                          float scale_log2, int lane) {
+#pragma unroll
+  for (int kq = 0; kq < BN / 32; ++kq) {
+    bf16x8 kf[D / 16];
+    f32x16 s[NQT];
+    read_k_quarter<D>(kt_lds, kq, lane, kf);
+    qk_mfma<D, NQT>(kf, qf, s);
+    bf16x8 pf[2][NQT];
+    softmax_quarter<D, NQT>(s, st, need_mask, k0 + 32 * kq, Sk, kpos0 - k0, qpos_lane0, causal,
+                            scale_log2, lane, pf);
+    bf16x8 vf[2][D / 32];
+    read_v_quarter<D>(vt_lds, kq, lane, vf);
+    pv_mfma<D, NQT>(vf, pf, st);
+  }
+}
+
+template <int D, int BN, int NQT, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, int64_t n_qtiles) {
-  using T = Tile<D>;
-  constexpr int BN = T::BN;
+  using T = Tile<D, BN>;
   constexpr int NDS = T::NDS;
   constexpr int NDT = T::NDT;
   constexpr int QW = 32 * NQT;
   constexpr int BM = QW * NW;
   constexpr int LOADS = 2 * (T::TILEB / 1024 / NW);   // load instructions per wave per tile
 
-  // Four distinct LDS objects (not one array) so the compiler can tell the
-  // tile being read from the tile the LDS-DMA prefetch is writing.
-  __shared__ __attribute__((aligned(1024))) char k_raw0[T::TILEB];
-  __shared__ __attribute__((aligned(1024))) char k_raw1[T::TILEB];
-  __shared__ __attribute__((aligned(1024))) char v_raw0[T::TILEB];
-  __shared__ __attribute__((aligned(1024))) char v_raw1[T::TILEB];
-  YRB_LDS char* const K0 = (YRB_LDS char*)k_raw0;
-  YRB_LDS char* const K1 = (YRB_LDS char*)k_raw1;
-  YRB_LDS char* const V0 = (YRB_LDS char*)v_raw0;
-  YRB_LDS char* const V1 = (YRB_LDS char*)v_raw1;
+  // Double-buffered K and V tiles: [buf][K, V] (dynamic LDS, 4 * TILEB bytes).
+  extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
+  YRB_LDS char* const K0 = (YRB_LDS char*)lds_raw;
+  YRB_LDS char* const V0 = K0 + T::TILEB;
+  YRB_LDS char* const K1 = K0 + 2 * T::TILEB;
+  YRB_LDS char* const V1 = K0 + 3 * T::TILEB;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -267,7 +315,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, int64
   const int Hq = (int)a.Hq;
   const int hp = rem - b * Hq;
   const int h = (Hq % 8 == 0) ? (hp & 7) * (Hq >> 3) + (hp >> 3) : hp;
-  const int qtile = a.causal ? (n_qtiles - 1 - rank) : rank;
+  const int qtile = a.causal ? (int)(n_qtiles - 1 - rank) : rank;
   const int hk = h / (Hq / (int)a.Hkv);
 
   const int q0w = qtile * BM + wave * QW;                // first row of this wave
@@ -364,32 +412,30 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, int64
   auto step = [&](YRB_LDS char* kc, YRB_LDS char* vc, YRB_LDS char* kn, YRB_LDS char* vn,
                   int jt) {
     if (jt + 1 < n_tiles) {
-      load_tile<D, NW, false>(kn, kbase, kstride, (jt + 1) * BN, Sk, wave, lane);
-      load_tile<D, NW, true>(vn, vbase, vstride, (jt + 1) * BN, Sk, wave, lane);
+      load_tile<D, BN, NW, false>(kn, kbase, kstride, (jt + 1) * BN, Sk, wave, lane);
+      load_tile<D, BN, NW, true>(vn, vbase, vstride, (jt + 1) * BN, Sk, wave, lane);
       wait_vmcnt<LOADS>();
     } else {
       wait_vmcnt<0>();
     }
     // Tile jt has landed in LDS for this wave (vmcnt); the barrier makes it
-    // so for all waves.  A bare s_barrier: a fence here would also wait for
-    // the prefetch of tile jt+1.
-    __builtin_amdgcn_s_barrier();
+    // so for all waves.  No fence: it would also wait for the prefetch.
+    tile_barrier();
     const int k0 = jt * BN;
     const int kpos0 = k_offset + k0;
     const bool skip = !wave_live || (a.causal && kpos0 > qw_last);
     if (!skip) {
       const bool need_mask = (a.causal && kpos0 + BN - 1 > qw_first) || (k0 + BN > Sk);
-      fold_tile<D, NQT>(kc, vc, qf, st, need_mask, k0, Sk, kpos0, qw_first + l32, a.causal != 0,
-                        scale_log2, lane);
+      fold_tile<D, BN, NQT>(kc, vc, qf, st, need_mask, k0, Sk, kpos0, qw_first + l32,
+                            a.causal != 0, scale_log2, lane);
     }
-    // Every wave is done reading (kc, vc) (its ds_reads fed the MFMAs above)
-    // before a later step refills them.
-    __builtin_amdgcn_s_barrier();
+    // Every wave is done reading (kc, vc) before a later step refills them.
+    tile_barrier();
   };
 
   if (n_tiles > 0) {
-    load_tile<D, NW, false>(K0, kbase, kstride, 0, Sk, wave, lane);
-    load_tile<D, NW, true>(V0, vbase, vstride, 0, Sk, wave, lane);
+    load_tile<D, BN, NW, false>(K0, kbase, kstride, 0, Sk, wave, lane);
+    load_tile<D, BN, NW, true>(V0, vbase, vstride, 0, Sk, wave, lane);
   }
   for (int jt = 0; jt < n_tiles; jt += 2) {
     step(K0, V0, K1, V1, jt);
@@ -540,14 +586,21 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int NQT, int NW>
+template <int D, int BN, int NQT, int NW>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
   constexpr int BM = 32 * NQT * NW;
+  constexpr int LDS_BYTES = 4 * Tile<D, BN>::TILEB;
   const int64_t n_qtiles = (a.Sq + BM - 1) / BM;
   const int64_t blocks = n_qtiles * a.B * a.Hq;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, NQT, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0,
-                     stream, a, n_qtiles);
+  if (LDS_BYTES > 65536) {   // above the default dynamic-LDS limit (gfx950 has 160 KiB)
+    const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&attn_bf16_kernel<D, BN, NQT, NW>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (attr != hipSuccess) return attr;
+  }
+  hipLaunchKernelGGL((attn_bf16_kernel<D, BN, NQT, NW>), dim3((unsigned)blocks), dim3(NW * 64),
+                     LDS_BYTES, stream, a, n_qtiles);
   return hipGetLastError();
 }
 
@@ -562,9 +615,22 @@ hipError_t launch_f32(const AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Keys per barrier step, query rows per wave (32 * NQT) and waves per
+// workgroup of the bf16 kernel.
+#ifndef YRB_PREFILL_BN
+#define YRB_PREFILL_BN 64
+#endif
+#ifndef YRB_PREFILL_NQT
+#define YRB_PREFILL_NQT 1
+#endif
+#ifndef YRB_PREFILL_NW
+#define YRB_PREFILL_NW 8
+#endif
+
 hipError_t launch_attention(int dtype, int D, const AttnArgs& a, hipStream_t stream) {
-  if (dtype == kBF16) return D == 64 ? launch_bf16<64, 1, 8>(a, stream)
-                                     : launch_bf16<128, 1, 8>(a, stream);
+  constexpr int BN = YRB_PREFILL_BN, NQT = YRB_PREFILL_NQT, NW = YRB_PREFILL_NW;
+  if (dtype == kBF16) return D == 64 ? launch_bf16<64, BN, NQT, NW>(a, stream)
+                                     : launch_bf16<128, BN, NQT, NW>(a, stream);
   return D == 64 ? launch_f32<64>(a, stream) : launch_f32<128>(a, stream);
 }
 

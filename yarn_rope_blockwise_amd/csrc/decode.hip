@@ -30,7 +30,22 @@ namespace yrb {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kRounds = 4;
+// Key rounds per wave per iteration, and whether the next iteration's K/V
+// loads are issued before the current one is reduced (register prefetch).
+#ifndef YRB_DECODE_ROUNDS
+#define YRB_DECODE_ROUNDS 4
+#endif
+#ifndef YRB_DECODE_PREFETCH
+#define YRB_DECODE_PREFETCH 1
+#endif
+constexpr int kRounds = YRB_DECODE_ROUNDS;
+
+// K/V of one iteration for one lane: kRounds keys, two 16-byte chunks each.
+struct KVChunk {
+  u32x4 klo[kRounds], khi[kRounds], vlo[kRounds], vhi[kRounds];
+  int epos[kRounds];
+  bool ok[kRounds];
+};
 
 template <int D, int G>
 __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) {
@@ -43,24 +58,25 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
   __shared__ float red_o[kWaves][G][D];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kg = lane / TPK;               // key within the round
   const int cc = lane % TPK;               // chunk: pairs 8cc .. 8cc+7
   const int64_t b = blockIdx.x / a.Hkv;
   const int hk = (int)(blockIdx.x % a.Hkv);
-  const int64_t C = a.n_sink + a.window;
+  const int C = (int)(a.n_sink + a.window);
+  const int n_sink = (int)a.n_sink, window = (int)a.window;
 
   const int len_raw = a.cache_len[b];
   const int rh_raw = a.ring_head ? a.ring_head[b] : 0;
-  const bool bad_seq = len_raw < 0 || len_raw > C || rh_raw < 0 || rh_raw >= a.window;
-  const int64_t len = bad_seq ? 0 : len_raw;
-  const int64_t rh = bad_seq ? 0 : rh_raw;
+  const bool bad_seq = len_raw < 0 || len_raw > C || rh_raw < 0 || rh_raw >= window;
+  const int len = bad_seq ? 0 : len_raw;
+  const int rh = bad_seq ? 0 : rh_raw;
 
   // Rotated query (fp32) for each of the G heads: pairs 8cc..8cc+7.
   float qlo[G][8], qhi[G][8];
   {
-    const int64_t qpos = len > 0 ? len - 1 : 0;
-    const f32x4* t = reinterpret_cast<const f32x4*>(a.cos_sin + qpos * D + 16 * cc);
+    const int qpos = len > 0 ? len - 1 : 0;
+    const f32x4* t = reinterpret_cast<const f32x4*>(a.cos_sin + (int64_t)qpos * D + 16 * cc);
     float c[8], s[8];
 #pragma unroll
     for (int u2 = 0; u2 < 4; ++u2) {
@@ -94,46 +110,47 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
 
   const __bf16* kb = reinterpret_cast<const __bf16*>(a.k) + b * a.cs[0] + hk * a.cs[1];
   const __bf16* vb = reinterpret_cast<const __bf16*>(a.v) + b * a.cs[0] + hk * a.cs[1];
-  const int64_t n_slots = len <= a.n_sink ? len : C;   // slots worth scanning
+  const int n_slots = len <= n_sink ? len : C;   // slots worth scanning
 
-  for (int64_t base = 0; base < n_slots; base += KWG) {
-    u32x4 klo[kRounds], khi[kRounds], vlo[kRounds], vhi[kRounds];
-    int64_t epos[kRounds];
-    bool ok[kRounds];
+  // Issue the K/V loads of the iteration starting at slot `base`.
+  auto load = [&](int base, KVChunk& ch) {
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
-      const int64_t slot = base + (int64_t)r * (KPW * kWaves) + wave * KPW + kg;
-      int64_t e;
-      if (slot < a.n_sink) {
+      const int slot = base + r * (KPW * kWaves) + wave * KPW + kg;
+      int e;
+      if (slot < n_sink) {
         e = slot;
       } else {
-        int64_t j = slot - a.n_sink - rh;
-        j %= a.window;
-        if (j < 0) j += a.window;
-        e = a.n_sink + j;
+        int j = (slot - n_sink - rh) % window;
+        if (j < 0) j += window;
+        e = n_sink + j;
       }
-      ok[r] = slot < n_slots && e < len;
-      epos[r] = ok[r] ? e : 0;
-      const int64_t sc = slot < C ? slot : C - 1;
-      const __bf16* kp = kb + sc * a.cs[2];
-      const __bf16* vp = vb + sc * a.cs[2];
-      klo[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 8 * cc));
-      khi[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + D / 2 + 8 * cc));
-      vlo[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + 8 * cc));
-      vhi[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + D / 2 + 8 * cc));
+      ch.ok[r] = slot < n_slots && e < len;
+      ch.epos[r] = ch.ok[r] ? e : 0;
+      const int sc = slot < C ? slot : C - 1;
+      const __bf16* kp = kb + (int64_t)sc * a.cs[2];
+      const __bf16* vp = vb + (int64_t)sc * a.cs[2];
+      ch.klo[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 8 * cc));
+      ch.khi[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + D / 2 + 8 * cc));
+      ch.vlo[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + 8 * cc));
+      ch.vhi[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + D / 2 + 8 * cc));
     }
+  };
+
+  // Fold one iteration's keys into (m, l, o).
+  auto fold = [&](const KVChunk& ch) {
     float sc_[G][kRounds];
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
-      const f32x4* t = reinterpret_cast<const f32x4*>(a.cos_sin + epos[r] * D + 16 * cc);
+      const f32x4* t = reinterpret_cast<const f32x4*>(a.cos_sin + (int64_t)ch.epos[r] * D + 16 * cc);
       float c[8], s[8], x[8], z[8];
 #pragma unroll
       for (int u2 = 0; u2 < 4; ++u2) {
         const f32x4 tt = t[u2];
         c[2 * u2] = tt[0]; s[2 * u2] = tt[1]; c[2 * u2 + 1] = tt[2]; s[2 * u2 + 1] = tt[3];
       }
-      unpack8(klo[r], x);
-      unpack8(khi[r], z);
+      unpack8(ch.klo[r], x);
+      unpack8(ch.khi[r], z);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float acc = 0.f;
@@ -146,7 +163,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
         // reduce over the TPK lanes of this key
 #pragma unroll
         for (int off = 1; off < TPK; off <<= 1) acc += __shfl_xor(acc, off);
-        sc_[g][r] = ok[r] ? acc * scale_log2 : -INFINITY;
+        sc_[g][r] = ch.ok[r] ? acc * scale_log2 : -INFINITY;
       }
     }
 #pragma unroll
@@ -171,16 +188,34 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
         const float p = fast_exp2(sc_[g][r] - mn);
         l[g] += p;
         float v1[8], v2[8];
-        unpack8(vlo[r], v1);
-        unpack8(vhi[r], v2);
+        unpack8(ch.vlo[r], v1);
+        unpack8(ch.vhi[r], v2);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          o_lo[g][u] = __builtin_fmaf(p, ok[r] ? v1[u] : 0.f, o_lo[g][u]);
-          o_hi[g][u] = __builtin_fmaf(p, ok[r] ? v2[u] : 0.f, o_hi[g][u]);
+          o_lo[g][u] = __builtin_fmaf(p, ch.ok[r] ? v1[u] : 0.f, o_lo[g][u]);
+          o_hi[g][u] = __builtin_fmaf(p, ch.ok[r] ? v2[u] : 0.f, o_hi[g][u]);
         }
       }
     }
+  };
+
+#if YRB_DECODE_PREFETCH
+  KVChunk c0, c1;
+  if (n_slots > 0) load(0, c0);
+  for (int base = 0; base < n_slots; base += 2 * KWG) {
+    if (base + KWG < n_slots) load(base + KWG, c1);
+    fold(c0);
+    if (base + KWG >= n_slots) break;
+    if (base + 2 * KWG < n_slots) load(base + 2 * KWG, c0);
+    fold(c1);
   }
+#else
+  for (int base = 0; base < n_slots; base += KWG) {
+    KVChunk c0;
+    load(base, c0);
+    fold(c0);
+  }
+#endif
 
   // Reduce across the key groups of the wave (lanes with equal cc).
 #pragma unroll
