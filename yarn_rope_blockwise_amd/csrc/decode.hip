@@ -11,17 +11,20 @@
 //
 // gfx950 design: the call is HBM-bound (every cached K and V byte is read
 // once, ~1 flop per byte), so the kernel is a streaming reduction.
-//  * One workgroup (4 waves) per (sequence, key/value head), covering the G
-//    query heads that share it.  Slots are walked in memory order.
+//  * One workgroup (4 waves) per (sequence, 4 key/value heads): wave w owns
+//    head 4g + w and the G query heads that share it.  All four waves walk
+//    the same slots in memory order, so the cos/sin row of each slot's
+//    position is fetched once per workgroup into LDS and shared (fetching
+//    it per head costs as many bytes as K and V together).
 //  * D/16 lanes share one key row: each lane reads the two 16-byte chunks
 //    holding pairs (i, i + d/2) for its 8 pairs, so the rotation is
-//    lane-local.  Per iteration a wave has 4 rounds of K and V loads in
-//    flight (non-temporal: the cache is far larger than the L2/MALL).
+//    lane-local.  Each step a wave holds 4 rounds of K/V loads in flight,
+//    and the next step's loads are issued before this step is reduced
+//    (non-temporal: the cache is far larger than the L2/MALL).
 //  * The score of a rotated key is  sum_i c_i (q_i k_i + q_j k_j) +
-//    s_i (q_j k_i - q_i k_j), j = i + d/2, with (c, s) read from the fp32
-//    table row of the entry's position (2 MiB for 4100 rows: L2-resident).
-//  * Online softmax per wave (exp2 domain), then the 4 waves' (m, l, o) are
-//    merged through LDS.
+//    s_i (q_j k_i - q_i k_j), j = i + d/2.
+//  * Online softmax per wave in the exp2 domain; lanes of one head then
+//    combine their partial sums with cross-lane shuffles.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,21 +32,12 @@ namespace yrb {
 
 namespace {
 
-constexpr int kWaves = 4;
-// Key rounds per wave per iteration, and whether the next iteration's K/V
-// loads are issued before the current one is reduced (register prefetch).
-#ifndef YRB_DECODE_ROUNDS
-#define YRB_DECODE_ROUNDS 4
-#endif
-#ifndef YRB_DECODE_PREFETCH
-#define YRB_DECODE_PREFETCH 1
-#endif
-constexpr int kRounds = YRB_DECODE_ROUNDS;
+constexpr int kWaves = 4;      // = key/value heads per workgroup
+constexpr int kRounds = 4;     // key rounds per wave per step
 
-// K/V of one iteration for one lane: kRounds keys, two 16-byte chunks each.
+// K/V of one step for one lane: kRounds keys, two 16-byte chunks each.
 struct KVChunk {
   u32x4 klo[kRounds], khi[kRounds], vlo[kRounds], vhi[kRounds];
-  int epos[kRounds];
   bool ok[kRounds];
 };
 
@@ -51,18 +45,24 @@ template <int D, int G>
 __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int TPK = D / 16;              // lanes per key row
   constexpr int KPW = 64 / TPK;            // keys per wave per round
-  constexpr int KPI = KPW * kRounds;       // keys per wave per iteration
-  constexpr int KWG = KPI * kWaves;        // keys per workgroup per iteration
-  __shared__ float red_m[kWaves][G];
-  __shared__ float red_l[kWaves][G];
-  __shared__ float red_o[kWaves][G][D];
+  constexpr int KPS = KPW * kRounds;       // slots per step (shared by the 4 waves)
+  constexpr int TROWB = 4 * D;             // bytes of one table row: D/2 pairs x (cos, sin)
+  constexpr int TABB = KPS * TROWB;        // table bytes per step
+  constexpr int TCH = TABB / 16 / (kWaves * 64);   // 16-byte table chunks per thread per step
+  static_assert(TCH * 16 * kWaves * 64 == TABB, "table tile must split over the threads");
+  __shared__ __attribute__((aligned(16))) char tab_raw[2 * TABB];
+  YRB_LDS char* const tab0 = (YRB_LDS char*)tab_raw;
+  YRB_LDS char* const tab1 = tab0 + TABB;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kg = lane / TPK;               // key within the round
   const int cc = lane % TPK;               // chunk: pairs 8cc .. 8cc+7
-  const int64_t b = blockIdx.x / a.Hkv;
-  const int hk = (int)(blockIdx.x % a.Hkv);
+  const int n_groups = (int)((a.Hkv + kWaves - 1) / kWaves);
+  const int64_t b = blockIdx.x / n_groups;
+  const int hk_raw = (int)(blockIdx.x % n_groups) * kWaves + wave;
+  const bool head_live = hk_raw < a.Hkv;
+  const int hk = head_live ? hk_raw : (int)a.Hkv - 1;   // idle waves read a valid head
   const int C = (int)(a.n_sink + a.window);
   const int n_sink = (int)a.n_sink, window = (int)a.window;
 
@@ -71,6 +71,19 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
   const bool bad_seq = len_raw < 0 || len_raw > C || rh_raw < 0 || rh_raw >= window;
   const int len = bad_seq ? 0 : len_raw;
   const int rh = bad_seq ? 0 : rh_raw;
+
+  // Position of the entry in `slot`, or -1 when the slot holds none.
+  auto position = [&](int slot) -> int {
+    int e;
+    if (slot < n_sink) {
+      e = slot;
+    } else {
+      int j = (slot - n_sink - rh) % window;
+      if (j < 0) j += window;
+      e = n_sink + j;
+    }
+    return (slot < C && e < len) ? e : -1;
+  };
 
   // Rotated query (fp32) for each of the G heads: pairs 8cc..8cc+7.
   float qlo[G][8], qhi[G][8];
@@ -112,21 +125,32 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
   const __bf16* vb = reinterpret_cast<const __bf16*>(a.v) + b * a.cs[0] + hk * a.cs[1];
   const int n_slots = len <= n_sink ? len : C;   // slots worth scanning
 
-  // Issue the K/V loads of the iteration starting at slot `base`.
-  auto load = [&](int base, KVChunk& ch) {
+  // Table rows of the step starting at `base`: thread t fetches TCH 16-byte
+  // chunks; chunk k of the tile is row k / (TROWB/16), column k % (TROWB/16).
+  auto load_tab = [&](int base, u32x4 (&tv)[TCH]) {
+#pragma unroll
+    for (int n = 0; n < TCH; ++n) {
+      const int k = n * (kWaves * 64) + threadIdx.x;
+      const int row = k / (TROWB / 16);
+      const int col = k % (TROWB / 16);
+      const int pos = position(base + row);
+      tv[n] = *reinterpret_cast<const u32x4*>(a.cos_sin + (int64_t)(pos < 0 ? 0 : pos) * D +
+                                               4 * col);
+    }
+  };
+  auto store_tab = [&](YRB_LDS char* dst, const u32x4 (&tv)[TCH]) {
+#pragma unroll
+    for (int n = 0; n < TCH; ++n) {
+      const int k = n * (kWaves * 64) + threadIdx.x;
+      *reinterpret_cast<YRB_LDS u32x4*>(dst + 16 * k) = tv[n];
+    }
+  };
+  // K/V loads of the step starting at `base`.
+  auto load_kv = [&](int base, KVChunk& ch) {
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
-      const int slot = base + r * (KPW * kWaves) + wave * KPW + kg;
-      int e;
-      if (slot < n_sink) {
-        e = slot;
-      } else {
-        int j = (slot - n_sink - rh) % window;
-        if (j < 0) j += window;
-        e = n_sink + j;
-      }
-      ch.ok[r] = slot < n_slots && e < len;
-      ch.epos[r] = ch.ok[r] ? e : 0;
+      const int slot = base + r * KPW + kg;
+      ch.ok[r] = position(slot) >= 0 && head_live;
       const int sc = slot < C ? slot : C - 1;
       const __bf16* kp = kb + (int64_t)sc * a.cs[2];
       const __bf16* vp = vb + (int64_t)sc * a.cs[2];
@@ -136,13 +160,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
       ch.vhi[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + D / 2 + 8 * cc));
     }
   };
-
-  // Fold one iteration's keys into (m, l, o).
-  auto fold = [&](const KVChunk& ch) {
+  // Fold one step's keys into (m, l, o); (cos, sin) come from the LDS tile.
+  auto fold = [&](const KVChunk& ch, const YRB_LDS char* tl) {
     float sc_[G][kRounds];
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
-      const f32x4* t = reinterpret_cast<const f32x4*>(a.cos_sin + (int64_t)ch.epos[r] * D + 16 * cc);
+      const YRB_LDS f32x4* t =
+          reinterpret_cast<const YRB_LDS f32x4*>(tl + (r * KPW + kg) * TROWB + 64 * cc);
       float c[8], s[8], x[8], z[8];
 #pragma unroll
       for (int u2 = 0; u2 < 4; ++u2) {
@@ -198,26 +222,47 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
       }
     }
   };
+  // LDS-only barrier: the table writes are done (lgkmcnt), the K/V prefetch
+  // in flight (vmcnt) is not waited for.
+  auto lds_barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt left at their maximum
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
-#if YRB_DECODE_PREFETCH
+  // Step: tables and K/V of the next step are issued (tables first), this
+  // step is reduced, then the next table tile is written to the other LDS
+  // buffer.  One barrier per step: all waves are done with the current tile
+  // before anyone overwrites the buffer it sits in.
+  if (n_slots > 0) {
+    u32x4 tv[TCH];
+    load_tab(0, tv);
+    store_tab(tab0, tv);
+  }
+  lds_barrier();
   KVChunk c0, c1;
-  if (n_slots > 0) load(0, c0);
-  for (int base = 0; base < n_slots; base += 2 * KWG) {
-    if (base + KWG < n_slots) load(base + KWG, c1);
-    fold(c0);
-    if (base + KWG >= n_slots) break;
-    if (base + 2 * KWG < n_slots) load(base + 2 * KWG, c0);
-    fold(c1);
+  if (n_slots > 0) load_kv(0, c0);
+  auto step = [&](int base, KVChunk& cur, KVChunk& nxt, const YRB_LDS char* tl,
+                  YRB_LDS char* tn) {
+    const bool more = base + KPS < n_slots;
+    u32x4 tv[TCH];
+    if (more) {
+      load_tab(base + KPS, tv);
+      load_kv(base + KPS, nxt);
+    }
+    fold(cur, tl);
+    if (more) store_tab(tn, tv);
+    lds_barrier();
+    return more;
+  };
+  for (int base = 0; base < n_slots; base += 2 * KPS) {
+    if (!step(base, c0, c1, tab0, tab1)) break;
+    if (!step(base + KPS, c1, c0, tab1, tab0)) break;
   }
-#else
-  for (int base = 0; base < n_slots; base += KWG) {
-    KVChunk c0;
-    load(base, c0);
-    fold(c0);
-  }
-#endif
 
-  // Reduce across the key groups of the wave (lanes with equal cc).
+  // Reduce across the key groups of the wave (lanes with equal cc), then
+  // write the G output rows of this head.
 #pragma unroll
   for (int g = 0; g < G; ++g) {
 #pragma unroll
@@ -229,44 +274,24 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
         o_hi[g][u] += __shfl_xor(o_hi[g][u], off);
       }
     }
-    if (kg == 0) {
+    if (head_live && kg == 0) {
+      const float inv = l[g] > 0.f ? 1.0f / l[g] : 0.f;
+      float lo[8], hi[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        red_o[wave][g][8 * cc + u] = o_lo[g][u];
-        red_o[wave][g][D / 2 + 8 * cc + u] = o_hi[g][u];
+        lo[u] = bad_seq ? __builtin_nanf("") : o_lo[g][u] * inv;
+        hi[u] = bad_seq ? __builtin_nanf("") : o_hi[g][u] * inv;
       }
-      if (cc == 0) {
-        red_m[wave][g] = m[g];
-        red_l[wave][g] = l[g];
-      }
+      __bf16* op = reinterpret_cast<__bf16*>(a.o) + b * a.os[0] + (int64_t)(hk * G + g) * a.os[1];
+      *reinterpret_cast<u32x4*>(op + 8 * cc) = pack8(lo);
+      *reinterpret_cast<u32x4*>(op + D / 2 + 8 * cc) = pack8(hi);
     }
-  }
-  __syncthreads();
-  // Merge the waves: thread t handles (g, d) pairs.
-  for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64) {
-    const int g = idx / D, d = idx % D;
-    float mm = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, red_m[w][g]);
-    float lt = 0.f, ot = 0.f;
-    if (mm != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float sw = red_m[w][g] == -INFINITY ? 0.f : fast_exp2(red_m[w][g] - mm);
-        lt += sw * red_l[w][g];
-        ot += sw * red_o[w][g][d];
-      }
-    }
-    float res = lt > 0.f ? ot / lt : 0.f;
-    if (bad_seq) res = __builtin_nanf("");
-    __bf16* op = reinterpret_cast<__bf16*>(a.o) + b * a.os[0] + (int64_t)(hk * G + g) * a.os[1];
-    op[d] = (__bf16)res;
   }
 }
 
 template <int D, int G>
 hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t blocks = a.B * a.Hkv;
+  const int64_t blocks = a.B * ((a.Hkv + kWaves - 1) / kWaves);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((decode_bf16_kernel<D, G>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
                      stream, a);
