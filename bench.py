@@ -36,6 +36,40 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HBM GB/s"
 
+# HBM bytes per launch from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE,
+# KiB per dispatch), scaled by what the same counters read for a plain 1 GiB
+# device copy (FETCH x1.99994, WRITE x1.0).  Each figure holds only for the
+# kernel sources it was taken on: the sha256 over the listed files must match,
+# else the line reports traffic null.
+MEASURED_TRAFFIC = {
+    "attn_bf16_kernel": {
+        "files": ("csrc/attn.hip", "csrc/common.h"),
+        "sha256": "cc4eb1d5df3868aad380a86ba643dce30d4f59858c3c65a08cfa70290902b86c",
+        "fetch_kib": 804486, "write_kib": 131075},
+    "decode_bf16_kernel": {
+        "files": ("csrc/decode.hip", "csrc/common.h"),
+        "sha256": "4d084fc7a493bbcefc586c89fae3e4bcdb1b9a60e2df51a48b9cdeb36d0253b3",
+        "fetch_kib": 2109102, "write_kib": 512},
+}
+FETCH_FACTOR, WRITE_FACTOR = 1.99994, 1.0
+
+
+def sources_sha256(files) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "yarn_rope_blockwise_amd", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """Calibrated HBM bytes per launch, or None once the kernel has changed."""
+    t = MEASURED_TRAFFIC[kernel]
+    if sources_sha256(t["files"]) != t["sha256"]:
+        return None
+    return round(t["fetch_kib"] * 1024 * FETCH_FACTOR + t["write_kib"] * 1024 * WRITE_FACTOR)
+
 
 def causal_flops(seq: int, heads: int, d: int, batch: int = 1) -> float:
     """4*d flop per visible (query, key) pair: QK^T and PV, 2 flop per MAC."""
@@ -153,32 +187,41 @@ def run_ring(steps: int, warmup: int):
     v = _upload((1, S, w.n_kv_heads, D), 2)
     tab, _, af = api.rope_tables_build(api.RopeConfig.of(w.rope), S)
     scale = af / np.sqrt(D)
-    k = api.rope_apply(k, tab)              # every block rotated once by its owner
+    k_raw = k
+    k = api.rope_apply(k_raw, tab)          # every block is rotated once by its owner
     st = api.AccState.empty(1, blk, H, D)
     out = torch.empty_like(q)
     order = W.ring_order(w)
-    qoff = w.q_block_index * blk
+    qi = w.q_block_index
+    qoff = qi * blk
+    own = slice(qi * blk, (qi + 1) * blk)
 
     def step(ev=None):
+        # this device rotates its own key block once per pass; the other
+        # blocks arrive already rotated by their owners
+        if ev is not None:
+            ev[0].record()
+        api.rope_apply(k_raw[:, own], tab, pos_offset=qoff, out=k[:, own])
         for t, j in enumerate(order):
             if ev is not None:
-                ev[t].record()
+                ev[t + 1].record()
             api.attn_block_accumulate(q, k[:, j * blk:(j + 1) * blk], v[:, j * blk:(j + 1) * blk],
                                       st, qoff, j * blk, scale, cos_sin=tab, first=(t == 0),
                                       finalize=(t == nb - 1), out=out)
         if ev is not None:
-            ev[nb].record()
+            ev[nb + 1].record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [_events(nb + 1) for _ in range(steps)]
+    evs = [_events(nb + 2) for _ in range(steps)]
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    per_call = np.array([[e[t].elapsed_time(e[t + 1]) for t in range(nb)] for e in evs]).mean(0)
+    per_call = np.array([[e[t + 1].elapsed_time(e[t + 2]) for t in range(nb)] for e in evs]).mean(0)
+    total = float(np.mean([e[0].elapsed_time(e[nb + 1]) for e in evs]))
     full = sum(1 for j in order if j < w.q_block_index)
-    return dict(ms=float(per_call.sum()), per_call_ms=[round(float(x), 4) for x in per_call],
+    return dict(ms=total, per_call_ms=[round(float(x), 4) for x in per_call],
                 flops=ring_flops(blk, H, D, full))
 
 
@@ -279,7 +322,8 @@ def main():
                    "step": "rope_tables_build + rope_apply(K) + attn_prefill_blockwise"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("attn_bf16_kernel"),
                      "kernel": "attn_bf16_kernel", "kernel_ms": round(pre["attn_ms"], 4),
                      "flops_per_launch": pre["flops"]},
         "step_breakdown_ms": {"rope_tables_build": round(pre["tables_ms"], 4),
@@ -295,7 +339,8 @@ def main():
                           "GB/s": round(gbs, 1),
                           "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                       "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                       "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                       "traffic": measured_traffic("decode_bf16_kernel"),
                                        "kernel": "decode_bf16_kernel",
                                        "bytes_per_launch": dec["bytes"]}}
         log("ring share: uploading blocks and timing")

@@ -79,18 +79,28 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One tile (BN rows of K or V) global -> LDS.  Rows past the end are clamped
-// to the last row: finite data, masked out of the softmax.
+// One tile (BN rows of K or V) global -> LDS.  The tile is TILEB/1024
+// DMA instructions of 1 KiB; wave w issues instructions w, w+NW, ...  Rows
+// past the end are clamped to the last row: finite data, masked out of the
+// softmax.
+template <int D, int BN, int NW>
+struct TileLoads {
+  static constexpr int INSTR = Tile<D, BN>::TILEB / 1024;
+  static constexpr int LO = INSTR / NW;                // every wave issues at least LO
+  static constexpr int EXTRA = INSTR % NW;             // waves < EXTRA issue LO + 1
+};
+
 template <int D, int BN, int NW, bool IS_V>
 __device__ __forceinline__ void load_tile(YRB_LDS char* dst, const __bf16* src, int stride, int k0,
                                           int Sk, int wave, int lane) {
   using T = Tile<D, BN>;
+  using TL = TileLoads<D, BN, NW>;
   constexpr int ROWB = T::ROWB;
-  constexpr int PER_WAVE = T::TILEB / 1024 / NW;
-  static_assert(PER_WAVE * NW * 1024 == T::TILEB, "tile must split evenly over the waves");
 #pragma unroll
-  for (int n = 0; n < PER_WAVE; ++n) {
-    const int base = (wave * PER_WAVE + n) * 1024;
+  for (int n = 0; n < TL::LO + (TL::EXTRA ? 1 : 0); ++n) {
+    const int idx = n * NW + wave;
+    if (n >= TL::LO && idx >= TL::INSTR) break;   // wave-uniform
+    const int base = idx * 1024;
     const int off = base + lane * 16;
     const int r = off / ROWB;
     const int p = (off % ROWB) >> 4;
@@ -293,7 +303,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, int64
   constexpr int NDT = T::NDT;
   constexpr int QW = 32 * NQT;
   constexpr int BM = QW * NW;
-  constexpr int LOADS = 2 * (T::TILEB / 1024 / NW);   // load instructions per wave per tile
+  using TL = TileLoads<D, BN, NW>;
 
   // Double-buffered K and V tiles: [buf][K, V] (dynamic LDS, 4 * TILEB bytes).
   extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
@@ -414,7 +424,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, int64
     if (jt + 1 < n_tiles) {
       load_tile<D, BN, NW, false>(kn, kbase, kstride, (jt + 1) * BN, Sk, wave, lane);
       load_tile<D, BN, NW, true>(vn, vbase, vstride, (jt + 1) * BN, Sk, wave, lane);
-      wait_vmcnt<LOADS>();
+      // all but the tile jt+1 loads this wave just issued (K and V)
+      if (TL::EXTRA && wave < TL::EXTRA) wait_vmcnt<2 * (TL::LO + 1)>();
+      else wait_vmcnt<2 * TL::LO>();
     } else {
       wait_vmcnt<0>();
     }
