@@ -42,10 +42,10 @@ METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HB
 # kernel sources it was taken on: the sha256 over the listed files must match,
 # else the line reports traffic null.
 MEASURED_TRAFFIC = {
-    "attn_bf16_kernel": {
-        "files": ("csrc/attn.hip", "csrc/common.h"),
-        "sha256": "cc4eb1d5df3868aad380a86ba643dce30d4f59858c3c65a08cfa70290902b86c",
-        "fetch_kib": 804486, "write_kib": 131075},
+    "attn_bf16_pp_kernel": {
+        "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
+        "sha256": None,   # not yet taken on this kernel
+        "fetch_kib": None, "write_kib": None},
     "decode_bf16_kernel": {
         "files": ("csrc/decode.hip", "csrc/common.h"),
         "sha256": "4d084fc7a493bbcefc586c89fae3e4bcdb1b9a60e2df51a48b9cdeb36d0253b3",
@@ -66,7 +66,7 @@ def sources_sha256(files) -> str:
 def measured_traffic(kernel: str):
     """Calibrated HBM bytes per launch, or None once the kernel has changed."""
     t = MEASURED_TRAFFIC[kernel]
-    if sources_sha256(t["files"]) != t["sha256"]:
+    if t["sha256"] is None or sources_sha256(t["files"]) != t["sha256"]:
         return None
     return round(t["fetch_kib"] * 1024 * FETCH_FACTOR + t["write_kib"] * 1024 * WRITE_FACTOR)
 
@@ -323,8 +323,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("attn_bf16_kernel"),
-                     "kernel": "attn_bf16_kernel", "kernel_ms": round(pre["attn_ms"], 4),
+                     "traffic": measured_traffic("attn_bf16_pp_kernel"),
+                     "kernel": "attn_bf16_pp_kernel", "kernel_ms": round(pre["attn_ms"], 4),
                      "flops_per_launch": pre["flops"]},
         "step_breakdown_ms": {"rope_tables_build": round(pre["tables_ms"], 4),
                               "rope_apply_k": round(pre["rope_k_ms"], 4),

@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libyrb.so")
-SOURCES = ["api.cpp", "rope.hip", "attn.hip", "decode.hip"]
+SOURCES = ["api.cpp", "rope.hip", "attn.hip", "attn_pp.hip", "decode.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code; the compiler

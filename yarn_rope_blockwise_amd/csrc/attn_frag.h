@@ -1,0 +1,438 @@
+// Fragment-level building blocks of the bf16 attention kernels (gfx950):
+// LDS tile geometry and swizzles, the LDS-DMA tile loader, the MFMA
+// fragment reads of K and V, the two products S^T = K Q^T and O^T += V^T P^T,
+// and the online-softmax update of one 32-key quarter.  Included by the
+// kernels' translation units; everything here has internal linkage.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace yrb {
+namespace {
+
+constexpr float kTau = 8.0f;   // lazy-rescale threshold (log2 units)
+
+template <int D, int BN_>
+struct Tile {
+  static constexpr int BN = BN_;            // keys per barrier step (64 or 128)
+  static constexpr int NKQ = BN / 32;       // 32-key quarters per step
+  static constexpr int ROWB = D * 2;        // bytes per K/V row in LDS
+  static constexpr int TILEB = BN * ROWB;   // bytes per K or V tile
+  static constexpr int NDS = D / 16;        // k-steps of S^T = K Q^T
+  static constexpr int NDT = D / 32;        // d tiles of O^T
+};
+
+// K tile: physical 16-byte chunk = logical chunk ^ ksw(row); makes the 16
+// lanes of each ds_read_b128 quarter hit distinct banks.
+template <int D>
+__device__ __forceinline__ int ksw(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+// V tile: XOR on 64-byte blocks; the 4 rows of each transposed half-wave
+// read land in distinct bank quarters.
+template <int D>
+__device__ __forceinline__ int vsw(int r) {
+  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding), other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that no memory access may cross in either direction at
+// compile time (the LDS-DMA below is invisible to the compiler's model).
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One tile (BN rows of K or V) global -> LDS.  The tile is TILEB/1024
+// DMA instructions of 1 KiB; wave w issues instructions w, w+NW, ...  Rows
+// past the end are clamped to the last row: finite data, masked out of the
+// softmax.
+template <int D, int BN, int NW>
+struct TileLoads {
+  static constexpr int INSTR = Tile<D, BN>::TILEB / 1024;
+  static constexpr int LO = INSTR / NW;                // every wave issues at least LO
+  static constexpr int EXTRA = INSTR % NW;             // waves < EXTRA issue LO + 1
+};
+
+template <int D, int BN, int NW, bool IS_V>
+__device__ __forceinline__ void load_tile(YRB_LDS char* dst, const __bf16* src, int stride, int k0,
+                                          int Sk, int wave, int lane) {
+  using T = Tile<D, BN>;
+  using TL = TileLoads<D, BN, NW>;
+  constexpr int ROWB = T::ROWB;
+#pragma unroll
+  for (int n = 0; n < TL::LO + (TL::EXTRA ? 1 : 0); ++n) {
+    const int idx = n * NW + wave;
+    if (n >= TL::LO && idx >= TL::INSTR) break;   // wave-uniform
+    const int base = idx * 1024;
+    const int off = base + lane * 16;
+    const int r = off / ROWB;
+    const int p = (off % ROWB) >> 4;
+    const int c = IS_V ? (p ^ vsw<D>(r)) : (p ^ ksw<D>(r));
+    const int row = min(k0 + r, Sk - 1);
+    const __bf16* g = src + (int64_t)row * stride + c * 8;
+    // global_load_lds_dwordx4: lane i's 16 bytes land at M0 + 16*i.  Issued
+    // from asm so the compiler does not add a vmcnt(0) before every LDS read
+    // of the other buffer; ordering is by the explicit vmcnt waits and
+    // barriers around fold_tile.  No register outputs.
+    const unsigned m0v = (unsigned)(uintptr_t)(dst + base);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved; nothing else here uses it
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(m0v)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+  }
+}
+
+template <int D, int NQT>
+struct WaveState {
+  f32x16 o[D / 32][NQT];
+  float m_use[NQT];    // max the exponentials are taken against (log2 units)
+  float m_true[NQT];   // exact running max (log2 units)
+  float l[NQT];        // per-lane partial row sum (this half's keys)
+};
+
+// K fragments (A operand of S^T = K Q^T) of quarter kq: lane holds key
+// 32kq + l32, dims 16ds + 8hh .. +7.
+template <int D>
+__device__ __forceinline__ void read_k_quarter(const YRB_LDS char* kt_lds, int kq, int lane,
+                                               bf16x8 (&kf)[D / 16]) {
+  constexpr int ROWB = D * 2;
+  const int hh = lane >> 5;
+  const int r = kq * 32 + (lane & 31);
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds) {
+    const int c = 2 * ds + hh;
+    kf[ds] = *reinterpret_cast<const YRB_LDS bf16x8*>(kt_lds + r * ROWB + ((c ^ ksw<D>(r)) << 4));
+  }
+}
+
+// S^T for 32 keys against the wave's queries:
+// s[qt][j] = q(row qt*32 + l32) . k(key 32kq + 8(j/4) + 4hh + j%4).
+template <int D, int NQT>
+__device__ __forceinline__ void qk_mfma(const bf16x8 (&kf)[D / 16],
+                                        const bf16x8 (&qf)[NQT][D / 16], f32x16 (&s)[NQT]) {
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) s[qt] = (f32x16){};
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+      s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[qt][ds], s[qt], 0, 0, 0);
+}
+
+// V^T fragments (A operand of O^T += V^T P^T) of quarter kq.  Lane i
+// supplies the address of V[row][d..d+3] with row = 16ks + 8*second +
+// 4(i/32) + (i%16)/4 and d = 32dt + 16((i/16)%2) + 4(i%4);
+// ds_read_b64_tr_b16 hands lane l the column d = 32dt + l%32 over keys
+// 16ks + 8*second + 4(l/32) + 0..3, the key order the packed P uses.
+template <int D>
+__device__ __forceinline__ void read_v_quarter(const YRB_LDS char* vt_lds, int kq, int lane,
+                                               bf16x8 (&vf)[2][D / 32]) {
+  constexpr int ROWB = D * 2;
+  const int g = lane >> 4;
+  const int t4 = (lane & 15) >> 2;
+  const int s4 = lane & 3;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int ks = 2 * kq + half;
+    const int row1 = 16 * ks + 4 * (g >> 1) + t4;
+    const int row2 = row1 + 8;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int c = dt * 4 + 2 * (g & 1) + (s4 >> 1);
+      const int boff = 8 * (s4 & 1);
+      const YRB_LDS char* a1 = vt_lds + row1 * ROWB + ((c ^ vsw<D>(row1)) << 4) + boff;
+      const YRB_LDS char* a2 = vt_lds + row2 * ROWB + ((c ^ vsw<D>(row2)) << 4) + boff;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a1);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a2);
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 vw = {lo2[0], lo2[1], hi2[0], hi2[1]};
+      vf[half][dt] = __builtin_bit_cast(bf16x8, vw);
+    }
+  }
+}
+
+template <int D, int NQT>
+__device__ __forceinline__ void pv_mfma(const bf16x8 (&vf)[2][D / 32], const bf16x8 (&pf)[2][NQT],
+                                        WaveState<D, NQT>& st) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt)
+        st.o[dt][qt] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][dt], pf[half][qt], st.o[dt][qt], 0, 0, 0);
+}
+
+// Online-softmax update for one quarter: mask, row max, (rare) rescale,
+// P = exp2(s * scale_log2 - m_use) packed to bf16 as the B operand of
+// O^T += V^T P^T (k-step 2kq + half takes j = 8*half .. 8*half+7).
+template <int D, int NQT>
+__device__ __forceinline__ void softmax_quarter(f32x16 (&s)[NQT], WaveState<D, NQT>& st,
+                                                bool need_mask, int kk0, int Sk, int kpos_base,
+                                                int qpos_lane0, bool causal, float scale_log2,
+                                                int lane, bf16x8 (&pf)[2][NQT]) {
+  const int hh = lane >> 5;
+  if (need_mask) {
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const int qpos = qpos_lane0 + qt * 32;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kk = kk0 + 8 * (j >> 2) + 4 * hh + (j & 3);   // key index in the block
+        const bool bad = (kk >= Sk) || (causal && kpos_base + kk > qpos);
+        if (bad) s[qt][j] = -INFINITY;
+      }
+    }
+  }
+  bool grow = false;
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    float mx = s[qt][0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[qt][j]);
+    mx = pair_max(mx) * scale_log2;     // scale > 0 commutes with max
+    st.m_true[qt] = fmaxf(st.m_true[qt], mx);
+    grow |= st.m_true[qt] > st.m_use[qt] + kTau;
+  }
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const float mn = st.m_true[qt];
+      const float alpha = (st.m_use[qt] == -INFINITY) ? 0.f : fast_exp2(st.m_use[qt] - mn);
+      if (mn != -INFINITY) {
+        st.l[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) st.o[dt][qt] *= alpha;
+        st.m_use[qt] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    const float mu = (st.m_use[qt] == -INFINITY) ? 0.f : st.m_use[qt];
+    float acc = 0.f;
+    float p[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      p[j] = fast_exp2(__builtin_fmaf(s[qt][j], scale_log2, -mu));
+      acc += p[j];
+    }
+    st.l[qt] += acc;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4 w;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = pack_bf16x2(p[8 * half + 2 * u], p[8 * half + 2 * u + 1]);
+      pf[half][qt] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+}
+
+// Fold one BN-key tile (already in LDS) into the wave's state, 32 keys
+// (one quarter) at a time: S = K Q^T on the MFMA, the online-softmax update
+// on the VALU, then O^T += V^T P^T.  With two waves per SIMD the matrix
+// core of one wave's MFMAs overlaps the other wave's softmax.  (Explicitly
+// pipelining quarters inside a wave measured no faster on gfx950.)
+template <int D, int BN, int NQT>
+__device__ __forceinline__ void fold_tile(const YRB_LDS char* kt_lds, const YRB_LDS char* vt_lds,
+                                          const bf16x8 (&qf)[NQT][D / 16],
+                                          WaveState<D, NQT>& st, bool need_mask, int k0, int Sk,
+                                          int kpos0, int qpos_lane0, bool causal,
+                                          float scale_log2, int lane) {
+#pragma unroll
+  for (int kq = 0; kq < BN / 32; ++kq) {
+    bf16x8 kf[D / 16];
+    f32x16 s[NQT];
+    read_k_quarter<D>(kt_lds, kq, lane, kf);
+    qk_mfma<D, NQT>(kf, qf, s);
+    bf16x8 pf[2][NQT];
+    softmax_quarter<D, NQT>(s, st, need_mask, k0 + 32 * kq, Sk, kpos0 - k0, qpos_lane0, causal,
+                            scale_log2, lane, pf);
+    bf16x8 vf[2][D / 32];
+    read_v_quarter<D>(vt_lds, kq, lane, vf);
+    pv_mfma<D, NQT>(vf, pf, st);
+  }
+}
+
+// Work item of a workgroup: the heaviest (causal) query tiles are launched
+// first, and consecutive workgroups take heads that are 8 apart, so the
+// workgroups an XCD runs at once (blocks go round-robin over the 8 XCDs)
+// share a few key/value heads in its L2.
+struct WorkItem {
+  int b, h, hk, qtile;
+};
+
+__device__ __forceinline__ WorkItem work_item(const AttnArgs& a, int64_t n_qtiles) {
+  const int Hq = (int)a.Hq;
+  const int per = (int)(a.B * a.Hq);
+  const int rank = (int)blockIdx.x / per;
+  const int rem = (int)blockIdx.x - rank * per;
+  WorkItem w;
+  w.b = rem / Hq;
+  const int hp = rem - w.b * Hq;
+  w.h = (Hq % 8 == 0) ? (hp & 7) * (Hq >> 3) + (hp >> 3) : hp;
+  w.qtile = a.causal ? (int)(n_qtiles - 1 - rank) : rank;
+  w.hk = w.h / (Hq / (int)a.Hkv);
+  return w;
+}
+
+// Query fragments (B operand of S^T = K Q^T) of one wave: lane holds query
+// row q0w + 32qt + l32 (clamped to the last row), dims 16ds + 8hh .. +7,
+// rotated here in fp32 from the table when one is given and rounded once to
+// bf16.
+template <int D, int NQT>
+__device__ __forceinline__ void load_q(const AttnArgs& a, int b, int h, int q0w, int lane,
+                                       bf16x8 (&qf)[NQT][D / 16]) {
+  constexpr int NDS = D / 16;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int Sq = (int)a.Sq;
+  const int q_offset = (int)a.q_offset;
+  const __bf16* qbase = reinterpret_cast<const __bf16*>(a.q) + b * a.qs[0] + h * a.qs[2];
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    const int row = min(q0w + qt * 32 + l32, Sq - 1);
+    const __bf16* qp = qbase + row * a.qs[1] + 8 * hh;
+    u32x4 raw[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) raw[ds] = *reinterpret_cast<const u32x4*>(qp + 16 * ds);
+    if (a.cos_sin) {
+      const float* cs = a.cos_sin + (int64_t)(q_offset + row) * D;
+#pragma unroll
+      for (int ds = 0; ds < NDS / 2; ++ds) {
+        const int i0 = 16 * ds + 8 * hh;
+        const f32x4* t = reinterpret_cast<const f32x4*>(cs + 2 * i0);
+        float x[8], z[8], lo[8], hi[8];
+        unpack8(raw[ds], x);
+        unpack8(raw[ds + NDS / 2], z);
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2) {
+          const f32x4 tt = t[u2];
+          lo[2 * u2] = x[2 * u2] * tt[0] - z[2 * u2] * tt[1];
+          hi[2 * u2] = x[2 * u2] * tt[1] + z[2 * u2] * tt[0];
+          lo[2 * u2 + 1] = x[2 * u2 + 1] * tt[2] - z[2 * u2 + 1] * tt[3];
+          hi[2 * u2 + 1] = x[2 * u2 + 1] * tt[3] + z[2 * u2 + 1] * tt[2];
+        }
+        raw[ds] = pack8(lo);
+        raw[ds + NDS / 2] = pack8(hi);
+      }
+    }
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qf[qt][ds] = __builtin_bit_cast(bf16x8, raw[ds]);
+  }
+}
+
+// Running state of one wave: empty, or read from (o_acc, m, l) of an
+// earlier step (m stored in natural-log units, kept here in log2 units).
+template <int D, int NQT>
+__device__ __forceinline__ void init_state(const AttnArgs& a, int b, int h, int q0w, int lane,
+                                           WaveState<D, NQT>& st) {
+  constexpr int NDT = D / 32;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int Sq = (int)a.Sq;
+  const int Hq = (int)a.Hq;
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    st.m_use[qt] = -INFINITY;
+    st.m_true[qt] = -INFINITY;
+    st.l[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) st.o[dt][qt] = (f32x16){};
+  }
+  if (a.load_state) {
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const int row = q0w + qt * 32 + l32;
+      if (row < Sq) {
+        const int64_t ml = ((int64_t)b * Hq + h) * Sq + row;
+        const float m0 = a.m[ml];
+        st.m_use[qt] = st.m_true[qt] = (m0 == -INFINITY) ? -INFINITY : m0 * kLog2e;
+        st.l[qt] = hh == 0 ? a.l[ml] : 0.f;
+        const float* op = a.o_acc + (((int64_t)b * Sq + row) * Hq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(op + dt * 32 + 8 * q4 + 4 * hh);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st.o[dt][qt][4 * q4 + e] = v[e];
+          }
+      }
+    }
+  }
+}
+
+// Epilogue of one wave: restore the exact running max, then store the state
+// (ring step) and/or the normalised output and log-sum-exp (last step).
+template <int D, int NQT>
+__device__ __forceinline__ void finish_rows(const AttnArgs& a, int b, int h, int q0w, int lane,
+                                            WaveState<D, NQT>& st) {
+  constexpr int NDT = D / 32;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int Sq = (int)a.Sq;
+  const int Hq = (int)a.Hq;
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    float lsum = pair_sum(st.l[qt]);
+    const float mt = st.m_true[qt];
+    if (mt != -INFINITY && st.m_use[qt] != mt) {
+      const float alpha = fast_exp2(st.m_use[qt] - mt);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) st.o[dt][qt] *= alpha;
+      st.m_use[qt] = mt;
+    }
+    const int row = q0w + qt * 32 + l32;
+    if (row >= Sq) continue;
+    const int64_t ml = ((int64_t)b * Hq + h) * Sq + row;
+    if (a.store_state) {
+      if (hh == 0) {
+        a.m[ml] = (mt == -INFINITY) ? -INFINITY : mt * kLn2;
+        a.l[ml] = lsum;
+      }
+      float* op = a.o_acc + (((int64_t)b * Sq + row) * Hq + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v = {st.o[dt][qt][4 * q4], st.o[dt][qt][4 * q4 + 1],
+                           st.o[dt][qt][4 * q4 + 2], st.o[dt][qt][4 * q4 + 3]};
+          *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * q4 + 4 * hh) = v;
+        }
+    }
+    if (a.finalize) {
+      const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+      __bf16* op = reinterpret_cast<__bf16*>(a.o) + b * a.os[0] + row * a.os[1] + h * a.os[2];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const u32x2 w = {pack_bf16x2(st.o[dt][qt][4 * q4] * inv, st.o[dt][qt][4 * q4 + 1] * inv),
+                           pack_bf16x2(st.o[dt][qt][4 * q4 + 2] * inv,
+                                       st.o[dt][qt][4 * q4 + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * q4 + 4 * hh) = w;
+        }
+      if (a.lse && hh == 0)
+        a.lse[ml] = lsum > 0.f ? (mt + __log2f(lsum)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace yrb

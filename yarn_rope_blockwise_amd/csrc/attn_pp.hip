@@ -1,0 +1,279 @@
+// Exact blockwise softmax attention with RoPE on the query load, for gfx950:
+// the software-pipelined bf16 kernel.  It computes the same thing as the
+// kernel in attn.hip (per query row, softmax-weighted sum of the visible
+// values, keys folded in with a running max and running sum; the update of
+// "Ring attention" in the jovanaeducation guide and of "Ring Attention" in
+// the 14cs17 notes), with a different mapping onto the CU:
+//
+//  * One wave per SIMD (4 waves, 256 query rows per workgroup), each wave
+//    owning 64 rows as two 32-row query tiles.  Every K/V fragment read from
+//    LDS then feeds twice the MFMA work it does with 32 rows per wave, which
+//    halves LDS read traffic per flop; the wave holds up to 512 registers.
+//  * With a single wave on the SIMD, MFMA and softmax VALU work overlap only
+//    inside the wave.  The two query tiles are run half a step apart:
+//        H1(q): MFMA  S1(q) = K(q) Q1^T,  O1 += V(q-1)^T P1(q-1)
+//               VALU  softmax of S0(q) -> P0(q)
+//        H2(q): MFMA  S0(q+1) = K(q+1) Q0^T,  O0 += V(q)^T P0(q)
+//               VALU  softmax of S1(q) -> P1(q)
+//    (q counts 32-key quarters), so the MFMAs of each half are independent
+//    of the VALU work beside them.  The LDS reads of K(q+1) and V(q) are
+//    issued in H1(q), a half step ahead of their use.
+//  * The softmax of a quarter is branch-free: when the running max grows by
+//    more than the lazy-rescale threshold, l and m move at once and the
+//    O-accumulator rescale is applied at the boundary between half steps,
+//    after the last product into that accumulator under the old max.
+//  * Key tiles of 64 go global -> LDS with LDS-DMA into four buffers, two
+//    tiles ahead, with one workgroup barrier per tile.  Tiles visible to
+//    every row of the workgroup run through the pipeline; the few tiles on
+//    the causal diagonal or at the ragged end of the keys are folded
+//    afterwards, masked, by the plain per-quarter loop.
+#include "attn_frag.h"
+#include "common.h"
+#include "kernels.h"
+
+#include <type_traits>
+
+namespace yrb {
+
+namespace {
+
+constexpr int kPPWaves = 4;    // one per SIMD
+constexpr int kPPBN = 64;      // keys per tile (two quarters)
+constexpr int kPPBufs = 4;     // LDS tile buffers (power of two)
+
+// S^T of 32 keys against one 32-row query tile.
+template <int D>
+__device__ __forceinline__ f32x16 qk_tile(const bf16x8 (&kf)[D / 16], const bf16x8 (&q)[D / 16]) {
+  f32x16 s = {};
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], q[ds], s, 0, 0, 0);
+  return s;
+}
+
+// O^T += V^T P^T for 32 keys and query tile QT.
+template <int D, int QT>
+__device__ __forceinline__ void pv_tile(const bf16x8 (&vf)[2][D / 32], const bf16x8 (&pf)[2],
+                                        WaveState<D, 2>& st) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      st.o[dt][QT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][dt], pf[half], st.o[dt][QT], 0, 0, 0);
+}
+
+// Online-softmax update of query tile QT over 32 keys that are all visible,
+// with no branch.  Returns the factor the O accumulator of the tile still
+// has to be multiplied by (1 when the max the exponentials use is kept).
+// The row sum is taken over the bf16-rounded P the product uses.
+template <int D, int QT>
+__device__ __forceinline__ float softmax_open(const f32x16& s, WaveState<D, 2>& st, float scale_log2,
+                                              bf16x8 (&pf)[2]) {
+  float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int j = 2; j < 16; ++j) mx = fmaxf(mx, s[j]);
+  mx = pair_max(mx) * scale_log2;   // scale > 0 commutes with max
+  const float mt = fmaxf(st.m_true[QT], mx);
+  st.m_true[QT] = mt;
+  const float mu_old = st.m_use[QT];
+  const bool grow = mt > mu_old + kTau;
+  const float mu = grow ? mt : mu_old;
+  const float alpha = grow ? fast_exp2(mu_old - mu) : 1.0f;
+  st.m_use[QT] = mu;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float acc = st.l[QT] * alpha;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    u32x4 w;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = 8 * half + 2 * u;
+      // The pair is packed into its own bf16x2 before the dot product: taking
+      // it as an element of the u32x4 miscompiled (every dot2 read element 0).
+      const bf16x2 pp = {(__bf16)fast_exp2(__builtin_fmaf(s[j], scale_log2, -mu)),
+                         (__bf16)fast_exp2(__builtin_fmaf(s[j + 1], scale_log2, -mu))};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
+      w[u] = __builtin_bit_cast(unsigned, pp);
+    }
+    pf[half] = __builtin_bit_cast(bf16x8, w);
+  }
+  st.l[QT] = acc;
+  return alpha;
+}
+
+// Deferred O rescale of query tile QT (rare: only when its max moved).
+template <int D, int QT>
+__device__ __forceinline__ void rescale_o(WaveState<D, 2>& st, float alpha) {
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) st.o[dt][QT] *= alpha;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs a, int64_t n_qtiles) {
+  constexpr int NW = kPPWaves, BN = kPPBN, QW = 64, BM = NW * QW;
+  constexpr int NDS = D / 16, NDT = D / 32;
+  using T = Tile<D, BN>;
+  using TL = TileLoads<D, BN, NW>;
+  static_assert(TL::EXTRA == 0, "tile DMA must split evenly over the waves");
+  constexpr int DMA = 2 * TL::LO;   // LDS-DMA instructions per wave per tile (K and V)
+
+  // kPPBufs x [K tile, V tile] (dynamic LDS).
+  extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
+  YRB_LDS char* const lds = (YRB_LDS char*)lds_raw;
+  auto kbuf = [&](int t) -> YRB_LDS char* { return lds + (t & (kPPBufs - 1)) * 2 * T::TILEB; };
+  auto vbuf = [&](int t) -> YRB_LDS char* { return kbuf(t) + T::TILEB; };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31;
+  const WorkItem wi = work_item(a, n_qtiles);
+  const int b = wi.b, h = wi.h, hk = wi.hk, qtile = wi.qtile;
+  const int q0w = qtile * BM + wave * QW;
+  const int Sq = (int)a.Sq, Sk = (int)a.Sk;
+  const int q_offset = (int)a.q_offset, k_offset = (int)a.k_offset;
+
+  bf16x8 qf[2][NDS];
+  load_q<D, 2>(a, b, h, q0w, lane, qf);
+  // Q stays in AGPRs for the whole launch (an MFMA reads its A/B operands
+  // from either register file); VGPRs hold O, S, P and the addresses.
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) asm volatile("" : "+a"(qf[t][ds]));
+  WaveState<D, 2> st;
+  init_state<D, 2>(a, b, h, q0w, lane, st);
+
+  // Key tiles: n_tiles reach the workgroup's last visible key; the first
+  // n_full are visible to every row of the workgroup and hold no key past Sk.
+  const int q_first_wg = q_offset + qtile * BM;
+  const int q_last_wg = q_offset + min(Sq, (qtile + 1) * BM) - 1;
+  int n_keys = Sk;
+  if (a.causal) n_keys = max(0, min(Sk, q_last_wg - k_offset + 1));
+  const int n_tiles = (n_keys + BN - 1) / BN;
+  int n_full = min(n_tiles, Sk / BN);
+  if (a.causal) n_full = min(n_full, max(0, q_first_wg - k_offset + 1) / BN);
+  const int qw_first = q_offset + q0w;
+  const int qw_last = q_offset + min(Sq, q0w + QW) - 1;
+  const bool wave_live = q0w < Sq;
+  const float scale_log2 = a.softmax_scale * kLog2e;
+
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(a.k) + b * a.ks[0] + hk * a.ks[2];
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(a.v) + b * a.vs[0] + hk * a.vs[2];
+  const int kstride = (int)a.ks[1], vstride = (int)a.vs[1];
+
+  // Q, table and state loads complete here, so the only vector-memory
+  // operations in flight below are the tile DMAs.
+  wait_vmcnt<0>();
+
+  auto issue = [&](int t) {
+    load_tile<D, BN, NW, false>(kbuf(t), kbase, kstride, t * BN, Sk, wave, lane);
+    load_tile<D, BN, NW, true>(vbuf(t), vbase, vstride, t * BN, Sk, wave, lane);
+  };
+  // Before the first LDS read of tile t: this wave's DMA of tile t is done
+  // (only tile t+1's may still be in flight), the barrier extends that to
+  // every wave and certifies that every wave is past its reads of tile t-2,
+  // whose buffer then takes tile t+2.
+  auto arrive = [&](int t) {
+    if (t + 1 < n_tiles) wait_vmcnt<DMA>();
+    else wait_vmcnt<0>();
+    tile_barrier();
+    if (t + 2 < n_tiles) issue(t + 2);
+  };
+  if (n_tiles > 0) issue(0);
+  if (n_tiles > 1) issue(1);
+
+  if (n_full > 0) {
+    bf16x8 kf[2][NDS];        // K(q) by quarter parity
+    bf16x8 vf[2][2][NDT];     // V(q) by quarter parity
+    bf16x8 p0[2], p1[2];
+    f32x16 s0, s1;
+    // The product of the quarter before the first is a no-op: P = V = 0.
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      p1[half] = (bf16x8){};
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vf[1][half][dt] = (bf16x8){};
+    }
+    arrive(0);
+    read_k_quarter<D>(kbuf(0), 0, lane, kf[0]);
+    s0 = qk_tile<D>(kf[0], qf[0]);
+
+    // Quarters 2t and 2t+1 of tile t; LAST: no tile follows in the pipeline.
+    auto tile = [&](int t, auto last_tag) {
+      constexpr bool LAST = decltype(last_tag)::value;
+      float al;
+      // H1(2t)
+      read_k_quarter<D>(kbuf(t), 1, lane, kf[1]);
+      read_v_quarter<D>(vbuf(t), 0, lane, vf[0]);
+      s1 = qk_tile<D>(kf[0], qf[1]);
+      pv_tile<D, 1>(vf[1], p1, st);
+      al = softmax_open<D, 0>(s0, st, scale_log2, p0);
+      rescale_o<D, 0>(st, al);
+      // H2(2t)
+      s0 = qk_tile<D>(kf[1], qf[0]);
+      pv_tile<D, 0>(vf[0], p0, st);
+      al = softmax_open<D, 1>(s1, st, scale_log2, p1);
+      rescale_o<D, 1>(st, al);
+      if constexpr (!LAST) arrive(t + 1);
+      // H1(2t+1)
+      if constexpr (!LAST) read_k_quarter<D>(kbuf(t + 1), 0, lane, kf[0]);
+      read_v_quarter<D>(vbuf(t), 1, lane, vf[1]);
+      s1 = qk_tile<D>(kf[1], qf[1]);
+      pv_tile<D, 1>(vf[0], p1, st);
+      al = softmax_open<D, 0>(s0, st, scale_log2, p0);
+      rescale_o<D, 0>(st, al);
+      // H2(2t+1)
+      if constexpr (!LAST) s0 = qk_tile<D>(kf[0], qf[0]);
+      pv_tile<D, 0>(vf[1], p0, st);
+      al = softmax_open<D, 1>(s1, st, scale_log2, p1);
+      rescale_o<D, 1>(st, al);
+    };
+    for (int t = 0; t + 1 < n_full; ++t) tile(t, std::false_type{});
+    tile(n_full - 1, std::true_type{});
+    pv_tile<D, 1>(vf[1], p1, st);
+  }
+
+  // Diagonal and ragged tiles: masked, per wave, skipping tiles wholly in
+  // the wave's future (the barrier sequence stays the same for all waves).
+  for (int t = n_full; t < n_tiles; ++t) {
+    arrive(t);
+    const int k0 = t * BN;
+    const int kpos0 = k_offset + k0;
+    const bool skip = !wave_live || (a.causal && kpos0 > qw_last);
+    if (!skip) {
+      const bool need_mask = (a.causal && kpos0 + BN - 1 > qw_first) || (k0 + BN > Sk);
+      fold_tile<D, BN, 2>(kbuf(t), vbuf(t), qf, st, need_mask, k0, Sk, kpos0, qw_first + l32,
+                          a.causal != 0, scale_log2, lane);
+    }
+  }
+
+  if (!wave_live) return;
+  finish_rows<D, 2>(a, b, h, q0w, lane, st);
+}
+
+template <int D>
+hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
+  constexpr int BM = kPPWaves * 64;
+  constexpr int LDS_BYTES = kPPBufs * 2 * Tile<D, kPPBN>::TILEB;
+  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
+  const int64_t n_qtiles = (a.Sq + BM - 1) / BM;
+  const int64_t blocks = n_qtiles * a.B * a.Hq;
+  if (blocks == 0) return hipSuccess;
+  if (LDS_BYTES > 65536) {   // above the default dynamic-LDS limit
+    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_pp_kernel<D>),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (attr != hipSuccess) return attr;
+  }
+  hipLaunchKernelGGL((attn_bf16_pp_kernel<D>), dim3((unsigned)blocks), dim3(kPPWaves * 64), LDS_BYTES,
+                     stream, a, n_qtiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_bf16_pp(int D, const AttnArgs& a, hipStream_t stream) {
+  return D == 64 ? launch_pp<64>(a, stream) : launch_pp<128>(a, stream);
+}
+
+}  // namespace yrb

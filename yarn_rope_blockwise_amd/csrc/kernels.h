@@ -48,6 +48,8 @@ struct AttnArgs {
   int finalize;                  // write o (and lse) at the end
 };
 hipError_t launch_attention(int dtype, int D, const AttnArgs& a, hipStream_t stream);
+// The software-pipelined bf16 kernel (attn_pp.hip); called by launch_attention.
+hipError_t launch_attention_bf16_pp(int D, const AttnArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
   const void* q;
