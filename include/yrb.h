@@ -21,8 +21,9 @@
  *  - Arguments are validated on the host before anything is queued: a
  *    negative return means nothing was launched and nothing was written.
  *  - Tensors are token-major [batch][token][head][dim] with the dim stride
- *    equal to 1; the other strides are given in elements.  Base pointers
- *    must be 16-byte aligned and strides multiples of 16 bytes.
+ *    equal to 1; the other strides are given in elements, each in
+ *    [0, 2^31) (else YRB_EINVAL).  Base pointers must be 16-byte aligned and
+ *    strides multiples of 16 bytes (else YRB_EALIGN).
  *  - dtype: YRB_BF16 (bfloat16 storage, fp32 arithmetic, bf16 MFMA for the
  *    products) or YRB_F32 (fp32 storage and arithmetic).
  *  - head_dim must be 64 or 128.

@@ -114,6 +114,7 @@ def test_rope_apply_validation():
     assert call(off=1) == EINVAL                                         # off + S > rows
     assert call(B=-1) == EINVAL
     assert call(B=0) == OK                                               # nothing to do
+    assert call(ys=_strides(8 * 128 * 32, 1 << 31, 128)) == EINVAL       # stride >= 2^31 elements
 
 
 def _prefill(**over):
@@ -138,6 +139,9 @@ def test_prefill_validation():
     assert _prefill(cs=MISALIGNED) == EALIGN
     assert _prefill(rows=63) == EINVAL         # table shorter than S
     assert _prefill(o=MISALIGNED) == EALIGN
+    big = 1 << 31                              # strides are indexed in 32 bits
+    assert _prefill(strides=_strides(*([64 * 4 * 128, big, 128] + [64 * 4 * 128, 4 * 128, 128] * 3))) == EINVAL
+    assert _prefill(strides=_strides(*([64 * 4 * 128, 4 * 128, 128] * 3 + [-128, 4 * 128, 128]))) == EINVAL
     assert _prefill(lse=MISALIGNED) == EALIGN
     assert _prefill(S=0) == OK
     assert _prefill(B=0) == OK

@@ -32,9 +32,10 @@ bool strides_aligned(const int64_t* s, int n, int32_t dtype) {
     if (s[i] % q != 0) return false;
   return true;
 }
+// Non-negative and below 2^31 elements (the kernels index rows in 32 bits).
 bool strides_nonneg(const int64_t* s, int n) {
   for (int i = 0; i < n; ++i)
-    if (s[i] < 0) return false;
+    if (s[i] < 0 || s[i] >= (int64_t(1) << 31)) return false;
   return true;
 }
 

@@ -94,6 +94,54 @@ __device__ __forceinline__ void load_tile(YRB_LDS char* dst, const __bf16* src, 
   }
 }
 
+// Tiles that need no row clamp: each lane's byte offsets (relative to the
+// tile's first row) of its 16-byte chunks in this wave's share of the DMA,
+// fixed for the whole launch; the tile's row base then goes in SGPRs.
+template <int D, int BN, int NW, bool IS_V>
+__device__ __forceinline__ void tile_offsets(int stride, int wave, int lane,
+                                             unsigned (&off)[TileLoads<D, BN, NW>::LO]) {
+  using TL = TileLoads<D, BN, NW>;
+  static_assert(TL::EXTRA == 0, "tile DMA must split evenly over the waves");
+  constexpr int ROWB = Tile<D, BN>::ROWB;
+#pragma unroll
+  for (int n = 0; n < TL::LO; ++n) {
+    const int o = (n * NW + wave) * 1024 + lane * 16;
+    const int r = o / ROWB;
+    const int p = (o % ROWB) >> 4;
+    const int c = IS_V ? (p ^ vsw<D>(r)) : (p ^ ksw<D>(r));
+    off[n] = (unsigned)(r * stride + c * 8) * 2u;
+  }
+}
+
+// A pointer the caller knows to be the same in every lane, moved to SGPRs.
+__device__ __forceinline__ const __bf16* wave_uniform(const __bf16* p) {
+  // readfirstlane works on int: each half is taken back as unsigned before
+  // widening, so the low half is zero-extended, not sign-extended.
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));
+  return reinterpret_cast<const __bf16*>((uintptr_t)(lo | (hi << 32)));
+}
+
+template <int D, int BN, int NW>
+__device__ __forceinline__ void load_tile_rows(YRB_LDS char* dst, const __bf16* tile_rows,
+                                               const unsigned (&off)[TileLoads<D, BN, NW>::LO],
+                                               int wave) {
+  using TL = TileLoads<D, BN, NW>;
+  const __bf16* const rows = wave_uniform(tile_rows);
+#pragma unroll
+  for (int n = 0; n < TL::LO; ++n) {
+    const unsigned m0v = (unsigned)(uintptr_t)(dst + (n * NW + wave) * 1024);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved; nothing else here uses it
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off[n]), "s"(rows), "s"(m0v)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+  }
+}
+
 template <int D, int NQT>
 struct WaveState {
   f32x16 o[D / 32][NQT];
@@ -292,11 +340,11 @@ __device__ __forceinline__ WorkItem work_item(const AttnArgs& a, int64_t n_qtile
 
 // Query fragments (B operand of S^T = K Q^T) of one wave: lane holds query
 // row q0w + 32qt + l32 (clamped to the last row), dims 16ds + 8hh .. +7,
-// rotated here in fp32 from the table when one is given and rounded once to
-// bf16.
+// rotated here in fp32 from the table when one is given, multiplied by
+// qscale, and rounded once to bf16.
 template <int D, int NQT>
 __device__ __forceinline__ void load_q(const AttnArgs& a, int b, int h, int q0w, int lane,
-                                       bf16x8 (&qf)[NQT][D / 16]) {
+                                       bf16x8 (&qf)[NQT][D / 16], float qscale = 1.0f) {
   constexpr int NDS = D / 16;
   const int hh = lane >> 5;
   const int l32 = lane & 31;
@@ -311,6 +359,7 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int b, int h, int q0w,
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) raw[ds] = *reinterpret_cast<const u32x4*>(qp + 16 * ds);
     if (a.cos_sin) {
+      // pair (i, i + D/2) of the rotation sits in fragments ds and ds + NDS/2
       const float* cs = a.cos_sin + (int64_t)(q_offset + row) * D;
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds) {
@@ -322,13 +371,22 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int b, int h, int q0w,
 #pragma unroll
         for (int u2 = 0; u2 < 4; ++u2) {
           const f32x4 tt = t[u2];
-          lo[2 * u2] = x[2 * u2] * tt[0] - z[2 * u2] * tt[1];
-          hi[2 * u2] = x[2 * u2] * tt[1] + z[2 * u2] * tt[0];
-          lo[2 * u2 + 1] = x[2 * u2 + 1] * tt[2] - z[2 * u2 + 1] * tt[3];
-          hi[2 * u2 + 1] = x[2 * u2 + 1] * tt[3] + z[2 * u2 + 1] * tt[2];
+          lo[2 * u2] = (x[2 * u2] * tt[0] - z[2 * u2] * tt[1]) * qscale;
+          hi[2 * u2] = (x[2 * u2] * tt[1] + z[2 * u2] * tt[0]) * qscale;
+          lo[2 * u2 + 1] = (x[2 * u2 + 1] * tt[2] - z[2 * u2 + 1] * tt[3]) * qscale;
+          hi[2 * u2 + 1] = (x[2 * u2 + 1] * tt[3] + z[2 * u2 + 1] * tt[2]) * qscale;
         }
         raw[ds] = pack8(lo);
         raw[ds + NDS / 2] = pack8(hi);
+      }
+    } else if (qscale != 1.0f) {
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        float x[8];
+        unpack8(raw[ds], x);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] *= qscale;
+        raw[ds] = pack8(x);
       }
     }
 #pragma unroll
