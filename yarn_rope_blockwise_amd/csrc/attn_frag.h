@@ -150,19 +150,21 @@ struct WaveState {
   float l[NQT];        // per-lane partial row sum (this half's keys)
 };
 
-// K fragments (A operand of S^T = K Q^T) of quarter kq: lane holds key
+// One K fragment (A operand of S^T = K Q^T) of quarter kq: lane holds key
 // 32kq + l32, dims 16ds + 8hh .. +7.
+template <int D>
+__device__ __forceinline__ bf16x8 read_k_frag(const YRB_LDS char* kt_lds, int kq, int lane, int ds) {
+  constexpr int ROWB = D * 2;
+  const int r = kq * 32 + (lane & 31);
+  const int c = 2 * ds + (lane >> 5);
+  return *reinterpret_cast<const YRB_LDS bf16x8*>(kt_lds + r * ROWB + ((c ^ ksw<D>(r)) << 4));
+}
+
 template <int D>
 __device__ __forceinline__ void read_k_quarter(const YRB_LDS char* kt_lds, int kq, int lane,
                                                bf16x8 (&kf)[D / 16]) {
-  constexpr int ROWB = D * 2;
-  const int hh = lane >> 5;
-  const int r = kq * 32 + (lane & 31);
 #pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds) {
-    const int c = 2 * ds + hh;
-    kf[ds] = *reinterpret_cast<const YRB_LDS bf16x8*>(kt_lds + r * ROWB + ((c ^ ksw<D>(r)) << 4));
-  }
+  for (int ds = 0; ds < D / 16; ++ds) kf[ds] = read_k_frag<D>(kt_lds, kq, lane, ds);
 }
 
 // S^T for 32 keys against the wave's queries:
@@ -179,37 +181,41 @@ __device__ __forceinline__ void qk_mfma(const bf16x8 (&kf)[D / 16],
       s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[qt][ds], s[qt], 0, 0, 0);
 }
 
-// V^T fragments (A operand of O^T += V^T P^T) of quarter kq.  Lane i
-// supplies the address of V[row][d..d+3] with row = 16ks + 8*second +
-// 4(i/32) + (i%16)/4 and d = 32dt + 16((i/16)%2) + 4(i%4);
-// ds_read_b64_tr_b16 hands lane l the column d = 32dt + l%32 over keys
-// 16ks + 8*second + 4(l/32) + 0..3, the key order the packed P uses.
+// One V^T fragment (A operand of O^T += V^T P^T) of quarter kq: k-step
+// 2kq + half, d tile dt.  Lane i supplies the address of V[row][d..d+3]
+// with row = 16ks + 8*second + 4(i/32) + (i%16)/4 and d = 32dt +
+// 16((i/16)%2) + 4(i%4); ds_read_b64_tr_b16 hands lane l the column
+// d = 32dt + l%32 over keys 16ks + 8*second + 4(l/32) + 0..3, the key order
+// the packed P uses.
 template <int D>
-__device__ __forceinline__ void read_v_quarter(const YRB_LDS char* vt_lds, int kq, int lane,
-                                               bf16x8 (&vf)[2][D / 32]) {
+__device__ __forceinline__ bf16x8 read_v_frag(const YRB_LDS char* vt_lds, int kq, int lane, int half,
+                                              int dt) {
   constexpr int ROWB = D * 2;
   const int g = lane >> 4;
   const int t4 = (lane & 15) >> 2;
   const int s4 = lane & 3;
+  const int ks = 2 * kq + half;
+  const int row1 = 16 * ks + 4 * (g >> 1) + t4;
+  const int row2 = row1 + 8;
+  const int c = dt * 4 + 2 * (g & 1) + (s4 >> 1);
+  const int boff = 8 * (s4 & 1);
+  const YRB_LDS char* a1 = vt_lds + row1 * ROWB + ((c ^ vsw<D>(row1)) << 4) + boff;
+  const YRB_LDS char* a2 = vt_lds + row2 * ROWB + ((c ^ vsw<D>(row2)) << 4) + boff;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a1);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a2);
+  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+  const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+  const u32x4 vw = {lo2[0], lo2[1], hi2[0], hi2[1]};
+  return __builtin_bit_cast(bf16x8, vw);
+}
+
+template <int D>
+__device__ __forceinline__ void read_v_quarter(const YRB_LDS char* vt_lds, int kq, int lane,
+                                               bf16x8 (&vf)[2][D / 32]) {
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int ks = 2 * kq + half;
-    const int row1 = 16 * ks + 4 * (g >> 1) + t4;
-    const int row2 = row1 + 8;
+  for (int half = 0; half < 2; ++half)
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const int c = dt * 4 + 2 * (g & 1) + (s4 >> 1);
-      const int boff = 8 * (s4 & 1);
-      const YRB_LDS char* a1 = vt_lds + row1 * ROWB + ((c ^ vsw<D>(row1)) << 4) + boff;
-      const YRB_LDS char* a2 = vt_lds + row2 * ROWB + ((c ^ vsw<D>(row2)) << 4) + boff;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a1);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a2);
-      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-      const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-      const u32x4 vw = {lo2[0], lo2[1], hi2[0], hi2[1]};
-      vf[half][dt] = __builtin_bit_cast(bf16x8, vw);
-    }
-  }
+    for (int dt = 0; dt < D / 32; ++dt) vf[half][dt] = read_v_frag<D>(vt_lds, kq, lane, half, dt);
 }
 
 template <int D, int NQT>
@@ -225,10 +231,31 @@ __device__ __forceinline__ void pv_mfma(const bf16x8 (&vf)[2][D / 32], const bf1
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][dt], pf[half][qt], st.o[dt][qt], 0, 0, 0);
 }
 
+// O^T(AGPR) += V^T P^T for one 32x32x16 step, as inline asm so that the
+// accumulator stays in AGPRs while the compiler keeps its own MFMAs in the
+// VGPR form.  The compiler does not see this MFMA: VALU code that touches
+// the accumulator next to it waits out the hazards itself (xdl_drain before
+// reading it, s_nop after writing it).
+__device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& v, const bf16x8& p) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
+}
+
+// Wait states after the inline-asm MFMAs before VALU code reads or writes
+// their accumulators (more than the longest MFMA-to-VALU requirement).
+__device__ __forceinline__ void xdl_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// O *= alpha on an accumulator that lives in AGPRs, between inline-asm MFMAs.
+__device__ __forceinline__ void scale_o_agpr(f32x16& o, float alpha) {
+  xdl_drain();
+  o *= alpha;
+  asm volatile("" : "+a"(o));
+  asm volatile("s_nop 4" ::: "memory");
+}
+
 // Online-softmax update for one quarter: mask, row max, (rare) rescale,
 // P = exp2(s * scale_log2 - m_use) packed to bf16 as the B operand of
 // O^T += V^T P^T (k-step 2kq + half takes j = 8*half .. 8*half+7).
-template <int D, int NQT>
+template <int D, int NQT, bool ASM_O = false>
 __device__ __forceinline__ void softmax_quarter(f32x16 (&s)[NQT], WaveState<D, NQT>& st,
                                                 bool need_mask, int kk0, int Sk, int kpos_base,
                                                 int qpos_lane0, bool causal, float scale_log2,
@@ -264,7 +291,10 @@ __device__ __forceinline__ void softmax_quarter(f32x16 (&s)[NQT], WaveState<D, N
       if (mn != -INFINITY) {
         st.l[qt] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) st.o[dt][qt] *= alpha;
+        for (int dt = 0; dt < D / 32; ++dt) {
+          if (ASM_O) scale_o_agpr(st.o[dt][qt], alpha);
+          else st.o[dt][qt] *= alpha;
+        }
         st.m_use[qt] = mn;
       }
     }
@@ -295,7 +325,8 @@ __device__ __forceinline__ void softmax_quarter(f32x16 (&s)[NQT], WaveState<D, N
 // on the VALU, then O^T += V^T P^T.  With two waves per SIMD the matrix
 // core of one wave's MFMAs overlaps the other wave's softmax.  (Explicitly
 // pipelining quarters inside a wave measured no faster on gfx950.)
-template <int D, int BN, int NQT>
+// ASM_O: O lives in AGPRs and the PV products are the inline-asm MFMAs.
+template <int D, int BN, int NQT, bool ASM_O = false>
 __device__ __forceinline__ void fold_tile(const YRB_LDS char* kt_lds, const YRB_LDS char* vt_lds,
                                           const bf16x8 (&qf)[NQT][D / 16],
                                           WaveState<D, NQT>& st, bool need_mask, int k0, int Sk,
@@ -308,11 +339,20 @@ __device__ __forceinline__ void fold_tile(const YRB_LDS char* kt_lds, const YRB_
     read_k_quarter<D>(kt_lds, kq, lane, kf);
     qk_mfma<D, NQT>(kf, qf, s);
     bf16x8 pf[2][NQT];
-    softmax_quarter<D, NQT>(s, st, need_mask, k0 + 32 * kq, Sk, kpos0 - k0, qpos_lane0, causal,
-                            scale_log2, lane, pf);
+    softmax_quarter<D, NQT, ASM_O>(s, st, need_mask, k0 + 32 * kq, Sk, kpos0 - k0, qpos_lane0, causal,
+                                   scale_log2, lane, pf);
     bf16x8 vf[2][D / 32];
     read_v_quarter<D>(vt_lds, kq, lane, vf);
-    pv_mfma<D, NQT>(vf, pf, st);
+    if (ASM_O) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int qt = 0; qt < NQT; ++qt) mfma_o(st.o[dt][qt], vf[half][dt], pf[half][qt]);
+    } else {
+      pv_mfma<D, NQT>(vf, pf, st);
+    }
   }
 }
 

@@ -10,18 +10,26 @@
 //    LDS then feeds twice the MFMA work it does with 32 rows per wave, which
 //    halves LDS read traffic per flop; the wave holds up to 512 registers.
 //  * With a single wave on the SIMD, MFMA and softmax VALU work overlap only
-//    inside the wave.  The two query tiles are run half a step apart:
-//        H1(q): MFMA  S1(q) = K(q) Q1^T,  O1 += V(q-1)^T P1(q-1)
-//               VALU  softmax of S0(q) -> P0(q)
-//        H2(q): MFMA  S0(q+1) = K(q+1) Q0^T,  O0 += V(q)^T P0(q)
-//               VALU  softmax of S1(q) -> P1(q)
-//    (q counts 32-key quarters), so the MFMAs of each half are independent
-//    of the VALU work beside them.  The LDS reads of K(q+1) and V(q) are
-//    issued in H1(q), a half step ahead of their use.
-//  * The softmax of a quarter is branch-free: when the running max grows by
-//    more than the lazy-rescale threshold, l and m move at once and the
-//    O-accumulator rescale is applied at the boundary between half steps,
-//    after the last product into that accumulator under the old max.
+//    inside the wave, and the wave issues one instruction per four cycles:
+//    the schedule is written out, one MFMA per issue step.  The two query
+//    tiles run half a step apart (q counts 32-key quarters):
+//        H1(q): MFMA  O1 += V(q-1)^T P1(q-1),  S1(q) = K(q) Q1^T
+//               VALU  softmax of S0(q) -> P0(q);  LDS  V(q)
+//        H2(q): MFMA  O0 += V(q)^T P0(q),      S0(q+1) = K(q+1) Q0^T
+//               VALU  softmax of S1(q) -> P1(q);  LDS  K(q+1)
+//    so the MFMAs of each half step are independent of the VALU work
+//    beside them, and every LDS read lands a half step before its use.
+//  * Scores come out of the MFMA in log2 units and offset by the running
+//    max (Q is pre-multiplied by softmax_scale * log2(e), and each S chain
+//    starts from minus that max), so the common softmax path is P = exp2(S).
+//    When a row max outgrows the lazy-rescale threshold, a rarely taken
+//    block at the half-step boundary redoes P against the new max and
+//    rescales O, after the last product into O under the old max.
+//  * O lives in AGPRs as the accumulator of the PV products, which are
+//    issued as inline-asm MFMAs (AGPR C/D, VGPR A/B); VGPRs hold S, P, the
+//    fragments and the offsets.  The compiler does not see those MFMAs, so
+//    the few places where VALU code touches O or P next to them wait out
+//    the MFMA hazards explicitly (xdl_drain, the s_nop after settle).
 //  * Key tiles of 64 go global -> LDS with LDS-DMA into four buffers, two
 //    tiles ahead, with one workgroup barrier per tile.  Tiles visible to
 //    every row of the workgroup run through the pipeline; the few tiles on
@@ -39,7 +47,7 @@ namespace {
 
 constexpr int kPPWaves = 4;    // one per SIMD
 constexpr int kPPBN = 64;      // keys per tile (two quarters)
-constexpr int kPPBufs = 4;     // LDS tile buffers (power of two)
+constexpr int kPPBufs = 4;     // LDS tile buffers (the tile loop is unrolled by this)
 
 // S^T of 32 keys against one 32-row query tile, accumulated onto `init`.
 template <int D>
@@ -51,17 +59,6 @@ __device__ __forceinline__ f32x16 qk_tile(const bf16x8 (&kf)[D / 16], const bf16
   return s;
 }
 
-// O^T += V^T P^T for 32 keys and query tile QT.
-template <int D, int QT>
-__device__ __forceinline__ void pv_tile(const bf16x8 (&vf)[2][D / 32], const bf16x8 (&pf)[2],
-                                        WaveState<D, 2>& st) {
-#pragma unroll
-  for (int half = 0; half < 2; ++half)
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-      st.o[dt][QT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][dt], pf[half], st.o[dt][QT], 0, 0, 0);
-}
-
 // IEEE maximum (v_maximum3_f32 on gfx950: no input canonicalisation).
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float pair_vmax(float x) {
@@ -69,22 +66,18 @@ __device__ __forceinline__ float pair_vmax(float x) {
   return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Sixteen copies of v, built as eight copies of a 64-bit pair (v_mov_b64).
 __device__ __forceinline__ f32x16 splat16(float v) {
-  typedef unsigned long long u64x8 __attribute__((ext_vector_type(8)));
-  const unsigned long long u = __float_as_uint(v);
-  const unsigned long long p = (u << 32) | u;
-  const u64x8 r = {p, p, p, p, p, p, p, p};
-  return __builtin_bit_cast(f32x16, r);
+  f32x16 r;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) r[j] = v;
+  return r;
 }
 
-// Scores come out of the MFMA already in log2 units (Q is pre-multiplied by
-// softmax_scale * log2(e)) and offset: each S chain starts from -base, base
-// being the max the exponentials use (0 while a row has none).  Then, as
-// long as no row max grows past that max by more than the threshold,
-// P = exp2(S) needs no per-element subtraction.
+// Offsets of the two query tiles: each S chain starts from negb = -base,
+// base being the max the exponentials use (0 while a row has none).
 struct Offsets {
-  float base[2];       // the S chains of the tile start from -base
+  f32x16 negb[2];
+  float base[2];
   float mu_tau[2];     // m_use + threshold
   float l_prev[2];     // row sum before the current quarter
 };
@@ -96,43 +89,9 @@ __device__ __forceinline__ void offsets_from(const WaveState<D, 2>& st, Offsets&
     const float mu = st.m_use[t];
     of.base[t] = mu == -INFINITY ? 0.f : mu;
     of.mu_tau[t] = mu + kTau;
+    of.negb[t] = splat16(-of.base[t]);
     of.l_prev[t] = st.l[t];
   }
-}
-
-// Common case of the online-softmax update of query tile QT over 32 keys
-// that are all visible: row max, exact running max, P = exp2(S) packed to
-// bf16 as the B operand of O^T += V^T P^T, and the row sum taken over the
-// bf16 values the product uses.  Returns whether the row max outgrew the
-// threshold, in which case settle() redoes P with a new max.
-template <int D, int QT>
-__device__ __forceinline__ bool softmax_fast(const f32x16& s, WaveState<D, 2>& st, Offsets& of,
-                                             bf16x8 (&pf)[2]) {
-  float mx = vmax(s[0], s[1]);
-#pragma unroll
-  for (int j = 2; j < 16; ++j) mx = vmax(mx, s[j]);
-  const float t1 = of.base[QT] + pair_vmax(mx);   // this quarter's row max
-  st.m_true[QT] = vmax(st.m_true[QT], t1);
-  const bool grow = t1 > of.mu_tau[QT];
-  of.l_prev[QT] = st.l[QT];
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float acc = st.l[QT];
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    u32x4 w;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = 8 * half + 2 * u;
-      // The pair is packed into its own bf16x2 before the dot product: taking
-      // it as an element of the u32x4 miscompiled (every dot2 read element 0).
-      const bf16x2 pp = {(__bf16)fast_exp2(s[j]), (__bf16)fast_exp2(s[j + 1])};
-      acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
-      w[u] = __builtin_bit_cast(unsigned, pp);
-    }
-    pf[half] = __builtin_bit_cast(bf16x8, w);
-  }
-  st.l[QT] = acc;
-  return grow;
 }
 
 // Rare case, at the boundary after the last product into O of tile QT under
@@ -143,9 +102,6 @@ template <int D, int QT>
 __device__ __forceinline__ void settle(const f32x16& s, WaveState<D, 2>& st, Offsets& of, bool grow,
                                        bf16x8 (&pf)[2]) {
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) == 0, 1)) return;
-  // A side effect, so the compiler keeps this block behind its branch rather
-  // than computing it on every quarter and selecting.
-  asm volatile("");
   const float mu_old = st.m_use[QT];
   const float mu_new = grow ? st.m_true[QT] : mu_old;
   const float shift = mu_new - of.base[QT];                          // 0 where kept
@@ -166,38 +122,208 @@ __device__ __forceinline__ void settle(const f32x16& s, WaveState<D, 2>& st, Off
   }
   st.l[QT] = acc;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) st.o[dt][QT] *= alpha;
+  for (int dt = 0; dt < D / 32; ++dt) scale_o_agpr(st.o[dt][QT], alpha);
   st.m_use[QT] = mu_new;
   of.base[QT] = mu_new == -INFINITY ? 0.f : mu_new;
   of.mu_tau[QT] = mu_new + kTau;
+  of.negb[QT] = splat16(-of.base[QT]);
+  // The next inline-asm MFMA may read this P at once.
+  asm volatile("s_nop 4" ::: "memory");
 }
 
-// Keep the computation of P inside its half step (a use of its registers
-// there, so nothing sinks it into the next block).
-#ifndef YRB_PP_FAST_DMA
-#define YRB_PP_FAST_DMA 1
-#endif
-__device__ __forceinline__ void keep(const bf16x8 (&pf)[2]) { asm volatile("" ::"v"(pf[0]), "v"(pf[1])); }
+// Pin a value to the current issue step: an empty volatile asm that reads
+// and writes it, ordered with the step fences, so the value is computed
+// within the step rather than wherever the instruction selector put it.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
 
-// Issue order of one half step: each MFMA followed by a few VALU
-// instructions (and, in H1, the LDS reads for the next half step), so the
-// VALU work and the reads go out while the matrix core is busy and no MFMA
-// waits on the one before it.  Masks: 0x008 MFMA, 0x002 VALU, 0x100 DS read.
-#ifndef YRB_PP_VALU_PER_MFMA
-#define YRB_PP_VALU_PER_MFMA 4
-#endif
-#ifndef YRB_PP_INTERLEAVE
-#define YRB_PP_INTERLEAVE 1
-#endif
-template <int NMFMA, int NDS_READ>
-__device__ __forceinline__ void interleave() {
-  if (!YRB_PP_INTERLEAVE) return;
+__device__ __forceinline__ void pack_pair(const float (&p)[16], int u, unsigned (&w)[8]) {
+  const bf16x2 pp = {(__bf16)p[2 * u], (__bf16)p[2 * u + 1]};
+  w[u] = __builtin_bit_cast(unsigned, pp);
+  pin(w[u]);
+}
+// A pair enters the dot product as its own bf16x2: taking it from a vector
+// element once miscompiled (every dot2 read element 0).
+__device__ __forceinline__ void add_pair(const unsigned (&w)[8], int u, bf16x2 ones, float& acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[u]), ones, acc, false);
+  pin(acc);
+}
+
+// LDS layout of the pipeline: the kPPBufs K tiles, then the kPPBufs V tiles.
+// Every fragment read is a per-lane base register (fixed for the launch)
+// plus an immediate for buffer, quarter and k-step, so the reads need no
+// address arithmetic.  The swizzles repeat every 16 rows, which keeps each
+// lane's swizzle the same for every quarter and k-step.
+template <int D>
+struct LdsMap {
+  static constexpr int TILEB = Tile<D, kPPBN>::TILEB;
+  static constexpr int ROWB = Tile<D, kPPBN>::ROWB;
+  static constexpr int VBASE = kPPBufs * TILEB;
+  unsigned k[D / 16];   // K fragment ds: quarter 0 of buffer 0
+  unsigned v[D / 32];   // V fragment dt: first transposed read, k-step 0 of buffer 0
+};
+
+template <int D>
+__device__ __forceinline__ LdsMap<D> lds_map(int lane) {
+  using M = LdsMap<D>;
+  LdsMap<D> m;
+  const int r = lane & 31, hh = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < NMFMA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < (NDS_READ + 1) / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, YRB_PP_VALU_PER_MFMA, 0);
+  for (int ds = 0; ds < D / 16; ++ds) m.k[ds] = r * M::ROWB + (((2 * ds + hh) ^ ksw<D>(r)) << 4);
+  const int g = lane >> 4, t4 = (lane & 15) >> 2, s4 = lane & 3;
+  const int row = 4 * (g >> 1) + t4;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int c = dt * 4 + 2 * (g & 1) + (s4 >> 1);
+    m.v[dt] = M::VBASE + row * M::ROWB + ((c ^ vsw<D>(row)) << 4) + 8 * (s4 & 1);
   }
+  return m;
+}
+
+template <int D, int B, int KQ>
+__device__ __forceinline__ bf16x8 read_k_at(const YRB_LDS char* lds, const LdsMap<D>& m, int ds) {
+  using M = LdsMap<D>;
+  return *reinterpret_cast<const YRB_LDS bf16x8*>(lds + m.k[ds] + (B * M::TILEB + KQ * 32 * M::ROWB));
+}
+
+template <int D, int B, int KQ>
+__device__ __forceinline__ bf16x8 read_v_at(const YRB_LDS char* lds, const LdsMap<D>& m, int half, int dt) {
+  using M = LdsMap<D>;
+  const YRB_LDS char* a1 = lds + m.v[dt] + (B * M::TILEB + (2 * KQ + half) * 16 * M::ROWB);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a1);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)(a1 + 8 * M::ROWB));
+  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+  const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+  const u32x4 vw = {lo2[0], lo2[1], hi2[0], hi2[1]};
+  return __builtin_bit_cast(bf16x8, vw);
+}
+
+// One of the two transposed 64-bit reads of a V fragment (second: the
+// k-step's keys 8..15).
+template <int D, int B, int KQ>
+__device__ __forceinline__ u32x2 read_v_part(const YRB_LDS char* lds, const LdsMap<D>& m, int half, int dt,
+                                             int second) {
+  using M = LdsMap<D>;
+  const YRB_LDS char* a = lds + m.v[dt] + (B * M::TILEB + (2 * KQ + half) * 16 * M::ROWB + second * 8 * M::ROWB);
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a));
+}
+
+// Issue steps of a half step (NS = 2 * D/16), as compile-time functions.
+// The softmax of the other tile runs in steps W0 .. NS-1: its scores come
+// from the S chain that ended the previous half step, whose last MFMA has
+// then had W0 steps to finish.
+template <int D>
+struct Steps {
+  static constexpr int NS = D / 8;
+  static constexpr int W0 = 2;
+  static constexpr int exp_at(int j) { return W0 + (j * (NS - W0)) / 16; }
+  static constexpr int max_at(int k) { return W0 + (k * (NS - W0)) / 8; }
+  static constexpr int pack_at(int u) { return exp_at(2 * u + 1) + 1; }
+  static constexpr int dot_at(int u) { return pack_at(u) + 1; }
+  static constexpr int final_at() { return max_at(7) + 1; }
+};
+
+// One half step, kept in order by sched_barrier(0) between issue steps.
+// Step i issues one MFMA (tile Y: the PV products in steps 0 .. NDS-1 on
+// vf, then the S chain on kf), one LDS fragment read (V in the second half
+// of H1, over the fragments the PV products just consumed; K in the first
+// half of H2, ahead of the S chain that uses them), and its share of tile
+// X's softmax: exps, the max chain, packs of finished pairs and the row sum.
+// In the common case (no row max outgrew the threshold) tile X's softmax is
+// then complete.  Returns whether any row grew, for settle().
+template <int D, int Y, int BV, int KQV, int BK, int KQK, bool READ_V, bool READ_K>
+__device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, const YRB_LDS char* lds,
+                                          const LdsMap<D>& m, bf16x8 (&vf)[2][D / 32],
+                                          const bf16x8 (&p_pv)[2], bf16x8 (&kf)[D / 16],
+                                          const bf16x8 (&q_s)[D / 16], f32x16& s_y, const f32x16& s_x,
+                                          bf16x8 (&p_x)[2]) {
+  constexpr int X = 1 - Y;
+  constexpr int NDS = D / 16, NDT = D / 32;
+  using S = Steps<D>;
+  constexpr int NS = S::NS;
+  const float base_x = of.base[X];
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float acc = st.l[X];
+  of.l_prev[X] = acc;
+  float p[16];
+  unsigned w[8];
+  float mx = 0.f;
+  bool grow = false;
+  u32x2 vlo[NDS];
+  // O stays in AGPRs (a no-op when the register allocator already has it there)
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(st.o[dt][t]));
+  auto finish_max = [&]() {
+    const float t1 = base_x + pair_vmax(mx);   // this quarter's row max
+    st.m_true[X] = vmax(st.m_true[X], t1);
+    grow = t1 > of.mu_tau[X];
+    pin(st.m_true[X]);
+  };
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    // MFMA
+    if (i < NDS) {
+      mfma_o(st.o[i % NDT][Y], vf[i / NDT][i % NDT], p_pv[i / NDT]);
+    } else {
+      const int ds = i - NDS;
+      s_y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], q_s[ds], ds == 0 ? of.negb[Y] : s_y, 0, 0, 0);
+    }
+    // LDS fragment reads
+    // V fragment f: its first read right after the PV product that used the
+    // old fragment f (step f), its second NDS - 1 steps later
+    if (READ_V) {
+#pragma unroll
+      for (int f = 0; f < NDS; ++f) {
+        if (i == f + 1) vlo[f] = read_v_part<D, BV, KQV>(lds, m, f / NDT, f % NDT, 0);
+        if (i == f + NDS) {
+          const u32x2 hi = read_v_part<D, BV, KQV>(lds, m, f / NDT, f % NDT, 1);
+          const u32x4 vw = {vlo[f][0], vlo[f][1], hi[0], hi[1]};
+          vf[f / NDT][f % NDT] = __builtin_bit_cast(bf16x8, vw);
+        }
+      }
+    }
+    if (READ_K && i < NDS) kf[i] = read_k_at<D, BK, KQK>(lds, m, i);
+    // softmax of tile X
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (S::exp_at(j) == i) {
+        p[j] = fast_exp2(s_x[j]);
+        pin(p[j]);
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (S::pack_at(u) == i) pack_pair(p, u, w);
+      if (S::dot_at(u) == i) add_pair(w, u, ones, acc);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (S::max_at(k) != i) continue;
+      if (k == 0) mx = vmax(vmax(s_x[0], s_x[1]), s_x[2]);
+      else if (k < 7) mx = vmax(vmax(mx, s_x[2 * k + 1]), s_x[2 * k + 2]);
+      else mx = vmax(mx, s_x[15]);
+      pin(mx);
+    }
+    if (S::final_at() == i) finish_max();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // work that falls past the last step
+  if (S::final_at() >= NS) finish_max();
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (S::pack_at(u) >= NS) pack_pair(p, u, w);
+    if (S::dot_at(u) >= NS) add_pair(w, u, ones, acc);
+  }
+  st.l[X] = acc;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const u32x4 v4 = {w[4 * half], w[4 * half + 1], w[4 * half + 2], w[4 * half + 3]};
+    p_x[half] = __builtin_bit_cast(bf16x8, v4);
+  }
+  // keep P and the row sum in this block (nothing sinks them to the next)
+  asm volatile("" ::"v"(p_x[0]), "v"(p_x[1]), "v"(acc));
+  return grow;
 }
 
 template <int D>
@@ -209,11 +335,13 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   static_assert(TL::EXTRA == 0, "tile DMA must split evenly over the waves");
   constexpr int DMA = 2 * TL::LO;   // LDS-DMA instructions per wave per tile (K and V)
 
-  // kPPBufs x [K tile, V tile] (dynamic LDS).
+  // kPPBufs K tiles, then kPPBufs V tiles (dynamic LDS).
   extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
   YRB_LDS char* const lds = (YRB_LDS char*)lds_raw;
-  auto kbuf = [&](int t) -> YRB_LDS char* { return lds + (t & (kPPBufs - 1)) * 2 * T::TILEB; };
-  auto vbuf = [&](int t) -> YRB_LDS char* { return kbuf(t) + T::TILEB; };
+  auto kbuf = [&](int t) -> YRB_LDS char* { return lds + (t & (kPPBufs - 1)) * T::TILEB; };
+  auto vbuf = [&](int t) -> YRB_LDS char* {
+    return lds + LdsMap<D>::VBASE + (t & (kPPBufs - 1)) * T::TILEB;
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -225,17 +353,21 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   const int q_offset = (int)a.q_offset, k_offset = (int)a.k_offset;
 
   // Q rotated and pre-multiplied by softmax_scale * log2(e): scores come out
-  // of the MFMA in log2 units.
+  // of the MFMA in log2 units.  Q and O stay in AGPRs for the whole launch.
   bf16x8 qf[2][NDS];
   load_q<D, 2>(a, b, h, q0w, lane, qf, a.softmax_scale * kLog2e);
-  // Q stays in AGPRs for the whole launch (an MFMA reads its A/B operands
-  // from either register file); VGPRs hold O, S, P and the addresses.
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) asm volatile("" : "+a"(qf[t][ds]));
   WaveState<D, 2> st;
   init_state<D, 2>(a, b, h, q0w, lane, st);
+  // O into the AGPRs the inline-asm MFMAs accumulate in.
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(st.o[dt][t]));
+  asm volatile("s_nop 4" ::: "memory");
 
   // Key tiles: n_tiles reach the workgroup's last visible key; the first
   // n_full are visible to every row of the workgroup and hold no key past Sk.
@@ -253,6 +385,8 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   const __bf16* kbase = reinterpret_cast<const __bf16*>(a.k) + b * a.ks[0] + hk * a.ks[2];
   const __bf16* vbase = reinterpret_cast<const __bf16*>(a.v) + b * a.vs[0] + hk * a.vs[2];
   const int kstride = (int)a.ks[1], vstride = (int)a.vs[1];
+  const __bf16* const kbase_s = wave_uniform(kbase);
+  const __bf16* const vbase_s = wave_uniform(vbase);
 
   // Q, table and state loads complete here, so the only vector-memory
   // operations in flight below are the tile DMAs.
@@ -264,9 +398,9 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   // Lane offsets of the fast DMA are 32-bit: (BN - 1) rows of stride plus a row.
   const bool fast_dma = (int64_t)max(kstride, vstride) * BN * 2 < ((int64_t)1 << 31);
   auto issue = [&](int t) {
-    if (YRB_PP_FAST_DMA && fast_dma && (t + 1) * BN <= Sk) {
-      load_tile_rows<D, BN, NW>(kbuf(t), kbase + (int64_t)t * BN * kstride, koff, wave);
-      load_tile_rows<D, BN, NW>(vbuf(t), vbase + (int64_t)t * BN * vstride, voff, wave);
+    if (fast_dma && (t + 1) * BN <= Sk) {
+      load_tile_rows<D, BN, NW>(kbuf(t), kbase_s + (int64_t)t * BN * kstride, koff, wave);
+      load_tile_rows<D, BN, NW>(vbuf(t), vbase_s + (int64_t)t * BN * vstride, voff, wave);
     } else {   // the ragged last tile: rows past the end read the last row
       load_tile<D, BN, NW, false>(kbuf(t), kbase, kstride, t * BN, Sk, wave, lane);
       load_tile<D, BN, NW, true>(vbuf(t), vbase, vstride, t * BN, Sk, wave, lane);
@@ -286,8 +420,9 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   if (n_tiles > 1) issue(1);
 
   if (n_full > 0) {
-    bf16x8 kf[2][NDS];        // K(q) by quarter parity
-    bf16x8 vf[2][2][NDT];     // V(q) by quarter parity
+    const LdsMap<D> m = lds_map<D>(lane);
+    bf16x8 kf[NDS];           // K of the next S chain
+    bf16x8 vf[2][NDT];        // V of the next PV products
     bf16x8 p0[2], p1[2];
     f32x16 s0, s1;
     // The product of the quarter before the first is a no-op: P = V = 0.
@@ -295,55 +430,51 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
     for (int half = 0; half < 2; ++half) {
       p1[half] = (bf16x8){};
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vf[1][half][dt] = (bf16x8){};
+      for (int dt = 0; dt < NDT; ++dt) vf[half][dt] = (bf16x8){};
     }
     Offsets of;
     offsets_from<D>(st, of);
     arrive(0);
-    read_k_quarter<D>(kbuf(0), 0, lane, kf[0]);
-    s0 = qk_tile<D>(kf[0], qf[0], splat16(-of.base[0]));
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) kf[ds] = read_k_at<D, 0, 0>(lds, m, ds);
+    s0 = qk_tile<D>(kf, qf[0], of.negb[0]);
 
-    // Quarters 2t and 2t+1 of tile t; LAST: no tile follows in the pipeline.
-    auto tile = [&](int t, auto last_tag) {
-      constexpr bool LAST = decltype(last_tag)::value;
+    // Tile t (buffer BT = t % 4, a compile-time constant here): quarters 2t
+    // and 2t+1.  After the last tile the S chain and the K reads of the
+    // quarter that does not exist run on stale LDS data and go unused.
+    auto tile = [&](int t, auto bt_tag) {
+      constexpr int BT = decltype(bt_tag)::value;
+      constexpr int BT1 = (BT + 1) % kPPBufs;
       bool g;
-      // H1(2t)
-      read_k_quarter<D>(kbuf(t), 1, lane, kf[1]);
-      read_v_quarter<D>(vbuf(t), 0, lane, vf[0]);
-      s1 = qk_tile<D>(kf[0], qf[1], splat16(-of.base[1]));
-      pv_tile<D, 1>(vf[1], p1, st);
-      g = softmax_fast<D, 0>(s0, st, of, p0);
-      keep(p0);
-      interleave<4 * NDS / 2, NDS + 2 * NDT * 2>();
+      // H1(2t): PV1(2t-1), S1(2t); softmax 0; read V(2t)
+      g = half_step<D, 1, BT, 0, 0, 0, true, false>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0);
       settle<D, 0>(s0, st, of, g, p0);
-      // H2(2t)
-      s0 = qk_tile<D>(kf[1], qf[0], splat16(-of.base[0]));
-      pv_tile<D, 0>(vf[0], p0, st);
-      g = softmax_fast<D, 1>(s1, st, of, p1);
-      keep(p1);
-      interleave<4 * NDS / 2, 0>();
+      // H2(2t): PV0(2t), S0(2t+1); softmax 1; read K(2t+1)
+      g = half_step<D, 0, 0, 0, BT, 1, false, true>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
       settle<D, 1>(s1, st, of, g, p1);
-      if constexpr (!LAST) arrive(t + 1);
-      // H1(2t+1)
-      if constexpr (!LAST) read_k_quarter<D>(kbuf(t + 1), 0, lane, kf[0]);
-      read_v_quarter<D>(vbuf(t), 1, lane, vf[1]);
-      s1 = qk_tile<D>(kf[1], qf[1], splat16(-of.base[1]));
-      pv_tile<D, 1>(vf[0], p1, st);
-      g = softmax_fast<D, 0>(s0, st, of, p0);
-      keep(p0);
-      interleave<4 * NDS / 2, (LAST ? 0 : NDS) + 2 * NDT * 2>();
+      if (t + 1 < n_full) arrive(t + 1);
+      // H1(2t+1): PV1(2t), S1(2t+1); softmax 0; read V(2t+1)
+      g = half_step<D, 1, BT, 1, 0, 0, true, false>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0);
       settle<D, 0>(s0, st, of, g, p0);
-      // H2(2t+1)
-      if constexpr (!LAST) s0 = qk_tile<D>(kf[0], qf[0], splat16(-of.base[0]));
-      pv_tile<D, 0>(vf[1], p0, st);
-      g = softmax_fast<D, 1>(s1, st, of, p1);
-      keep(p1);
-      interleave<(LAST ? 2 : 4) * NDS / 2, 0>();
+      // H2(2t+1): PV0(2t+1), S0(2t+2); softmax 1; read K(2t+2)
+      g = half_step<D, 0, 0, 0, BT1, 0, false, true>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
       settle<D, 1>(s1, st, of, g, p1);
     };
-    for (int t = 0; t + 1 < n_full; ++t) tile(t, std::false_type{});
-    tile(n_full - 1, std::true_type{});
-    pv_tile<D, 1>(vf[1], p1, st);
+    for (int t = 0;;) {
+      tile(t, std::integral_constant<int, 0>{});
+      if (++t == n_full) break;
+      tile(t, std::integral_constant<int, 1>{});
+      if (++t == n_full) break;
+      tile(t, std::integral_constant<int, 2>{});
+      if (++t == n_full) break;
+      tile(t, std::integral_constant<int, 3>{});
+      if (++t == n_full) break;
+    }
+    // PV of the last quarter, tile 1; then let the asm MFMAs finish before
+    // any VALU code reads O.
+#pragma unroll
+    for (int i = 0; i < NDS; ++i) mfma_o(st.o[i % NDT][1], vf[i / NDT][i % NDT], p1[i / NDT]);
+    xdl_drain();
   }
 
   // Diagonal and ragged tiles: masked, per wave, skipping tiles wholly in
@@ -355,11 +486,12 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
     const bool skip = !wave_live || (a.causal && kpos0 > qw_last);
     if (!skip) {
       const bool need_mask = (a.causal && kpos0 + BN - 1 > qw_first) || (k0 + BN > Sk);
-      fold_tile<D, BN, 2>(kbuf(t), vbuf(t), qf, st, need_mask, k0, Sk, kpos0, qw_first + l32,
-                          a.causal != 0, 1.0f, lane);   // Q carries the scale
+      fold_tile<D, BN, 2, true>(kbuf(t), vbuf(t), qf, st, need_mask, k0, Sk, kpos0, qw_first + l32,
+                                a.causal != 0, 1.0f, lane);   // Q carries the scale
     }
   }
 
+  xdl_drain();
   if (!wave_live) return;
   finish_rows<D, 2>(a, b, h, q0w, lane, st);
 }
