@@ -106,7 +106,6 @@ __device__ __forceinline__ void settle(const f32x16& s, WaveState<D, 2>& st, Off
   const float mu_new = grow ? st.m_true[QT] : mu_old;
   const float shift = mu_new - of.base[QT];                          // 0 where kept
   const float alpha = grow ? fast_exp2(mu_old - mu_new) : 1.0f;      // 0 from an empty row
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float acc = of.l_prev[QT] * alpha;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -114,8 +113,9 @@ __device__ __forceinline__ void settle(const f32x16& s, WaveState<D, 2>& st, Off
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int j = 8 * half + 2 * u;
-      const bf16x2 pp = {(__bf16)fast_exp2(s[j] - shift), (__bf16)fast_exp2(s[j + 1] - shift)};
-      acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
+      const float p0 = fast_exp2(s[j] - shift), p1 = fast_exp2(s[j + 1] - shift);
+      acc += p0 + p1;
+      const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
       w[u] = __builtin_bit_cast(unsigned, pp);
     }
     pf[half] = __builtin_bit_cast(bf16x8, w);
@@ -142,10 +142,10 @@ __device__ __forceinline__ void pack_pair(const float (&p)[16], int u, unsigned 
   w[u] = __builtin_bit_cast(unsigned, pp);
   pin(w[u]);
 }
-// A pair enters the dot product as its own bf16x2: taking it from a vector
-// element once miscompiled (every dot2 read element 0).
-__device__ __forceinline__ void add_pair(const unsigned (&w)[8], int u, bf16x2 ones, float& acc) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[u]), ones, acc, false);
+// Row sum of a pair, in fp32 adds: the bf16 dot instructions run on the
+// matrix pipe on gfx950 and stall the MFMAs they sit between.
+__device__ __forceinline__ void add_pair(const float (&p)[16], int u, float& acc) {
+  acc += p[2 * u] + p[2 * u + 1];
   pin(acc);
 }
 
@@ -242,7 +242,6 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
   using S = Steps<D>;
   constexpr int NS = S::NS;
   const float base_x = of.base[X];
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float acc = st.l[X];
   of.l_prev[X] = acc;
   float p[16];
@@ -295,7 +294,7 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (S::pack_at(u) == i) pack_pair(p, u, w);
-      if (S::dot_at(u) == i) add_pair(w, u, ones, acc);
+      if (S::dot_at(u) == i) add_pair(p, u, acc);
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -313,7 +312,7 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     if (S::pack_at(u) >= NS) pack_pair(p, u, w);
-    if (S::dot_at(u) >= NS) add_pair(w, u, ones, acc);
+    if (S::dot_at(u) >= NS) add_pair(p, u, acc);
   }
   st.l[X] = acc;
 #pragma unroll
