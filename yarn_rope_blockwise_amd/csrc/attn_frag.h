@@ -62,36 +62,49 @@ struct TileLoads {
   static constexpr int EXTRA = INSTR % NW;             // waves < EXTRA issue LO + 1
 };
 
+// global_load_lds_dwordx4: lane i's 16 bytes land at m0 + 16*i, with
+// m0 = m0_base + IMM.  The constant is added inside the asm, so the compiler
+// cannot hoist one m0 value per (buffer, instruction) out of a loop into
+// SGPRs.  Issued from asm so the compiler does not add a vmcnt(0) before
+// every LDS read of another buffer: ordering is by explicit vmcnt waits and
+// barriers.  No register outputs.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved; nothing else here uses it
+template <int IMM>
+__device__ __forceinline__ void dma_lds_vaddr(unsigned m0_base, const void* g) {
+  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(m0_base), "i"(IMM)
+               : "memory", "m0", "scc");
+}
+// Same with an SGPR base address and a 32-bit per-lane byte offset.
+template <int IMM>
+__device__ __forceinline__ void dma_lds_saddr(unsigned m0_base, const void* rows, unsigned off) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(rows), "s"(m0_base), "i"(IMM)
+               : "memory", "m0", "scc");
+}
+#pragma clang diagnostic pop
+
 template <int D, int BN, int NW, bool IS_V>
 __device__ __forceinline__ void load_tile(YRB_LDS char* dst, const __bf16* src, int stride, int k0,
                                           int Sk, int wave, int lane) {
   using T = Tile<D, BN>;
   using TL = TileLoads<D, BN, NW>;
   constexpr int ROWB = T::ROWB;
-#pragma unroll
-  for (int n = 0; n < TL::LO + (TL::EXTRA ? 1 : 0); ++n) {
+  const unsigned m0w = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst + wave * 1024);
+  static_for<TL::LO + (TL::EXTRA ? 1 : 0)>([&](auto n_tag) YRB_INLINE {
+    constexpr int n = decltype(n_tag)::value;
     const int idx = n * NW + wave;
-    if (n >= TL::LO && idx >= TL::INSTR) break;   // wave-uniform
-    const int base = idx * 1024;
-    const int off = base + lane * 16;
+    if (n >= TL::LO && idx >= TL::INSTR) return;   // wave-uniform
+    const int off = idx * 1024 + lane * 16;
     const int r = off / ROWB;
     const int p = (off % ROWB) >> 4;
     const int c = IS_V ? (p ^ vsw<D>(r)) : (p ^ ksw<D>(r));
     const int row = min(k0 + r, Sk - 1);
-    const __bf16* g = src + (int64_t)row * stride + c * 8;
-    // global_load_lds_dwordx4: lane i's 16 bytes land at M0 + 16*i.  Issued
-    // from asm so the compiler does not add a vmcnt(0) before every LDS read
-    // of the other buffer; ordering is by the explicit vmcnt waits and
-    // barriers around fold_tile.  No register outputs.
-    const unsigned m0v = (unsigned)(uintptr_t)(dst + base);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved; nothing else here uses it
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(g), "s"(m0v)
-                 : "memory", "m0");
-#pragma clang diagnostic pop
-  }
+    dma_lds_vaddr<n * NW * 1024>(m0w, src + (int64_t)row * stride + c * 8);
+  });
 }
 
 // Tiles that need no row clamp: each lane's byte offsets (relative to the
@@ -129,17 +142,11 @@ __device__ __forceinline__ void load_tile_rows(YRB_LDS char* dst, const __bf16* 
                                                int wave) {
   using TL = TileLoads<D, BN, NW>;
   const __bf16* const rows = wave_uniform(tile_rows);
-#pragma unroll
-  for (int n = 0; n < TL::LO; ++n) {
-    const unsigned m0v = (unsigned)(uintptr_t)(dst + (n * NW + wave) * 1024);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved; nothing else here uses it
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(off[n]), "s"(rows), "s"(m0v)
-                 : "memory", "m0");
-#pragma clang diagnostic pop
-  }
+  const unsigned m0w = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst + wave * 1024);
+  static_for<TL::LO>([&](auto n_tag) YRB_INLINE {
+    constexpr int n = decltype(n_tag)::value;
+    dma_lds_saddr<n * NW * 1024>(m0w, rows, off[n]);
+  });
 }
 
 template <int D, int NQT>

@@ -31,7 +31,10 @@
 //    the few places where VALU code touches O or P next to them wait out
 //    the MFMA hazards explicitly (xdl_drain, the s_nop after settle).
 //  * Key tiles of 64 go global -> LDS with LDS-DMA into four buffers, two
-//    tiles ahead, with one workgroup barrier per tile.  Tiles visible to
+//    tiles ahead, with one workgroup barrier per tile.  Both sit inside a
+//    half step: the barrier after its first MFMA, the tile's DMA
+//    instructions one per issue step after it, so the matrix pipe runs
+//    through them.  Tiles visible to
 //    every row of the workgroup run through the pipeline; the few tiles on
 //    the causal diagonal or at the ragged end of the keys are folded
 //    afterwards, masked, by the plain per-quarter loop.
@@ -208,6 +211,39 @@ __device__ __forceinline__ u32x2 read_v_part(const YRB_LDS char* lds, const LdsM
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a));
 }
 
+// The DMA of one tile, spread over the issue steps of a half step: source
+// rows (SGPRs) and destination LDS addresses of K and V.  A tile that the
+// fast path cannot load (past the keys the workgroup needs, ragged, or
+// strides beyond the 32-bit lane offsets) still issues the same number of
+// instructions, from the first key rows into a spare LDS region, so the
+// vmcnt count per tile stays fixed; `slow` then asks for the clamped load
+// of a ragged tile after the half step.
+struct DmaPlan {
+  const __bf16* k;
+  const __bf16* v;
+  unsigned k_m0, v_m0;
+  bool slow;
+};
+
+// Plan of tile u (every argument wave-uniform; k_m0/v_m0: LDS address of
+// buffer 0 of K/V plus this wave's 1 KiB slot, spare_m0 likewise).
+template <int D>
+__device__ __forceinline__ DmaPlan dma_plan(int u, bool fast, int n_tiles, int Sk, const __bf16* kb,
+                                            const __bf16* vb, int kstride, int vstride, unsigned k_m0,
+                                            unsigned v_m0, unsigned spare_m0) {
+  constexpr int BN = kPPBN, TILEB = Tile<D, kPPBN>::TILEB;
+  u = __builtin_amdgcn_readfirstlane(u);
+  const bool real = fast && u < n_tiles && (u + 1) * BN <= Sk;
+  DmaPlan p;
+  p.k = wave_uniform(kb + (real ? (int64_t)u * BN * kstride : 0));
+  p.v = wave_uniform(vb + (real ? (int64_t)u * BN * vstride : 0));
+  const unsigned boff = (unsigned)(u & (kPPBufs - 1)) * TILEB;
+  p.k_m0 = __builtin_amdgcn_readfirstlane(real ? k_m0 + boff : spare_m0);
+  p.v_m0 = __builtin_amdgcn_readfirstlane(real ? v_m0 + boff : spare_m0);
+  p.slow = !real && u < n_tiles;
+  return p;
+}
+
 // Issue steps of a half step (NS = 2 * D/16), as compile-time functions.
 // The softmax of the other tile runs in steps W0 .. NS-1: its scores come
 // from the S chain that ended the previous half step, whose last MFMA has
@@ -231,13 +267,22 @@ struct Steps {
 // X's softmax: exps, the max chain, packs of finished pairs and the row sum.
 // In the common case (no row max outgrew the threshold) tile X's softmax is
 // then complete.  Returns whether any row grew, for settle().
-template <int D, int Y, int BV, int KQV, int BK, int KQK, bool READ_V, bool READ_K>
+template <int D, int Y, int BV, int KQV, int BK, int KQK, bool READ_V, bool READ_K, bool ARRIVE = false>
 __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, const YRB_LDS char* lds,
                                           const LdsMap<D>& m, bf16x8 (&vf)[2][D / 32],
                                           const bf16x8 (&p_pv)[2], bf16x8 (&kf)[D / 16],
                                           const bf16x8 (&q_s)[D / 16], f32x16& s_y, const f32x16& s_x,
-                                          bf16x8 (&p_x)[2]) {
+                                          bf16x8 (&p_x)[2], const DmaPlan* dp = nullptr,
+                                          const unsigned* koff = nullptr, const unsigned* voff = nullptr,
+                                          int wave = 0) {
   constexpr int X = 1 - Y;
+  constexpr int NL = TileLoads<D, kPPBN, kPPWaves>::LO;   // DMA instructions per tile per wave, K or V
+  static_assert(!ARRIVE || 2 * NL < D / 8, "the DMA pieces must fit the half step");
+  auto dma_at = [&](auto i_tag) YRB_INLINE {   // DMA instruction of step i (1 .. 2 NL)
+    constexpr int n = decltype(i_tag)::value - 1;
+    if constexpr (n >= 0 && n < NL) dma_lds_saddr<n * kPPWaves * 1024>(dp->k_m0, dp->k, koff[n]);
+    else if constexpr (n >= NL && n < 2 * NL) dma_lds_saddr<(n - NL) * kPPWaves * 1024>(dp->v_m0, dp->v, voff[n - NL]);
+  };
   constexpr int NDS = D / 16, NDT = D / 32;
   using S = Steps<D>;
   constexpr int NS = S::NS;
@@ -254,7 +299,7 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(st.o[dt][t]));
-  auto finish_max = [&]() {
+  auto finish_max = [&]() YRB_INLINE {
     const float t1 = base_x + pair_vmax(mx);   // this quarter's row max
     st.m_true[X] = vmax(st.m_true[X], t1);
     grow = t1 > of.mu_tau[X];
@@ -268,6 +313,19 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
     } else {
       const int ds = i - NDS;
       s_y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], q_s[ds], ds == 0 ? of.negb[Y] : s_y, 0, 0, 0);
+    }
+    // Tile arrival (the step-0 MFMA runs meanwhile): this wave's DMA of the
+    // next tile is done, the barrier extends that to every wave; then the
+    // DMA of the tile two ahead, one instruction per step.
+    if (ARRIVE) {
+      if (i == 0) {
+        wait_vmcnt<2 * NL>();
+        tile_barrier();
+      } else {
+        static_for<2 * NL + 1>([&](auto j_tag) YRB_INLINE {
+          if (decltype(j_tag)::value == i) dma_at(j_tag);
+        });
+      }
     }
     // LDS fragment reads
     // V fragment f: its first read right after the PV product that used the
@@ -337,8 +395,8 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   // kPPBufs K tiles, then kPPBufs V tiles (dynamic LDS).
   extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
   YRB_LDS char* const lds = (YRB_LDS char*)lds_raw;
-  auto kbuf = [&](int t) -> YRB_LDS char* { return lds + (t & (kPPBufs - 1)) * T::TILEB; };
-  auto vbuf = [&](int t) -> YRB_LDS char* {
+  auto kbuf = [&](int t) YRB_INLINE -> YRB_LDS char* { return lds + (t & (kPPBufs - 1)) * T::TILEB; };
+  auto vbuf = [&](int t) YRB_INLINE -> YRB_LDS char* {
     return lds + LdsMap<D>::VBASE + (t & (kPPBufs - 1)) * T::TILEB;
   };
 
@@ -391,12 +449,14 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   // operations in flight below are the tile DMAs.
   wait_vmcnt<0>();
 
-  unsigned koff[TL::LO], voff[TL::LO];
-  tile_offsets<D, BN, NW, false>(kstride, wave, lane, koff);
-  tile_offsets<D, BN, NW, true>(vstride, wave, lane, voff);
   // Lane offsets of the fast DMA are 32-bit: (BN - 1) rows of stride plus a row.
+  // Without the fast path they are taken with stride 0, which keeps the
+  // placeholder DMA of DmaPlan on the first key row.
   const bool fast_dma = (int64_t)max(kstride, vstride) * BN * 2 < ((int64_t)1 << 31);
-  auto issue = [&](int t) {
+  unsigned koff[TL::LO], voff[TL::LO];
+  tile_offsets<D, BN, NW, false>(fast_dma ? kstride : 0, wave, lane, koff);
+  tile_offsets<D, BN, NW, true>(fast_dma ? vstride : 0, wave, lane, voff);
+  auto issue = [&](int t) YRB_INLINE {
     if (fast_dma && (t + 1) * BN <= Sk) {
       load_tile_rows<D, BN, NW>(kbuf(t), kbase_s + (int64_t)t * BN * kstride, koff, wave);
       load_tile_rows<D, BN, NW>(vbuf(t), vbase_s + (int64_t)t * BN * vstride, voff, wave);
@@ -409,7 +469,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   // (only tile t+1's may still be in flight), the barrier extends that to
   // every wave and certifies that every wave is past its reads of tile t-2,
   // whose buffer then takes tile t+2.
-  auto arrive = [&](int t) {
+  auto arrive = [&](int t) YRB_INLINE {
     if (t + 1 < n_tiles) wait_vmcnt<DMA>();
     else wait_vmcnt<0>();
     tile_barrier();
@@ -417,6 +477,13 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   };
   if (n_tiles > 0) issue(0);
   if (n_tiles > 1) issue(1);
+
+  // The pipeline's DMA: every tile it asks for is one group of DMA
+  // instructions (a placeholder when the tile is not a full one inside the
+  // keys, plus the clamped load after the half step when it is ragged).
+  const unsigned k0_m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds + wave * 1024);
+  const unsigned v0_m0 = k0_m0 + LdsMap<D>::VBASE;
+  const unsigned spare_m0 = k0_m0 + 2 * kPPBufs * T::TILEB;
 
   if (n_full > 0) {
     const LdsMap<D> m = lds_map<D>(lane);
@@ -433,7 +500,19 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
     }
     Offsets of;
     offsets_from<D>(st, of);
-    arrive(0);
+    {   // arrival of tile 0; tile 2 (or a placeholder) goes out at once
+      if (n_tiles > 1) wait_vmcnt<DMA>();
+      else wait_vmcnt<0>();
+      tile_barrier();
+      const DmaPlan dp = dma_plan<D>(2, fast_dma, n_tiles, Sk, kbase_s, vbase_s, kstride, vstride, k0_m0,
+                                     v0_m0, spare_m0);
+      static_for<TL::LO>([&](auto n_tag) YRB_INLINE {
+        constexpr int n = decltype(n_tag)::value;
+        dma_lds_saddr<n * NW * 1024>(dp.k_m0, dp.k, koff[n]);
+        dma_lds_saddr<n * NW * 1024>(dp.v_m0, dp.v, voff[n]);
+      });
+      if (dp.slow) issue(2);
+    }
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) kf[ds] = read_k_at<D, 0, 0>(lds, m, ds);
     s0 = qk_tile<D>(kf, qf[0], of.negb[0]);
@@ -441,7 +520,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
     // Tile t (buffer BT = t % 4, a compile-time constant here): quarters 2t
     // and 2t+1.  After the last tile the S chain and the K reads of the
     // quarter that does not exist run on stale LDS data and go unused.
-    auto tile = [&](int t, auto bt_tag) {
+    auto tile = [&](int t, auto bt_tag) YRB_INLINE {
       constexpr int BT = decltype(bt_tag)::value;
       constexpr int BT1 = (BT + 1) % kPPBufs;
       bool g;
@@ -451,10 +530,15 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
       // H2(2t): PV0(2t), S0(2t+1); softmax 1; read K(2t+1)
       g = half_step<D, 0, 0, 0, BT, 1, false, true>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
       settle<D, 1>(s1, st, of, g, p1);
-      if (t + 1 < n_full) arrive(t + 1);
-      // H1(2t+1): PV1(2t), S1(2t+1); softmax 0; read V(2t+1)
-      g = half_step<D, 1, BT, 1, 0, 0, true, false>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0);
+      // H1(2t+1): PV1(2t), S1(2t+1); softmax 0; read V(2t+1); arrival of
+      // tile t+1 (the first edge tile after the last pipeline tile) and the
+      // DMA of tile t+3 into the buffer of tile t-1
+      const DmaPlan dp = dma_plan<D>(t + 3, fast_dma, n_tiles, Sk, kbase_s, vbase_s, kstride, vstride, k0_m0,
+                                     v0_m0, spare_m0);
+      g = half_step<D, 1, BT, 1, 0, 0, true, false, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, &dp,
+                                                          koff, voff, wave);
       settle<D, 0>(s0, st, of, g, p0);
+      if (__builtin_expect(dp.slow, 0)) issue(t + 3);
       // H2(2t+1): PV0(2t+1), S0(2t+2); softmax 1; read K(2t+2)
       g = half_step<D, 0, 0, 0, BT1, 0, false, true>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
       settle<D, 1>(s1, st, of, g, p1);
@@ -479,7 +563,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   // Diagonal and ragged tiles: masked, per wave, skipping tiles wholly in
   // the wave's future (the barrier sequence stays the same for all waves).
   for (int t = n_full; t < n_tiles; ++t) {
-    arrive(t);
+    if (t > n_full || n_full == 0) arrive(t);   // the pipeline's last tile did tile n_full's
     const int k0 = t * BN;
     const int kpos0 = k_offset + k0;
     const bool skip = !wave_live || (a.causal && kpos0 > qw_last);
@@ -490,6 +574,8 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
     }
   }
 
+  // no DMA (placeholders included) may land after the workgroup leaves
+  wait_vmcnt<0>();
   xdl_drain();
   if (!wave_live) return;
   finish_rows<D, 2>(a, b, h, q0w, lane, st);
@@ -498,7 +584,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
 template <int D>
 hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   constexpr int BM = kPPWaves * 64;
-  constexpr int LDS_BYTES = kPPBufs * 2 * Tile<D, kPPBN>::TILEB;
+  constexpr int LDS_BYTES = (kPPBufs * 2 + 1) * Tile<D, kPPBN>::TILEB;   // K, V tiles and a spare
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
   const int64_t n_qtiles = (a.Sq + BM - 1) / BM;
   const int64_t blocks = n_qtiles * a.B * a.Hq;

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace yrb {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -17,6 +20,9 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 #define YRB_LDS __attribute__((address_space(3)))
+// For lambdas in device code: a lambda the compiler outlines turns its
+// by-reference captures into stack (scratch) objects.
+#define YRB_INLINE __attribute__((always_inline))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -62,5 +68,16 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile
+// time (for instruction immediates that depend on the index).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 }  // namespace yrb
