@@ -13,12 +13,13 @@
 //    inside the wave, and the wave issues one instruction per four cycles:
 //    the schedule is written out, one MFMA per issue step.  The two query
 //    tiles run half a step apart (q counts 32-key quarters):
-//        H1(q): MFMA  O1 += V(q-1)^T P1(q-1),  S1(q) = K(q) Q1^T
-//               VALU  softmax of S0(q) -> P0(q);  LDS  V(q)
-//        H2(q): MFMA  O0 += V(q)^T P0(q),      S0(q+1) = K(q+1) Q0^T
-//               VALU  softmax of S1(q) -> P1(q);  LDS  K(q+1)
+//        H1(q): MFMA  S1(q) = K(q) Q1^T,      O1 += V(q-1)^T P1(q-1)
+//               VALU  softmax of S0(q) -> P0(q);  LDS  K(q+1)
+//        H2(q): MFMA  S0(q+1) = K(q+1) Q0^T,  O0 += V(q)^T P0(q)
+//               VALU  softmax of S1(q) -> P1(q);  LDS  V(q)
 //    so the MFMAs of each half step are independent of the VALU work
-//    beside them, and every LDS read lands a half step before its use.
+//    beside them, the scores a softmax reads were finished half a step
+//    earlier, and every LDS read lands eight MFMAs before its use.
 //  * Scores come out of the MFMA in log2 units and offset by the running
 //    max (Q is pre-multiplied by softmax_scale * log2(e), and each S chain
 //    starts from minus that max), so the common softmax path is P = exp2(S).
@@ -245,28 +246,30 @@ __device__ __forceinline__ DmaPlan dma_plan(int u, bool fast, int n_tiles, int S
 }
 
 // Issue steps of a half step (NS = 2 * D/16), as compile-time functions.
-// The softmax of the other tile runs in steps W0 .. NS-1: its scores come
-// from the S chain that ended the previous half step, whose last MFMA has
-// then had W0 steps to finish.
+// The scores the softmax reads come from the S chain in the first half of
+// the previous half step, long finished, so the softmax starts at step 0;
+// it ends two steps early so that the row-max tail and the grow test run
+// beside the last MFMAs rather than after them.
 template <int D>
 struct Steps {
   static constexpr int NS = D / 8;
-  static constexpr int W0 = 2;
-  static constexpr int exp_at(int j) { return W0 + (j * (NS - W0)) / 16; }
-  static constexpr int max_at(int k) { return W0 + (k * (NS - W0)) / 8; }
+  static constexpr int SPAN = NS - 2;
+  static constexpr int exp_at(int j) { return (j * SPAN) / 16; }
+  static constexpr int max_at(int k) { return (k * SPAN) / 8; }
   static constexpr int pack_at(int u) { return exp_at(2 * u + 1) + 1; }
-  static constexpr int dot_at(int u) { return pack_at(u) + 1; }
-  static constexpr int final_at() { return max_at(7) + 1; }
+  static constexpr int dot_at(int u) { return pack_at(u); }
+  static constexpr int final_at() { return NS - 2; }
 };
 
 // One half step, kept in order by sched_barrier(0) between issue steps.
-// Step i issues one MFMA (tile Y: the PV products in steps 0 .. NDS-1 on
-// vf, then the S chain on kf), one LDS fragment read (V in the second half
-// of H1, over the fragments the PV products just consumed; K in the first
-// half of H2, ahead of the S chain that uses them), and its share of tile
-// X's softmax: exps, the max chain, packs of finished pairs and the row sum.
-// In the common case (no row max outgrew the threshold) tile X's softmax is
-// then complete.  Returns whether any row grew, for settle().
+// Step i issues one MFMA (tile Y: the S chain on kf in steps 0 .. NDS-1,
+// then the PV products on vf), LDS fragment reads (in H1 the next quarter's
+// K, each fragment right after the S step that used the old one; in H2 the
+// current quarter's V, a fragment per step in the first half, eight steps
+// ahead of its PV product), and its share of tile X's softmax: exps, the
+// max chain, packs of finished pairs and the row sum.  In the common case
+// (no row max outgrew the threshold) tile X's softmax is then complete.
+// Returns whether any row grew, for settle().
 template <int D, int Y, int BV, int KQV, int BK, int KQK, bool READ_V, bool READ_K, bool ARRIVE = false>
 __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, const YRB_LDS char* lds,
                                           const LdsMap<D>& m, bf16x8 (&vf)[2][D / 32],
@@ -293,7 +296,6 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
   unsigned w[8];
   float mx = 0.f;
   bool grow = false;
-  u32x2 vlo[NDS];
   // O stays in AGPRs (a no-op when the register allocator already has it there)
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -309,10 +311,10 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
   for (int i = 0; i < NS; ++i) {
     // MFMA
     if (i < NDS) {
-      mfma_o(st.o[i % NDT][Y], vf[i / NDT][i % NDT], p_pv[i / NDT]);
+      s_y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], q_s[i], i == 0 ? of.negb[Y] : s_y, 0, 0, 0);
     } else {
-      const int ds = i - NDS;
-      s_y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], q_s[ds], ds == 0 ? of.negb[Y] : s_y, 0, 0, 0);
+      const int f = i - NDS;
+      mfma_o(st.o[f % NDT][Y], vf[f / NDT][f % NDT], p_pv[f / NDT]);
     }
     // Tile arrival (the step-0 MFMA runs meanwhile): this wave's DMA of the
     // next tile is done, the barrier extends that to every wave; then the
@@ -328,20 +330,8 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
       }
     }
     // LDS fragment reads
-    // V fragment f: its first read right after the PV product that used the
-    // old fragment f (step f), its second NDS - 1 steps later
-    if (READ_V) {
-#pragma unroll
-      for (int f = 0; f < NDS; ++f) {
-        if (i == f + 1) vlo[f] = read_v_part<D, BV, KQV>(lds, m, f / NDT, f % NDT, 0);
-        if (i == f + NDS) {
-          const u32x2 hi = read_v_part<D, BV, KQV>(lds, m, f / NDT, f % NDT, 1);
-          const u32x4 vw = {vlo[f][0], vlo[f][1], hi[0], hi[1]};
-          vf[f / NDT][f % NDT] = __builtin_bit_cast(bf16x8, vw);
-        }
-      }
-    }
-    if (READ_K && i < NDS) kf[i] = read_k_at<D, BK, KQK>(lds, m, i);
+    if (READ_K && i >= 1 && i <= NDS) kf[i - 1] = read_k_at<D, BK, KQK>(lds, m, i - 1);
+    if (READ_V && i < NDS) vf[i / NDT][i % NDT] = read_v_at<D, BV, KQV>(lds, m, i / NDT, i % NDT);
     // softmax of tile X
 #pragma unroll
     for (int j = 0; j < 16; ++j)
@@ -524,23 +514,23 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
       constexpr int BT = decltype(bt_tag)::value;
       constexpr int BT1 = (BT + 1) % kPPBufs;
       bool g;
-      // H1(2t): PV1(2t-1), S1(2t); softmax 0; read V(2t)
-      g = half_step<D, 1, BT, 0, 0, 0, true, false>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0);
+      // H1(2t): S1(2t), PV1(2t-1); softmax 0; read K(2t+1)
+      g = half_step<D, 1, 0, 0, BT, 1, false, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0);
       settle<D, 0>(s0, st, of, g, p0);
-      // H2(2t): PV0(2t), S0(2t+1); softmax 1; read K(2t+1)
-      g = half_step<D, 0, 0, 0, BT, 1, false, true>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
+      // H2(2t): S0(2t+1), PV0(2t); softmax 1; read V(2t)
+      g = half_step<D, 0, BT, 0, 0, 0, true, false>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
       settle<D, 1>(s1, st, of, g, p1);
-      // H1(2t+1): PV1(2t), S1(2t+1); softmax 0; read V(2t+1); arrival of
-      // tile t+1 (the first edge tile after the last pipeline tile) and the
-      // DMA of tile t+3 into the buffer of tile t-1
+      // H1(2t+1): S1(2t+1), PV1(2t); softmax 0; arrival of tile t+1 (the
+      // first edge tile after the last pipeline tile), read K(2t+2) from
+      // it, and the DMA of tile t+3 into the buffer of tile t-1
       const DmaPlan dp = dma_plan<D>(t + 3, fast_dma, n_tiles, Sk, kbase_s, vbase_s, kstride, vstride, k0_m0,
                                      v0_m0, spare_m0);
-      g = half_step<D, 1, BT, 1, 0, 0, true, false, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, &dp,
-                                                          koff, voff, wave);
+      g = half_step<D, 1, 0, 0, BT1, 0, false, true, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, &dp,
+                                                           koff, voff, wave);
       settle<D, 0>(s0, st, of, g, p0);
       if (__builtin_expect(dp.slow, 0)) issue(t + 3);
-      // H2(2t+1): PV0(2t+1), S0(2t+2); softmax 1; read K(2t+2)
-      g = half_step<D, 0, 0, 0, BT1, 0, false, true>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
+      // H2(2t+1): S0(2t+2), PV0(2t+1); softmax 1; read V(2t+1)
+      g = half_step<D, 0, BT, 1, 0, 0, true, false>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
       settle<D, 1>(s1, st, of, g, p1);
     };
     for (int t = 0;;) {
