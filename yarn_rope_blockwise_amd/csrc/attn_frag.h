@@ -43,6 +43,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(n), other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
+}
+
 // Workgroup barrier that no memory access may cross in either direction at
 // compile time (the LDS-DMA below is invisible to the compiler's model).
 __device__ __forceinline__ void tile_barrier() {

@@ -226,21 +226,22 @@ struct DmaPlan {
   bool slow;
 };
 
-// Plan of tile u (every argument wave-uniform; k_m0/v_m0: LDS address of
-// buffer 0 of K/V plus this wave's 1 KiB slot, spare_m0 likewise).
-template <int D>
-__device__ __forceinline__ DmaPlan dma_plan(int u, bool fast, int n_tiles, int Sk, const __bf16* kb,
-                                            const __bf16* vb, int kstride, int vstride, unsigned k_m0,
-                                            unsigned v_m0, unsigned spare_m0) {
-  constexpr int BN = kPPBN, TILEB = Tile<D, kPPBN>::TILEB;
-  u = __builtin_amdgcn_readfirstlane(u);
-  const bool real = fast && u < n_tiles && (u + 1) * BN <= Sk;
+// Plan of tile u, whose buffer is UB = u % kPPBufs (every argument
+// wave-uniform): tiles below n_fast come from k_rows/v_rows (that tile's
+// first key row) into buffer UB (k_m0/v_m0: buffer 0 plus this wave's
+// 1 KiB slot), the others are placeholders from the first key rows
+// (kb/vb) into the spare region.
+template <int D, int UB>
+__device__ __forceinline__ DmaPlan dma_plan(int u, int n_fast, int n_tiles, const __bf16* k_rows,
+                                            const __bf16* v_rows, const __bf16* kb, const __bf16* vb,
+                                            unsigned k_m0, unsigned v_m0, unsigned spare_m0) {
+  constexpr unsigned BOFF = UB * Tile<D, kPPBN>::TILEB;
+  const bool real = u < n_fast;
   DmaPlan p;
-  p.k = wave_uniform(kb + (real ? (int64_t)u * BN * kstride : 0));
-  p.v = wave_uniform(vb + (real ? (int64_t)u * BN * vstride : 0));
-  const unsigned boff = (unsigned)(u & (kPPBufs - 1)) * TILEB;
-  p.k_m0 = __builtin_amdgcn_readfirstlane(real ? k_m0 + boff : spare_m0);
-  p.v_m0 = __builtin_amdgcn_readfirstlane(real ? v_m0 + boff : spare_m0);
+  p.k = real ? k_rows : kb;
+  p.v = real ? v_rows : vb;
+  p.k_m0 = real ? k_m0 + BOFF : spare_m0;
+  p.v_m0 = real ? v_m0 + BOFF : spare_m0;
   p.slow = !real && u < n_tiles;
   return p;
 }
@@ -309,6 +310,14 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
   };
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
+    // LDS waits of H2, three instead of one per MFMA: the K fragments (read
+    // in H1) before the first S step, then the V fragments of this half
+    // step in two halves, each half four or more steps after its reads.
+    if (READ_V) {
+      if (i == 0) wait_lgkmcnt<0>();
+      if (i == NDS) wait_lgkmcnt<NDS>();
+      if (i == NDS + NDS / 2) wait_lgkmcnt<0>();
+    }
     // MFMA
     if (i < NDS) {
       s_y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], q_s[i], i == 0 ? of.negb[Y] : s_y, 0, 0, 0);
@@ -471,6 +480,12 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   // The pipeline's DMA: every tile it asks for is one group of DMA
   // instructions (a placeholder when the tile is not a full one inside the
   // keys, plus the clamped load after the half step when it is ragged).
+  // Tiles [0, n_fast) are full tiles inside the keys the workgroup needs and
+  // go by the fast path; the pipeline walks their first rows tile by tile.
+  const int n_fast = fast_dma ? min(n_tiles, Sk / BN) : 0;
+  const int64_t kstep = fast_dma ? (int64_t)BN * kstride : 0, vstep = fast_dma ? (int64_t)BN * vstride : 0;
+  const __bf16* k_rows = kbase_s + 2 * kstep;   // tile 2, then one tile further per pipeline tile
+  const __bf16* v_rows = vbase_s + 2 * vstep;
   const unsigned k0_m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds + wave * 1024);
   const unsigned v0_m0 = k0_m0 + LdsMap<D>::VBASE;
   const unsigned spare_m0 = k0_m0 + 2 * kPPBufs * T::TILEB;
@@ -494,8 +509,8 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
       if (n_tiles > 1) wait_vmcnt<DMA>();
       else wait_vmcnt<0>();
       tile_barrier();
-      const DmaPlan dp = dma_plan<D>(2, fast_dma, n_tiles, Sk, kbase_s, vbase_s, kstride, vstride, k0_m0,
-                                     v0_m0, spare_m0);
+      const DmaPlan dp = dma_plan<D, 2 % kPPBufs>(2, n_fast, n_tiles, k_rows, v_rows, kbase_s, vbase_s, k0_m0,
+                                                  v0_m0, spare_m0);
       static_for<TL::LO>([&](auto n_tag) YRB_INLINE {
         constexpr int n = decltype(n_tag)::value;
         dma_lds_saddr<n * NW * 1024>(dp.k_m0, dp.k, koff[n]);
@@ -523,8 +538,10 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
       // H1(2t+1): S1(2t+1), PV1(2t); softmax 0; arrival of tile t+1 (the
       // first edge tile after the last pipeline tile), read K(2t+2) from
       // it, and the DMA of tile t+3 into the buffer of tile t-1
-      const DmaPlan dp = dma_plan<D>(t + 3, fast_dma, n_tiles, Sk, kbase_s, vbase_s, kstride, vstride, k0_m0,
-                                     v0_m0, spare_m0);
+      k_rows += kstep;
+      v_rows += vstep;
+      const DmaPlan dp = dma_plan<D, (BT + 3) % kPPBufs>(t + 3, n_fast, n_tiles, k_rows, v_rows, kbase_s, vbase_s,
+                                                         k0_m0, v0_m0, spare_m0);
       g = half_step<D, 1, 0, 0, BT1, 0, false, true, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, &dp,
                                                            koff, voff, wave);
       settle<D, 0>(s0, st, of, g, p0);
