@@ -259,9 +259,20 @@ __device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& v, const bf16x8&
 __device__ __forceinline__ void xdl_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 // O *= alpha on an accumulator that lives in AGPRs, between inline-asm MFMAs.
+// Each element goes AGPR -> VGPR -> AGPR inside one asm statement, so the
+// compiler never holds O in VGPRs (it would hoist such copies out of this
+// rarely taken path into the hot one).
 __device__ __forceinline__ void scale_o_agpr(f32x16& o, float alpha) {
   xdl_drain();
-  o *= alpha;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float e = o[j];
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(e), "=&v"(tmp)
+                 : "v"(alpha));
+    o[j] = e;
+  }
   asm volatile("" : "+a"(o));
   asm volatile("s_nop 4" ::: "memory");
 }

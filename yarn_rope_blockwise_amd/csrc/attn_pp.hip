@@ -36,9 +36,9 @@
 //    half step: the barrier after its first MFMA, the tile's DMA
 //    instructions one per issue step after it, so the matrix pipe runs
 //    through them.  Tiles visible to
-//    every row of the workgroup run through the pipeline; the few tiles on
-//    the causal diagonal or at the ragged end of the keys are folded
-//    afterwards, masked, by the plain per-quarter loop.
+//    every row of the workgroup run through the pipeline as they are; the
+//    few on the causal diagonal or at the ragged end of the keys run
+//    through it too, their scores masked to -inf before the softmax.
 #include "attn_frag.h"
 #include "common.h"
 #include "kernels.h"
@@ -98,14 +98,31 @@ __device__ __forceinline__ void offsets_from(const WaveState<D, 2>& st, Offsets&
   }
 }
 
+// Per lane, for masking: the last key index (less 4(lane/32), the lane's
+// row offset inside a quarter) inside the keys and, for each query tile,
+// visible to the lane's query row under the causal mask.
+struct MaskInfo {
+  int key_last;
+  int q_last[2];
+  bool causal;
+};
+
+// Causal / ragged mask of the quarter whose first key index is kbase, for
+// query tile X: lane element j holds key row 8(j/4) + (j%4) of the quarter
+// past 4(lane/32); keys past the lane's last visible one get -inf, so P = 0.
+__device__ __forceinline__ void mask_scores(f32x16& s, const MaskInfo& mi, int X, int kbase) {
+  const int lim = (mi.causal ? min(mi.key_last, mi.q_last[X]) : mi.key_last) - kbase;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s[j] = (8 * (j >> 2) + (j & 3) <= lim) ? s[j] : -INFINITY;
+}
+
 // Rare case, at the boundary after the last product into O of tile QT under
 // the old max: rows that grew take their exact max as the new base, P and
 // the row sum are redone against it, O is rescaled, and the S chains of the
 // following quarters start from the new base.
 template <int D, int QT>
-__device__ __forceinline__ void settle(const f32x16& s, WaveState<D, 2>& st, Offsets& of, bool grow,
-                                       bf16x8 (&pf)[2]) {
-  if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) == 0, 1)) return;
+__device__ __forceinline__ void settle_rows(const f32x16& s, WaveState<D, 2>& st, Offsets& of, bool grow,
+                                            bf16x8 (&pf)[2]) {
   const float mu_old = st.m_use[QT];
   const float mu_new = grow ? st.m_true[QT] : mu_old;
   const float shift = mu_new - of.base[QT];                          // 0 where kept
@@ -133,6 +150,20 @@ __device__ __forceinline__ void settle(const f32x16& s, WaveState<D, 2>& st, Off
   of.negb[QT] = splat16(-of.base[QT]);
   // The next inline-asm MFMA may read this P at once.
   asm volatile("s_nop 4" ::: "memory");
+}
+
+// The boundary after a half step, one rarely taken branch for both rare
+// cases: settle_rows when a row of tile QT grew, and the mask of the scores
+// the next half step's softmax reads (s_next, query tile X_next, first key
+// index kbase) when they come from a masked tile.
+template <int D, int QT>
+__device__ __forceinline__ void settle(const f32x16& s, WaveState<D, 2>& st, Offsets& of, bool grow,
+                                       bf16x8 (&pf)[2], bool mask_next, f32x16& s_next, const MaskInfo& mi,
+                                       int X_next, int kbase) {
+  const uint64_t grown = __builtin_amdgcn_ballot_w64(grow);
+  if (__builtin_expect(grown == 0 && !mask_next, 1)) return;
+  if (grown != 0) settle_rows<D, QT>(s, st, of, grow, pf);
+  if (mask_next) mask_scores(s_next, mi, X_next, kbase);
 }
 
 // Pin a value to the current issue step: an empty volatile asm that reads
@@ -408,23 +439,6 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   const int Sq = (int)a.Sq, Sk = (int)a.Sk;
   const int q_offset = (int)a.q_offset, k_offset = (int)a.k_offset;
 
-  // Q rotated and pre-multiplied by softmax_scale * log2(e): scores come out
-  // of the MFMA in log2 units.  Q and O stay in AGPRs for the whole launch.
-  bf16x8 qf[2][NDS];
-  load_q<D, 2>(a, b, h, q0w, lane, qf, a.softmax_scale * kLog2e);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) asm volatile("" : "+a"(qf[t][ds]));
-  WaveState<D, 2> st;
-  init_state<D, 2>(a, b, h, q0w, lane, st);
-  // O into the AGPRs the inline-asm MFMAs accumulate in.
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(st.o[dt][t]));
-  asm volatile("s_nop 4" ::: "memory");
-
   // Key tiles: n_tiles reach the workgroup's last visible key; the first
   // n_full are visible to every row of the workgroup and hold no key past Sk.
   const int q_first_wg = q_offset + qtile * BM;
@@ -434,8 +448,6 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   const int n_tiles = (n_keys + BN - 1) / BN;
   int n_full = min(n_tiles, Sk / BN);
   if (a.causal) n_full = min(n_full, max(0, q_first_wg - k_offset + 1) / BN);
-  const int qw_first = q_offset + q0w;
-  const int qw_last = q_offset + min(Sq, q0w + QW) - 1;
   const bool wave_live = q0w < Sq;
 
   const __bf16* kbase = reinterpret_cast<const __bf16*>(a.k) + b * a.ks[0] + hk * a.ks[2];
@@ -443,10 +455,6 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   const int kstride = (int)a.ks[1], vstride = (int)a.vs[1];
   const __bf16* const kbase_s = wave_uniform(kbase);
   const __bf16* const vbase_s = wave_uniform(vbase);
-
-  // Q, table and state loads complete here, so the only vector-memory
-  // operations in flight below are the tile DMAs.
-  wait_vmcnt<0>();
 
   // Lane offsets of the fast DMA are 32-bit: (BN - 1) rows of stride plus a row.
   // Without the fast path they are taken with stride 0, which keeps the
@@ -464,18 +472,32 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
       load_tile<D, BN, NW, true>(vbuf(t), vbase, vstride, t * BN, Sk, wave, lane);
     }
   };
-  // Before the first LDS read of tile t: this wave's DMA of tile t is done
-  // (only tile t+1's may still be in flight), the barrier extends that to
-  // every wave and certifies that every wave is past its reads of tile t-2,
-  // whose buffer then takes tile t+2.
-  auto arrive = [&](int t) YRB_INLINE {
-    if (t + 1 < n_tiles) wait_vmcnt<DMA>();
-    else wait_vmcnt<0>();
-    tile_barrier();
-    if (t + 2 < n_tiles) issue(t + 2);
-  };
+  // The first two tiles' DMA goes out before the Q load, so the two memory
+  // round trips overlap.
   if (n_tiles > 0) issue(0);
   if (n_tiles > 1) issue(1);
+
+  // Q rotated and pre-multiplied by softmax_scale * log2(e): scores come out
+  // of the MFMA in log2 units.  Q and O stay in AGPRs for the whole launch.
+  bf16x8 qf[2][NDS];
+  load_q<D, 2>(a, b, h, q0w, lane, qf, a.softmax_scale * kLog2e);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) asm volatile("" : "+a"(qf[t][ds]));
+  WaveState<D, 2> st;
+  init_state<D, 2>(a, b, h, q0w, lane, st);
+  // O into the AGPRs the inline-asm MFMAs accumulate in.
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(st.o[dt][t]));
+  asm volatile("s_nop 4" ::: "memory");
+
+  // Q, table and state loads (and, being older, the first two tiles' DMA)
+  // complete here, so the only vector-memory operations in flight below
+  // are the tile DMAs.
+  wait_vmcnt<0>();
 
   // The pipeline's DMA: every tile it asks for is one group of DMA
   // instructions (a placeholder when the tile is not a full one inside the
@@ -490,8 +512,13 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   const unsigned v0_m0 = k0_m0 + LdsMap<D>::VBASE;
   const unsigned spare_m0 = k0_m0 + 2 * kPPBufs * T::TILEB;
 
-  if (n_full > 0) {
+  if (n_tiles > 0) {
     const LdsMap<D> m = lds_map<D>(lane);
+    MaskInfo mi;
+    mi.key_last = Sk - 1 - 4 * (lane >> 5);
+    mi.q_last[0] = q_offset + q0w + l32 - k_offset - 4 * (lane >> 5);
+    mi.q_last[1] = mi.q_last[0] + 32;
+    mi.causal = a.causal != 0;
     bf16x8 kf[NDS];           // K of the next S chain
     bf16x8 vf[2][NDT];        // V of the next PV products
     bf16x8 p0[2], p1[2];
@@ -521,64 +548,54 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) kf[ds] = read_k_at<D, 0, 0>(lds, m, ds);
     s0 = qk_tile<D>(kf, qf[0], of.negb[0]);
+    const int n_full_s = __builtin_amdgcn_readfirstlane(n_full);
+    if (n_full_s == 0) mask_scores(s0, mi, 0, 0);
 
     // Tile t (buffer BT = t % 4, a compile-time constant here): quarters 2t
-    // and 2t+1.  After the last tile the S chain and the K reads of the
-    // quarter that does not exist run on stale LDS data and go unused.
+    // and 2t+1; tiles from n_full on (the causal diagonal, the ragged end)
+    // have their scores masked at the boundary before their softmax.  After the last tile the S chain and the K
+    // reads of the quarter that does not exist run on stale LDS data and go
+    // unused.
     auto tile = [&](int t, auto bt_tag) YRB_INLINE {
       constexpr int BT = decltype(bt_tag)::value;
       constexpr int BT1 = (BT + 1) % kPPBufs;
+      const bool mk = t >= n_full_s, mk1 = t + 1 >= n_full_s;   // quarters 2t, 2t+1 / 2t+2 masked
       bool g;
       // H1(2t): S1(2t), PV1(2t-1); softmax 0; read K(2t+1)
       g = half_step<D, 1, 0, 0, BT, 1, false, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0);
-      settle<D, 0>(s0, st, of, g, p0);
+      settle<D, 0>(s0, st, of, g, p0, mk, s1, mi, 1, 64 * t);
       // H2(2t): S0(2t+1), PV0(2t); softmax 1; read V(2t)
       g = half_step<D, 0, BT, 0, 0, 0, true, false>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
-      settle<D, 1>(s1, st, of, g, p1);
-      // H1(2t+1): S1(2t+1), PV1(2t); softmax 0; arrival of tile t+1 (the
-      // first edge tile after the last pipeline tile), read K(2t+2) from
-      // it, and the DMA of tile t+3 into the buffer of tile t-1
+      settle<D, 1>(s1, st, of, g, p1, mk, s0, mi, 0, 64 * t + 32);
+      // H1(2t+1): S1(2t+1), PV1(2t); softmax 0; arrival of tile t+1, read
+      // K(2t+2) from it, and the DMA of tile t+3 into the buffer of tile t-1
       k_rows += kstep;
       v_rows += vstep;
       const DmaPlan dp = dma_plan<D, (BT + 3) % kPPBufs>(t + 3, n_fast, n_tiles, k_rows, v_rows, kbase_s, vbase_s,
                                                          k0_m0, v0_m0, spare_m0);
       g = half_step<D, 1, 0, 0, BT1, 0, false, true, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, &dp,
                                                            koff, voff, wave);
-      settle<D, 0>(s0, st, of, g, p0);
+      settle<D, 0>(s0, st, of, g, p0, mk, s1, mi, 1, 64 * t + 32);
       if (__builtin_expect(dp.slow, 0)) issue(t + 3);
       // H2(2t+1): S0(2t+2), PV0(2t+1); softmax 1; read V(2t+1)
       g = half_step<D, 0, BT, 1, 0, 0, true, false>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
-      settle<D, 1>(s1, st, of, g, p1);
+      settle<D, 1>(s1, st, of, g, p1, mk1, s0, mi, 0, 64 * t + 64);
     };
     for (int t = 0;;) {
       tile(t, std::integral_constant<int, 0>{});
-      if (++t == n_full) break;
+      if (++t == n_tiles) break;
       tile(t, std::integral_constant<int, 1>{});
-      if (++t == n_full) break;
+      if (++t == n_tiles) break;
       tile(t, std::integral_constant<int, 2>{});
-      if (++t == n_full) break;
+      if (++t == n_tiles) break;
       tile(t, std::integral_constant<int, 3>{});
-      if (++t == n_full) break;
+      if (++t == n_tiles) break;
     }
     // PV of the last quarter, tile 1; then let the asm MFMAs finish before
     // any VALU code reads O.
 #pragma unroll
     for (int i = 0; i < NDS; ++i) mfma_o(st.o[i % NDT][1], vf[i / NDT][i % NDT], p1[i / NDT]);
     xdl_drain();
-  }
-
-  // Diagonal and ragged tiles: masked, per wave, skipping tiles wholly in
-  // the wave's future (the barrier sequence stays the same for all waves).
-  for (int t = n_full; t < n_tiles; ++t) {
-    if (t > n_full || n_full == 0) arrive(t);   // the pipeline's last tile did tile n_full's
-    const int k0 = t * BN;
-    const int kpos0 = k_offset + k0;
-    const bool skip = !wave_live || (a.causal && kpos0 > qw_last);
-    if (!skip) {
-      const bool need_mask = (a.causal && kpos0 + BN - 1 > qw_first) || (k0 + BN > Sk);
-      fold_tile<D, BN, 2, true>(kbuf(t), vbuf(t), qf, st, need_mask, k0, Sk, kpos0, qw_first + l32,
-                                a.causal != 0, 1.0f, lane);   // Q carries the scale
-    }
   }
 
   // no DMA (placeholders included) may land after the workgroup leaves
