@@ -44,12 +44,12 @@ METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HB
 MEASURED_TRAFFIC = {
     "attn_bf16_pp_kernel": {
         "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
-        "sha256": None,   # not yet taken on this kernel
-        "fetch_kib": None, "write_kib": None},
+        "sha256": "9c4f80792f9e3b5f3e4acce75d376c652636c034a9a8fe8148636f1d89c5a1da",
+        "fetch_kib": 698908, "write_kib": 131158},
     "decode_bf16_kernel": {
         "files": ("csrc/decode.hip", "csrc/common.h"),
-        "sha256": "4d084fc7a493bbcefc586c89fae3e4bcdb1b9a60e2df51a48b9cdeb36d0253b3",
-        "fetch_kib": 2109102, "write_kib": 512},
+        "sha256": "ae8cf56a20c0a14593b206381671dabe73240b75c121f6dc18a0e1670b2692e2",
+        "fetch_kib": 2109599, "write_kib": 512},
 }
 FETCH_FACTOR, WRITE_FACTOR = 1.99994, 1.0
 
