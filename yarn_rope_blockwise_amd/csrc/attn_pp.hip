@@ -84,7 +84,12 @@ struct Offsets {
   float base[2];
   float mu_tau[2];     // m_use + threshold
   float l_prev[2];     // row sum before the current quarter
+  float thr[2];        // sum test: a quarter's P sum above this may hold a P above 2^threshold
 };
+
+// The sum test: with a reference in use, any P above 2^threshold makes the
+// lane's quarter sum exceed 2^threshold; without one, any visible key does.
+__device__ __forceinline__ float sum_threshold(float m_use) { return m_use == -INFINITY ? 0.f : exp2f(kTau); }
 
 template <int D>
 __device__ __forceinline__ void offsets_from(const WaveState<D, 2>& st, Offsets& of) {
@@ -95,6 +100,7 @@ __device__ __forceinline__ void offsets_from(const WaveState<D, 2>& st, Offsets&
     of.mu_tau[t] = mu + kTau;
     of.negb[t] = splat16(-of.base[t]);
     of.l_prev[t] = st.l[t];
+    of.thr[t] = sum_threshold(mu);
   }
 }
 
@@ -122,9 +128,9 @@ __device__ __forceinline__ void mask_scores(f32x16& s, const MaskInfo& mi, int X
 // following quarters start from the new base.
 template <int D, int QT>
 __device__ __forceinline__ void settle_rows(const f32x16& s, WaveState<D, 2>& st, Offsets& of, bool grow,
-                                            bf16x8 (&pf)[2]) {
+                                            bf16x8 (&pf)[2], float t_max) {
   const float mu_old = st.m_use[QT];
-  const float mu_new = grow ? st.m_true[QT] : mu_old;
+  const float mu_new = grow ? t_max : mu_old;
   const float shift = mu_new - of.base[QT];                          // 0 where kept
   const float alpha = grow ? fast_exp2(mu_old - mu_new) : 1.0f;      // 0 from an empty row
   float acc = of.l_prev[QT] * alpha;
@@ -147,6 +153,7 @@ __device__ __forceinline__ void settle_rows(const f32x16& s, WaveState<D, 2>& st
   st.m_use[QT] = mu_new;
   of.base[QT] = mu_new == -INFINITY ? 0.f : mu_new;
   of.mu_tau[QT] = mu_new + kTau;
+  of.thr[QT] = sum_threshold(mu_new);
   of.negb[QT] = splat16(-of.base[QT]);
   // The next inline-asm MFMA may read this P at once.
   asm volatile("s_nop 4" ::: "memory");
@@ -155,14 +162,27 @@ __device__ __forceinline__ void settle_rows(const f32x16& s, WaveState<D, 2>& st
 // The boundary after a half step, one rarely taken branch for both rare
 // cases: settle_rows when a row of tile QT grew, and the mask of the scores
 // the next half step's softmax reads (s_next, query tile X_next, first key
-// index kbase) when they come from a masked tile.
-template <int D, int QT>
+// index kbase) when they come from a masked tile.  With EXACT the half step
+// tracked the exact row max and `grow` is final; without, `grow` is the sum
+// test's candidate and the exact max of the quarter is taken here.
+template <int D, int QT, bool EXACT>
 __device__ __forceinline__ void settle(const f32x16& s, WaveState<D, 2>& st, Offsets& of, bool grow,
                                        bf16x8 (&pf)[2], bool mask_next, f32x16& s_next, const MaskInfo& mi,
                                        int X_next, int kbase) {
   const uint64_t grown = __builtin_amdgcn_ballot_w64(grow);
   if (__builtin_expect(grown == 0 && !mask_next, 1)) return;
-  if (grown != 0) settle_rows<D, QT>(s, st, of, grow, pf);
+  if (grown != 0) {
+    if constexpr (EXACT) {
+      settle_rows<D, QT>(s, st, of, grow, pf, st.m_true[QT]);
+    } else {
+      float mx = s[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) mx = vmax(mx, s[j]);
+      const float t_max = of.base[QT] + pair_vmax(mx);   // this quarter's exact row max
+      const bool g = t_max > of.mu_tau[QT];
+      if (__builtin_amdgcn_ballot_w64(g) != 0) settle_rows<D, QT>(s, st, of, g, pf, t_max);
+    }
+  }
   if (mask_next) mask_scores(s_next, mi, X_next, kbase);
 }
 
@@ -302,7 +322,7 @@ struct Steps {
 // max chain, packs of finished pairs and the row sum.  In the common case
 // (no row max outgrew the threshold) tile X's softmax is then complete.
 // Returns whether any row grew, for settle().
-template <int D, int Y, int BV, int KQV, int BK, int KQK, bool READ_V, bool READ_K, bool ARRIVE = false>
+template <int D, int Y, int BV, int KQV, int BK, int KQK, bool READ_V, bool READ_K, bool EXACT, bool ARRIVE = false>
 __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, const YRB_LDS char* lds,
                                           const LdsMap<D>& m, bf16x8 (&vf)[2][D / 32],
                                           const bf16x8 (&p_pv)[2], bf16x8 (&kf)[D / 16],
@@ -324,6 +344,7 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
   const float base_x = of.base[X];
   float acc = st.l[X];
   of.l_prev[X] = acc;
+  float qs = 0.f;   // without EXACT: this quarter's P sum
   float p[16];
   unsigned w[8];
   float mx = 0.f;
@@ -382,25 +403,31 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (S::pack_at(u) == i) pack_pair(p, u, w);
-      if (S::dot_at(u) == i) add_pair(p, u, acc);
+      if (S::dot_at(u) == i) add_pair(p, u, EXACT ? acc : qs);
     }
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (S::max_at(k) != i) continue;
-      if (k == 0) mx = vmax(vmax(s_x[0], s_x[1]), s_x[2]);
-      else if (k < 7) mx = vmax(vmax(mx, s_x[2 * k + 1]), s_x[2 * k + 2]);
-      else mx = vmax(mx, s_x[15]);
-      pin(mx);
+      for (int k = 0; k < 8; ++k) {
+        if (S::max_at(k) != i) continue;
+        if (k == 0) mx = vmax(vmax(s_x[0], s_x[1]), s_x[2]);
+        else if (k < 7) mx = vmax(vmax(mx, s_x[2 * k + 1]), s_x[2 * k + 2]);
+        else mx = vmax(mx, s_x[15]);
+        pin(mx);
+      }
+      if (S::final_at() == i) finish_max();
     }
-    if (S::final_at() == i) finish_max();
     __builtin_amdgcn_sched_barrier(0);
   }
   // work that falls past the last step
-  if (S::final_at() >= NS) finish_max();
+  if (EXACT && S::final_at() >= NS) finish_max();
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     if (S::pack_at(u) >= NS) pack_pair(p, u, w);
-    if (S::dot_at(u) >= NS) add_pair(p, u, acc);
+    if (S::dot_at(u) >= NS) add_pair(p, u, EXACT ? acc : qs);
+  }
+  if constexpr (!EXACT) {
+    acc += qs;
+    grow = qs > of.thr[X];
   }
   st.l[X] = acc;
 #pragma unroll
@@ -413,7 +440,10 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
   return grow;
 }
 
-template <int D>
+// EXACT: track the exact running max (calls that store the state, whose m
+// is that max); without it the grow test is the sum test and the output and
+// log-sum-exp use the reference in use, which gives the same values.
+template <int D, bool EXACT>
 __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs a, int64_t n_qtiles) {
   constexpr int NW = kPPWaves, BN = kPPBN, QW = 64, BM = NW * QW;
   constexpr int NDS = D / 16, NDT = D / 32;
@@ -562,24 +592,24 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
       const bool mk = t >= n_full_s, mk1 = t + 1 >= n_full_s;   // quarters 2t, 2t+1 / 2t+2 masked
       bool g;
       // H1(2t): S1(2t), PV1(2t-1); softmax 0; read K(2t+1)
-      g = half_step<D, 1, 0, 0, BT, 1, false, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0);
-      settle<D, 0>(s0, st, of, g, p0, mk, s1, mi, 1, 64 * t);
+      g = half_step<D, 1, 0, 0, BT, 1, false, true, EXACT>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0);
+      settle<D, 0, EXACT>(s0, st, of, g, p0, mk, s1, mi, 1, 64 * t);
       // H2(2t): S0(2t+1), PV0(2t); softmax 1; read V(2t)
-      g = half_step<D, 0, BT, 0, 0, 0, true, false>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
-      settle<D, 1>(s1, st, of, g, p1, mk, s0, mi, 0, 64 * t + 32);
+      g = half_step<D, 0, BT, 0, 0, 0, true, false, EXACT>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
+      settle<D, 1, EXACT>(s1, st, of, g, p1, mk, s0, mi, 0, 64 * t + 32);
       // H1(2t+1): S1(2t+1), PV1(2t); softmax 0; arrival of tile t+1, read
       // K(2t+2) from it, and the DMA of tile t+3 into the buffer of tile t-1
       k_rows += kstep;
       v_rows += vstep;
       const DmaPlan dp = dma_plan<D, (BT + 3) % kPPBufs>(t + 3, n_fast, n_tiles, k_rows, v_rows, kbase_s, vbase_s,
                                                          k0_m0, v0_m0, spare_m0);
-      g = half_step<D, 1, 0, 0, BT1, 0, false, true, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, &dp,
+      g = half_step<D, 1, 0, 0, BT1, 0, false, true, EXACT, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, &dp,
                                                            koff, voff, wave);
-      settle<D, 0>(s0, st, of, g, p0, mk, s1, mi, 1, 64 * t + 32);
+      settle<D, 0, EXACT>(s0, st, of, g, p0, mk, s1, mi, 1, 64 * t + 32);
       if (__builtin_expect(dp.slow, 0)) issue(t + 3);
       // H2(2t+1): S0(2t+2), PV0(2t+1); softmax 1; read V(2t+1)
-      g = half_step<D, 0, BT, 1, 0, 0, true, false>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
-      settle<D, 1>(s1, st, of, g, p1, mk1, s0, mi, 0, 64 * t + 64);
+      g = half_step<D, 0, BT, 1, 0, 0, true, false, EXACT>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
+      settle<D, 1, EXACT>(s1, st, of, g, p1, mk1, s0, mi, 0, 64 * t + 64);
     };
     for (int t = 0;;) {
       tile(t, std::integral_constant<int, 0>{});
@@ -602,11 +632,15 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   wait_vmcnt<0>();
   xdl_drain();
   if (!wave_live) return;
+  if constexpr (!EXACT) {   // the reference in use stands for the max
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) st.m_true[qt] = st.m_use[qt];
+  }
   finish_rows<D, 2>(a, b, h, q0w, lane, st);
 }
 
-template <int D>
-hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
+template <int D, bool EXACT>
+hipError_t launch_pp_as(const AttnArgs& a, hipStream_t stream) {
   constexpr int BM = kPPWaves * 64;
   constexpr int LDS_BYTES = (kPPBufs * 2 + 1) * Tile<D, kPPBN>::TILEB;   // K, V tiles and a spare
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
@@ -614,13 +648,18 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   const int64_t blocks = n_qtiles * a.B * a.Hq;
   if (blocks == 0) return hipSuccess;
   if (LDS_BYTES > 65536) {   // above the default dynamic-LDS limit
-    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_pp_kernel<D>),
+    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_pp_kernel<D, EXACT>),
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (attr != hipSuccess) return attr;
   }
-  hipLaunchKernelGGL((attn_bf16_pp_kernel<D>), dim3((unsigned)blocks), dim3(kPPWaves * 64), LDS_BYTES,
+  hipLaunchKernelGGL((attn_bf16_pp_kernel<D, EXACT>), dim3((unsigned)blocks), dim3(kPPWaves * 64), LDS_BYTES,
                      stream, a, n_qtiles);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
+  return a.store_state ? launch_pp_as<D, true>(a, stream) : launch_pp_as<D, false>(a, stream);
 }
 
 }  // namespace
