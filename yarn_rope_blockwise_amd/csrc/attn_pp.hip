@@ -166,11 +166,11 @@ __device__ __forceinline__ void settle_rows(const f32x16& s, WaveState<D, 2>& st
 // tracked the exact row max and `grow` is final; without, `grow` is the sum
 // test's candidate and the exact max of the quarter is taken here.
 template <int D, int QT, bool EXACT>
-__device__ __forceinline__ void settle(const f32x16& s, WaveState<D, 2>& st, Offsets& of, bool grow,
+__device__ __forceinline__ void settle(const f32x16& s, WaveState<D, 2>& st, Offsets& of, bool grow, bool need,
                                        bf16x8 (&pf)[2], bool mask_next, f32x16& s_next, const MaskInfo& mi,
                                        int X_next, int kbase) {
+  if (__builtin_expect(!need, 1)) return;
   const uint64_t grown = __builtin_amdgcn_ballot_w64(grow);
-  if (__builtin_expect(grown == 0 && !mask_next, 1)) return;
   if (grown != 0) {
     if constexpr (EXACT) {
       settle_rows<D, QT>(s, st, of, grow, pf, st.m_true[QT]);
@@ -299,18 +299,20 @@ __device__ __forceinline__ DmaPlan dma_plan(int u, int n_fast, int n_tiles, cons
 
 // Issue steps of a half step (NS = 2 * D/16), as compile-time functions.
 // The scores the softmax reads come from the S chain in the first half of
-// the previous half step, long finished, so the softmax starts at step 0;
-// it ends two steps early so that the row-max tail and the grow test run
-// beside the last MFMAs rather than after them.
+// the previous half step, long finished, so the softmax starts at step 0.
+// It ends three steps early: the row-max tail, then (step NS-2) the grow
+// test and the boundary's branch condition run beside the last MFMAs, and
+// the last step holds its MFMA alone.
 template <int D>
 struct Steps {
   static constexpr int NS = D / 8;
-  static constexpr int SPAN = NS - 2;
+  static constexpr int SPAN = NS - 3;
   static constexpr int exp_at(int j) { return (j * SPAN) / 16; }
   static constexpr int max_at(int k) { return (k * SPAN) / 8; }
   static constexpr int pack_at(int u) { return exp_at(2 * u + 1) + 1; }
   static constexpr int dot_at(int u) { return pack_at(u); }
-  static constexpr int final_at() { return NS - 2; }
+  static constexpr int final_at() { return NS - 3; }
+  static constexpr int need_at() { return NS - 2; }
 };
 
 // One half step, kept in order by sched_barrier(0) between issue steps.
@@ -327,7 +329,8 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
                                           const LdsMap<D>& m, bf16x8 (&vf)[2][D / 32],
                                           const bf16x8 (&p_pv)[2], bf16x8 (&kf)[D / 16],
                                           const bf16x8 (&q_s)[D / 16], f32x16& s_y, const f32x16& s_x,
-                                          bf16x8 (&p_x)[2], const DmaPlan* dp = nullptr,
+                                          bf16x8 (&p_x)[2], bool mask_next, bool& need,
+                                          const DmaPlan* dp = nullptr,
                                           const unsigned* koff = nullptr, const unsigned* voff = nullptr,
                                           int wave = 0) {
   constexpr int X = 1 - Y;
@@ -416,6 +419,15 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
       }
       if (S::final_at() == i) finish_max();
     }
+    // the boundary's branch condition, beside the last MFMA rather than
+    // after it: any row may have grown, or the next scores need a mask
+    if (i == S::need_at()) {
+      if constexpr (!EXACT) {
+        acc += qs;
+        grow = qs > of.thr[X];
+      }
+      need = __builtin_amdgcn_ballot_w64(grow) != 0 || mask_next;
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   // work that falls past the last step
@@ -424,10 +436,6 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
   for (int u = 0; u < 8; ++u) {
     if (S::pack_at(u) >= NS) pack_pair(p, u, w);
     if (S::dot_at(u) >= NS) add_pair(p, u, EXACT ? acc : qs);
-  }
-  if constexpr (!EXACT) {
-    acc += qs;
-    grow = qs > of.thr[X];
   }
   st.l[X] = acc;
 #pragma unroll
@@ -590,26 +598,27 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
       constexpr int BT = decltype(bt_tag)::value;
       constexpr int BT1 = (BT + 1) % kPPBufs;
       const bool mk = t >= n_full_s, mk1 = t + 1 >= n_full_s;   // quarters 2t, 2t+1 / 2t+2 masked
-      bool g;
+      bool g, nd;
       // H1(2t): S1(2t), PV1(2t-1); softmax 0; read K(2t+1)
-      g = half_step<D, 1, 0, 0, BT, 1, false, true, EXACT>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0);
-      settle<D, 0, EXACT>(s0, st, of, g, p0, mk, s1, mi, 1, 64 * t);
+      g = half_step<D, 1, 0, 0, BT, 1, false, true, EXACT>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, mk, nd);
+      settle<D, 0, EXACT>(s0, st, of, g, nd, p0, mk, s1, mi, 1, 64 * t);
       // H2(2t): S0(2t+1), PV0(2t); softmax 1; read V(2t)
-      g = half_step<D, 0, BT, 0, 0, 0, true, false, EXACT>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
-      settle<D, 1, EXACT>(s1, st, of, g, p1, mk, s0, mi, 0, 64 * t + 32);
+      g = half_step<D, 0, BT, 0, 0, 0, true, false, EXACT>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1, mk, nd);
+      settle<D, 1, EXACT>(s1, st, of, g, nd, p1, mk, s0, mi, 0, 64 * t + 32);
       // H1(2t+1): S1(2t+1), PV1(2t); softmax 0; arrival of tile t+1, read
       // K(2t+2) from it, and the DMA of tile t+3 into the buffer of tile t-1
       k_rows += kstep;
       v_rows += vstep;
       const DmaPlan dp = dma_plan<D, (BT + 3) % kPPBufs>(t + 3, n_fast, n_tiles, k_rows, v_rows, kbase_s, vbase_s,
                                                          k0_m0, v0_m0, spare_m0);
-      g = half_step<D, 1, 0, 0, BT1, 0, false, true, EXACT, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, &dp,
+      g = half_step<D, 1, 0, 0, BT1, 0, false, true, EXACT, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, mk,
+                                                                  nd, &dp,
                                                            koff, voff, wave);
-      settle<D, 0, EXACT>(s0, st, of, g, p0, mk, s1, mi, 1, 64 * t + 32);
+      settle<D, 0, EXACT>(s0, st, of, g, nd, p0, mk, s1, mi, 1, 64 * t + 32);
       if (__builtin_expect(dp.slow, 0)) issue(t + 3);
       // H2(2t+1): S0(2t+2), PV0(2t+1); softmax 1; read V(2t+1)
-      g = half_step<D, 0, BT, 1, 0, 0, true, false, EXACT>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1);
-      settle<D, 1, EXACT>(s1, st, of, g, p1, mk1, s0, mi, 0, 64 * t + 64);
+      g = half_step<D, 0, BT, 1, 0, 0, true, false, EXACT>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1, mk1, nd);
+      settle<D, 1, EXACT>(s1, st, of, g, nd, p1, mk1, s0, mi, 0, 64 * t + 64);
     };
     for (int t = 0;;) {
       tile(t, std::integral_constant<int, 0>{});
