@@ -448,6 +448,51 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
   return grow;
 }
 
+// Final output of a prefill call (no state stored) through LDS: the wave's
+// normalised 64 x D bf16 rows go into its own LDS region, 16-byte chunks
+// XOR-swizzled by row so that the writes from the Oᵀ accumulator layout
+// (a lane per row) spread over all banks, and come back a row per 16 (D=128)
+// lanes, so each store writes whole rows.  Log-sum-exp as in finish_rows.
+template <int D>
+__device__ __forceinline__ void finish_rows_lds(const AttnArgs& a, int b, int h, int q0w, int lane,
+                                                WaveState<D, 2>& st, YRB_LDS char* region) {
+  constexpr int NDT = D / 32, CH = D / 8;   // 16-byte chunks per row
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int Sq = (int)a.Sq, Hq = (int)a.Hq;
+  auto swz = [](int r) YRB_INLINE { return r & (CH - 1); };
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float lsum = pair_sum(st.l[qt]);
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    const int r = qt * 32 + l32;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c = dt * 4 + q4;   // dims 8c .. 8c+7; this lane holds 8c + 4hh .. +3
+        const u32x2 w = {pack_bf16x2(st.o[dt][qt][4 * q4] * inv, st.o[dt][qt][4 * q4 + 1] * inv),
+                         pack_bf16x2(st.o[dt][qt][4 * q4 + 2] * inv, st.o[dt][qt][4 * q4 + 3] * inv)};
+        *reinterpret_cast<YRB_LDS u32x2*>(region + r * (2 * D) + ((c ^ swz(r)) << 4) + 8 * hh) = w;
+      }
+    const int row = q0w + r;
+    if (a.lse && hh == 0 && row < Sq)
+      a.lse[((int64_t)b * Hq + h) * Sq + row] = lsum > 0.f ? (st.m_true[qt] + __log2f(lsum)) * kLn2 : -INFINITY;
+  }
+  // The region is this wave's alone: no barrier, only the wave's own writes.
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+  constexpr int RPI = 64 / CH;   // rows per read instruction
+#pragma unroll
+  for (int i = 0; i < 64 / RPI; ++i) {
+    const int r = i * RPI + lane / CH, c = lane % CH;
+    const u32x4 v = *reinterpret_cast<const YRB_LDS u32x4*>(region + r * (2 * D) + ((c ^ swz(r)) << 4));
+    const int row = q0w + r;
+    if (row < Sq) {
+      __bf16* op = reinterpret_cast<__bf16*>(a.o) + b * a.os[0] + row * a.os[1] + h * a.os[2];
+      *reinterpret_cast<u32x4*>(op + 8 * c) = v;
+    }
+  }
+}
+
 // EXACT: track the exact running max (calls that store the state, whose m
 // is that max); without it the grow test is the sum test and the output and
 // log-sum-exp use the reference in use, which gives the same values.
@@ -640,11 +685,19 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   // no DMA (placeholders included) may land after the workgroup leaves
   wait_vmcnt<0>();
   xdl_drain();
-  if (!wave_live) return;
   if constexpr (!EXACT) {   // the reference in use stands for the max
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) st.m_true[qt] = st.m_use[qt];
   }
+  if (a.finalize && !a.store_state) {
+    // every wave is past its last tile reads and its DMA has landed: the LDS
+    // is free for the output transpose (16 KiB per wave)
+    tile_barrier();
+    if (!wave_live) return;
+    finish_rows_lds<D>(a, b, h, q0w, lane, st, lds + wave * (64 * 2 * D));
+    return;
+  }
+  if (!wave_live) return;
   finish_rows<D, 2>(a, b, h, q0w, lane, st);
 }
 
