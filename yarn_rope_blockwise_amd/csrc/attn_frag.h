@@ -389,11 +389,11 @@ struct WorkItem {
   int b, h, hk, qtile;
 };
 
-__device__ __forceinline__ WorkItem work_item(const AttnArgs& a, int64_t n_qtiles) {
+__device__ __forceinline__ WorkItem work_item_at(const AttnArgs& a, int64_t n_qtiles, int idx) {
   const int Hq = (int)a.Hq;
   const int per = (int)(a.B * a.Hq);
-  const int rank = (int)blockIdx.x / per;
-  const int rem = (int)blockIdx.x - rank * per;
+  const int rank = idx / per;
+  const int rem = idx - rank * per;
   WorkItem w;
   w.b = rem / Hq;
   const int hp = rem - w.b * Hq;
@@ -402,14 +402,23 @@ __device__ __forceinline__ WorkItem work_item(const AttnArgs& a, int64_t n_qtile
   w.hk = w.h / (Hq / (int)a.Hkv);
   return w;
 }
+__device__ __forceinline__ WorkItem work_item(const AttnArgs& a, int64_t n_qtiles) {
+  return work_item_at(a, n_qtiles, (int)blockIdx.x);
+}
 
-// Query fragments (B operand of S^T = K Q^T) of one wave: lane holds query
-// row q0w + 32qt + l32 (clamped to the last row), dims 16ds + 8hh .. +7,
-// rotated here in fp32 from the table when one is given, multiplied by
-// qscale, and rounded once to bf16.
+// Q fragments and their table rows as loaded, before the rotation.
 template <int D, int NQT>
-__device__ __forceinline__ void load_q(const AttnArgs& a, int b, int h, int q0w, int lane,
-                                       bf16x8 (&qf)[NQT][D / 16], float qscale = 1.0f) {
+struct QRaw {
+  u32x4 raw[NQT][D / 16];
+  f32x4 tab[NQT][D / 32][4];
+};
+
+// Every load of Q and of its table rows goes out before any arithmetic:
+// one memory round trip (issued per tile, the loads would wait on each
+// other through register reuse).
+template <int D, int NQT, bool TAB = true>
+__device__ __forceinline__ void load_q_raw(const AttnArgs& a, int b, int h, int q0w, int lane,
+                                           QRaw<D, NQT>& qr) {
   constexpr int NDS = D / 16;
   const int hh = lane >> 5;
   const int l32 = lane & 31;
@@ -420,43 +429,70 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int b, int h, int q0w,
   for (int qt = 0; qt < NQT; ++qt) {
     const int row = min(q0w + qt * 32 + l32, Sq - 1);
     const __bf16* qp = qbase + row * a.qs[1] + 8 * hh;
-    u32x4 raw[NDS];
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) raw[ds] = *reinterpret_cast<const u32x4*>(qp + 16 * ds);
-    if (a.cos_sin) {
-      // pair (i, i + D/2) of the rotation sits in fragments ds and ds + NDS/2
+    for (int ds = 0; ds < NDS; ++ds) qr.raw[qt][ds] = *reinterpret_cast<const u32x4*>(qp + 16 * ds);
+    if (TAB && a.cos_sin) {
       const float* cs = a.cos_sin + (int64_t)(q_offset + row) * D;
 #pragma unroll
+      for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2)
+          qr.tab[qt][ds][u2] = reinterpret_cast<const f32x4*>(cs + 2 * (16 * ds + 8 * hh))[u2];
+    }
+  }
+}
+
+// Rotation (pair (i, i + D/2) sits in fragments ds and ds + NDS/2), the
+// qscale factor, and one rounding to bf16.
+template <int D, int NQT>
+__device__ __forceinline__ void rotate_q(const AttnArgs& a, QRaw<D, NQT>& qr, bf16x8 (&qf)[NQT][D / 16],
+                                         float qscale) {
+  constexpr int NDS = D / 16;
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    if (a.cos_sin) {
+#pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds) {
-        const int i0 = 16 * ds + 8 * hh;
-        const f32x4* t = reinterpret_cast<const f32x4*>(cs + 2 * i0);
         float x[8], z[8], lo[8], hi[8];
-        unpack8(raw[ds], x);
-        unpack8(raw[ds + NDS / 2], z);
+        unpack8(qr.raw[qt][ds], x);
+        unpack8(qr.raw[qt][ds + NDS / 2], z);
 #pragma unroll
         for (int u2 = 0; u2 < 4; ++u2) {
-          const f32x4 tt = t[u2];
+          const f32x4 tt = qr.tab[qt][ds][u2];
           lo[2 * u2] = (x[2 * u2] * tt[0] - z[2 * u2] * tt[1]) * qscale;
           hi[2 * u2] = (x[2 * u2] * tt[1] + z[2 * u2] * tt[0]) * qscale;
           lo[2 * u2 + 1] = (x[2 * u2 + 1] * tt[2] - z[2 * u2 + 1] * tt[3]) * qscale;
           hi[2 * u2 + 1] = (x[2 * u2 + 1] * tt[3] + z[2 * u2 + 1] * tt[2]) * qscale;
         }
-        raw[ds] = pack8(lo);
-        raw[ds + NDS / 2] = pack8(hi);
+        qr.raw[qt][ds] = pack8(lo);
+        qr.raw[qt][ds + NDS / 2] = pack8(hi);
       }
     } else if (qscale != 1.0f) {
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         float x[8];
-        unpack8(raw[ds], x);
+        unpack8(qr.raw[qt][ds], x);
 #pragma unroll
         for (int u = 0; u < 8; ++u) x[u] *= qscale;
-        raw[ds] = pack8(x);
+        qr.raw[qt][ds] = pack8(x);
       }
     }
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) qf[qt][ds] = __builtin_bit_cast(bf16x8, raw[ds]);
+    for (int ds = 0; ds < NDS; ++ds) qf[qt][ds] = __builtin_bit_cast(bf16x8, qr.raw[qt][ds]);
   }
+}
+
+// Query fragments (B operand of S^T = K Q^T) of one wave: lane holds query
+// row q0w + 32qt + l32 (clamped to the last row), dims 16ds + 8hh .. +7,
+// rotated here in fp32 from the table when one is given, multiplied by
+// qscale, and rounded once to bf16.
+template <int D, int NQT>
+__device__ __forceinline__ void load_q(const AttnArgs& a, int b, int h, int q0w, int lane,
+                                       bf16x8 (&qf)[NQT][D / 16], float qscale = 1.0f) {
+  QRaw<D, NQT> qr;
+  load_q_raw<D, NQT>(a, b, h, q0w, lane, qr);
+  __builtin_amdgcn_sched_barrier(0);
+  rotate_q<D, NQT>(a, qr, qf, qscale);
 }
 
 // Running state of one wave: empty, or read from (o_acc, m, l) of an

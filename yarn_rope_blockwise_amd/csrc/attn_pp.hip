@@ -493,6 +493,41 @@ __device__ __forceinline__ void finish_rows_lds(const AttnArgs& a, int b, int h,
   }
 }
 
+// The table rows of one 32-row query tile (positions q_offset + row, rows
+// clamped to the last query row) global -> LDS by DMA into the wave's
+// region: 4D bytes a row, 1 KiB (256/D rows) per instruction, 16-byte chunk
+// c of row r stored at position c ^ (r mod D/4) so that the lane reads below
+// spread over the banks.
+template <int D>
+__device__ __forceinline__ void table_rows_to_lds(const AttnArgs& a, int row0, int lane, YRB_LDS char* region) {
+  constexpr int CHT = D / 4;           // 16-byte chunks a table row
+  constexpr int RPI = 64 / CHT;        // rows per DMA instruction
+  const int Sq = (int)a.Sq;
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)region);
+  static_for<32 / RPI>([&](auto n_tag) YRB_INLINE {
+    constexpr int n = decltype(n_tag)::value;
+    const int r = n * RPI + lane / CHT;            // row inside the tile
+    const int c = (lane % CHT) ^ (r & (CHT - 1));  // chunk this lane fetches
+    const int row = min(row0 + r, Sq - 1);
+    dma_lds_vaddr<n * 1024>(m0, a.cos_sin + (int64_t)((int)a.q_offset + row) * D + 4 * c);
+  });
+}
+
+// The cos/sin a lane needs for query tile rows (row l32; chunks 8ds + 4hh + u2)
+// from the wave's LDS region.
+template <int D>
+__device__ __forceinline__ void table_from_lds(const YRB_LDS char* region, int lane, f32x4 (&tab)[D / 32][4]) {
+  constexpr int CHT = D / 4;
+  const int r = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds)
+#pragma unroll
+    for (int u2 = 0; u2 < 4; ++u2) {
+      const int c = 8 * ds + 4 * hh + u2;
+      tab[ds][u2] = *reinterpret_cast<const YRB_LDS f32x4*>(region + r * (4 * D) + ((c ^ (r & (CHT - 1))) << 4));
+    }
+}
+
 // EXACT: track the exact running max (calls that store the state, whose m
 // is that max); without it the grow test is the sum test and the output and
 // log-sum-exp use the reference in use, which gives the same values.
@@ -555,15 +590,40 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
       load_tile<D, BN, NW, true>(vbuf(t), vbase, vstride, t * BN, Sk, wave, lane);
     }
   };
-  // The first two tiles' DMA goes out before the Q load, so the two memory
-  // round trips overlap.
-  if (n_tiles > 0) issue(0);
-  if (n_tiles > 1) issue(1);
-
   // Q rotated and pre-multiplied by softmax_scale * log2(e): scores come out
   // of the MFMA in log2 units.  Q and O stay in AGPRs for the whole launch.
+  // Loads: the first query tile's table rows by DMA into the wave's region
+  // of buffers 2/3 (free until the first tile arrives), the first two key
+  // tiles, then Q; the second tile's table rows follow through the same
+  // region while the first tile is rotated.
   bf16x8 qf[2][NDS];
-  load_q<D, 2>(a, b, h, q0w, lane, qf, a.softmax_scale * kLog2e);
+  {
+    YRB_LDS char* const region = lds + (wave < 2 ? 0 : LdsMap<D>::VBASE) + (2 + (wave & 1)) * T::TILEB;
+    static_assert(32 * 4 * D <= T::TILEB, "a query tile's table rows fit one tile buffer");
+    const float qscale = a.softmax_scale * kLog2e;
+    QRaw<D, 2> qr;
+    if (a.cos_sin) table_rows_to_lds<D>(a, q0w, lane, region);
+    if (n_tiles > 0) issue(0);
+    if (n_tiles > 1) issue(1);
+    load_q_raw<D, 2, false>(a, b, h, q0w, lane, qr);   // Q only
+    if (a.cos_sin) {
+      // Loads return in order: the table rows are in once no more than the
+      // later loads are outstanding (both tiles by the fast path, the Q loads).
+      // (The empty asm statements keep the LDS reads between the waits.)
+      if (fast_dma && 2 * BN <= Sk) wait_vmcnt<2 * DMA + 2 * NDS>();
+      else wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      table_from_lds<D>(region, lane, qr.tab[0]);
+      wait_lgkmcnt<0>();   // the reads are done before the region is refilled
+      asm volatile("" ::: "memory");
+      table_rows_to_lds<D>(a, q0w + 32, lane, region);
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      table_from_lds<D>(region, lane, qr.tab[1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    rotate_q<D, 2>(a, qr, qf, qscale);
+  }
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
