@@ -13,8 +13,14 @@
  *
  * Conventions shared by every call
  *  - Every device buffer is owned by the caller.  The library allocates no
- *    memory, never synchronises and keeps no mutable global state; calls are
- *    thread-safe.
+ *    memory, never synchronises and calls are thread-safe.  Its one piece of
+ *    mutable state is a static device array of 64 work-claim counters
+ *    (4 KiB per GPU) that attn_prefill_blockwise and attn_block_accumulate
+ *    use to balance the second half of their grid across the XCDs: each
+ *    launch takes the next counter in turn and leaves it at zero.  Two
+ *    launches on one GPU that run at the same time with the same counter
+ *    (64 launches apart, or one captured graph replayed on two streams at
+ *    once) race and may skip or repeat query tiles.
  *  - Work is queued on `stream` (a hipStream_t; NULL = the default stream)
  *    and completes asynchronously.  A kernel fault surfaces at the caller's
  *    next synchronisation.

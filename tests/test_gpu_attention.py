@@ -108,6 +108,33 @@ def test_prefill_deterministic():
     assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("S,Hq,Hkv", [(2000, 4, 4), (1300, 3, 1)])
+def test_prefill_claimed_items_repeated(S, Hq, Hkv):
+    # The second half of the grid claims its work items at run time from
+    # counters that each launch leaves at zero: more launches than counter
+    # slots, each into a NaN-filled output, must all write every row and
+    # agree bit for bit (grids of 32 and 18 blocks).
+    require_gpu()
+    import torch
+    rope = W.Rope(W.YARN, 128, 1e4, 4.0, 128)
+    tab, th, scale, (qv, kv, vv), (q, k, v) = _setup(1, S, Hq, Hkv, 128, "bf16", rope, seed_base=9)
+    say(f"attn_prefill_blockwise claimed items S={S} Hq={Hq} x70")
+    kr = api.rope_apply(k, tab)
+    first = None
+    for i in range(70):
+        o = torch.full_like(q, float("nan"))
+        api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab, out=o)
+        torch.cuda.synchronize()
+        if first is None:
+            first = o.clone()
+            assert not torch.isnan(first).any()
+            rows = _sample_rows(S, 5, 24)
+            ref = A.prefill(qv, kv, vv, th, scale, rows=rows)
+            assert max_abs(host(first[0, rows]), ref[0]) <= BF16_TOL
+        else:
+            assert torch.equal(o, first), i
+
+
 def _sample_rows(S, seed, count=40):
     edges = [0, 1, 2, 63, 64, 127, 128, 255, 256, 257, S // 2, S - 257, S - 256, S - 2, S - 1]
     return synth.sample_rows(S, count, seed, must=edges)

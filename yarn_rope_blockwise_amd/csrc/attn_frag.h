@@ -442,44 +442,49 @@ __device__ __forceinline__ void load_q_raw(const AttnArgs& a, int b, int h, int 
   }
 }
 
-// Rotation (pair (i, i + D/2) sits in fragments ds and ds + NDS/2), the
-// qscale factor, and one rounding to bf16.
+// Rotation of query tile QT (pair (i, i + D/2) sits in fragments ds and
+// ds + NDS/2), the qscale factor, and one rounding to bf16.
+template <int D, int NQT, int QT>
+__device__ __forceinline__ void rotate_q_tile(const AttnArgs& a, QRaw<D, NQT>& qr, bf16x8 (&qf)[NQT][D / 16],
+                                              float qscale) {
+  constexpr int NDS = D / 16;
+  if (a.cos_sin) {
+#pragma unroll
+    for (int ds = 0; ds < NDS / 2; ++ds) {
+      float x[8], z[8], lo[8], hi[8];
+      unpack8(qr.raw[QT][ds], x);
+      unpack8(qr.raw[QT][ds + NDS / 2], z);
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2) {
+        const f32x4 tt = qr.tab[QT][ds][u2];
+        lo[2 * u2] = (x[2 * u2] * tt[0] - z[2 * u2] * tt[1]) * qscale;
+        hi[2 * u2] = (x[2 * u2] * tt[1] + z[2 * u2] * tt[0]) * qscale;
+        lo[2 * u2 + 1] = (x[2 * u2 + 1] * tt[2] - z[2 * u2 + 1] * tt[3]) * qscale;
+        hi[2 * u2 + 1] = (x[2 * u2 + 1] * tt[3] + z[2 * u2 + 1] * tt[2]) * qscale;
+      }
+      qr.raw[QT][ds] = pack8(lo);
+      qr.raw[QT][ds + NDS / 2] = pack8(hi);
+    }
+  } else if (qscale != 1.0f) {
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      float x[8];
+      unpack8(qr.raw[QT][ds], x);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] *= qscale;
+      qr.raw[QT][ds] = pack8(x);
+    }
+  }
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) qf[QT][ds] = __builtin_bit_cast(bf16x8, qr.raw[QT][ds]);
+}
+
 template <int D, int NQT>
 __device__ __forceinline__ void rotate_q(const AttnArgs& a, QRaw<D, NQT>& qr, bf16x8 (&qf)[NQT][D / 16],
                                          float qscale) {
-  constexpr int NDS = D / 16;
-#pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    if (a.cos_sin) {
-#pragma unroll
-      for (int ds = 0; ds < NDS / 2; ++ds) {
-        float x[8], z[8], lo[8], hi[8];
-        unpack8(qr.raw[qt][ds], x);
-        unpack8(qr.raw[qt][ds + NDS / 2], z);
-#pragma unroll
-        for (int u2 = 0; u2 < 4; ++u2) {
-          const f32x4 tt = qr.tab[qt][ds][u2];
-          lo[2 * u2] = (x[2 * u2] * tt[0] - z[2 * u2] * tt[1]) * qscale;
-          hi[2 * u2] = (x[2 * u2] * tt[1] + z[2 * u2] * tt[0]) * qscale;
-          lo[2 * u2 + 1] = (x[2 * u2 + 1] * tt[2] - z[2 * u2 + 1] * tt[3]) * qscale;
-          hi[2 * u2 + 1] = (x[2 * u2 + 1] * tt[3] + z[2 * u2 + 1] * tt[2]) * qscale;
-        }
-        qr.raw[qt][ds] = pack8(lo);
-        qr.raw[qt][ds + NDS / 2] = pack8(hi);
-      }
-    } else if (qscale != 1.0f) {
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        float x[8];
-        unpack8(qr.raw[qt][ds], x);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] *= qscale;
-        qr.raw[qt][ds] = pack8(x);
-      }
-    }
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) qf[qt][ds] = __builtin_bit_cast(bf16x8, qr.raw[qt][ds]);
-  }
+  static_for<NQT>([&](auto qt_tag) YRB_INLINE {
+    rotate_q_tile<D, NQT, decltype(qt_tag)::value>(a, qr, qf, qscale);
+  });
 }
 
 // Query fragments (B operand of S^T = K Q^T) of one wave: lane holds query

@@ -43,6 +43,7 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace yrb {
@@ -52,6 +53,39 @@ namespace {
 constexpr int kPPWaves = 4;    // one per SIMD
 constexpr int kPPBN = 64;      // keys per tile (two quarters)
 constexpr int kPPBufs = 4;     // LDS tile buffers (the tile loop is unrolled by this)
+
+// Work items of the second half of the grid are claimed at run time.  Blocks
+// go round robin over the 8 XCDs and each XCD runs its share at its own
+// clock, which under load differs from XCD to XCD by a few percent: with a
+// fixed item per block the slowest XCD finishes last while the others idle.
+// A block from claim_from on takes the next item of a counter instead, so an
+// XCD that runs ahead takes the heavier items (they come first).  The counter
+// of a launch is one of kClaimSlots, taken in turn by successive launches;
+// the block that claims the launch's last item sets it back to zero.
+// Launches that run at the same time on one GPU must not share a slot (more
+// than kClaimSlots launches apart, or a captured graph replayed on two
+// streams at once).
+constexpr int kClaimSlots = 64;
+constexpr int kClaimMinBlocks = 16;   // smaller grids take every item statically
+struct ClaimSlot {
+  unsigned next;      // items claimed so far
+  unsigned pad[15];   // one 64-byte line per slot
+};
+__device__ ClaimSlot g_claims[kClaimSlots];
+
+// The item of this block: blockIdx.x below claim_from, else claimed.
+__device__ __forceinline__ int claim_item(int claim_from, unsigned slot, YRB_LDS int* cell) {
+  if ((int)blockIdx.x < claim_from) return (int)blockIdx.x;
+  if (threadIdx.x == 0) {
+    unsigned* next = &g_claims[slot].next;
+    const unsigned c = __hip_atomic_fetch_add(next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int)c == (int)gridDim.x - claim_from - 1)   // every claim of the launch is made
+      __hip_atomic_store(next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *cell = claim_from + (int)c;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*cell);
+}
 
 // S^T of 32 keys against one 32-row query tile, accumulated onto `init`.
 template <int D>
@@ -532,7 +566,8 @@ __device__ __forceinline__ void table_from_lds(const YRB_LDS char* region, int l
 // is that max); without it the grow test is the sum test and the output and
 // log-sum-exp use the reference in use, which gives the same values.
 template <int D, bool EXACT>
-__global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs a, int64_t n_qtiles) {
+__global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs a, int64_t n_qtiles, int claim_from,
+                                                                         unsigned claim_slot) {
   constexpr int NW = kPPWaves, BN = kPPBN, QW = 64, BM = NW * QW;
   constexpr int NDS = D / 16, NDT = D / 32;
   using T = Tile<D, BN>;
@@ -551,7 +586,10 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
-  const WorkItem wi = work_item(a, n_qtiles);
+  // (The claim's LDS cell is in the spare region, which no DMA reaches
+  // before the first tile's barrier.)
+  const int item = claim_item(claim_from, claim_slot, (YRB_LDS int*)(lds + 2 * kPPBufs * T::TILEB));
+  const WorkItem wi = work_item_at(a, n_qtiles, item);
   const int b = wi.b, h = wi.h, hk = wi.hk, qtile = wi.qtile;
   const int q0w = qtile * BM + wave * QW;
   const int Sq = (int)a.Sq, Sk = (int)a.Sk;
@@ -592,37 +630,38 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   };
   // Q rotated and pre-multiplied by softmax_scale * log2(e): scores come out
   // of the MFMA in log2 units.  Q and O stay in AGPRs for the whole launch.
-  // Loads: the first query tile's table rows by DMA into the wave's region
-  // of buffers 2/3 (free until the first tile arrives), the first two key
-  // tiles, then Q; the second tile's table rows follow through the same
-  // region while the first tile is rotated.
+  // Loads: the first two key tiles, the first query tile's table rows by
+  // DMA into the wave's region of buffers 2/3 (free until the first tile
+  // arrives), then Q; the second query tile's table rows follow through the
+  // same region while the first query tile is rotated.
   bf16x8 qf[2][NDS];
   {
     YRB_LDS char* const region = lds + (wave < 2 ? 0 : LdsMap<D>::VBASE) + (2 + (wave & 1)) * T::TILEB;
     static_assert(32 * 4 * D <= T::TILEB, "a query tile's table rows fit one tile buffer");
     const float qscale = a.softmax_scale * kLog2e;
     QRaw<D, 2> qr;
-    if (a.cos_sin) table_rows_to_lds<D>(a, q0w, lane, region);
     if (n_tiles > 0) issue(0);
     if (n_tiles > 1) issue(1);
+    if (a.cos_sin) table_rows_to_lds<D>(a, q0w, lane, region);
     load_q_raw<D, 2, false>(a, b, h, q0w, lane, qr);   // Q only
     if (a.cos_sin) {
-      // Loads return in order: the table rows are in once no more than the
-      // later loads are outstanding (both tiles by the fast path, the Q loads).
-      // (The empty asm statements keep the LDS reads between the waits.)
-      if (fast_dma && 2 * BN <= Sk) wait_vmcnt<2 * DMA + 2 * NDS>();
-      else wait_vmcnt<0>();
+      // Q arrives with the table rows (waiting for both keeps the compiler's
+      // own waits, which do not see the DMA, off the rotation below).  The
+      // empty asm statements keep the LDS reads between the waits.
+      wait_vmcnt<0>();
       asm volatile("" ::: "memory");
       table_from_lds<D>(region, lane, qr.tab[0]);
       wait_lgkmcnt<0>();   // the reads are done before the region is refilled
       asm volatile("" ::: "memory");
       table_rows_to_lds<D>(a, q0w + 32, lane, region);
+      rotate_q_tile<D, 2, 0>(a, qr, qf, qscale);
       wait_vmcnt<0>();
       asm volatile("" ::: "memory");
       table_from_lds<D>(region, lane, qr.tab[1]);
+      rotate_q_tile<D, 2, 1>(a, qr, qf, qscale);
+    } else {
+      rotate_q<D, 2>(a, qr, qf, qscale);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    rotate_q<D, 2>(a, qr, qf, qscale);
   }
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -774,8 +813,11 @@ hipError_t launch_pp_as(const AttnArgs& a, hipStream_t stream) {
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (attr != hipSuccess) return attr;
   }
+  static std::atomic<unsigned> next_slot{0};
+  const unsigned slot = next_slot.fetch_add(1, std::memory_order_relaxed) % kClaimSlots;
+  const int claim_from = blocks >= kClaimMinBlocks ? (int)(blocks / 2) : (int)blocks;
   hipLaunchKernelGGL((attn_bf16_pp_kernel<D, EXACT>), dim3((unsigned)blocks), dim3(kPPWaves * 64), LDS_BYTES,
-                     stream, a, n_qtiles);
+                     stream, a, n_qtiles, claim_from, slot);
   return hipGetLastError();
 }
 
