@@ -16,7 +16,7 @@
  *    memory, never synchronises and calls are thread-safe.  Its one piece of
  *    mutable state is a static device array of 64 work-claim counters
  *    (4 KiB per GPU) that attn_prefill_blockwise and attn_block_accumulate
- *    use to balance the second half of their grid across the XCDs: each
+ *    use to balance the last 30 % of their grid across the XCDs: each
  *    launch takes the next counter in turn and leaves it at zero.  Two
  *    launches on one GPU that run at the same time with the same counter
  *    (64 launches apart, or one captured graph replayed on two streams at

@@ -110,7 +110,7 @@ def test_prefill_deterministic():
 
 @pytest.mark.parametrize("S,Hq,Hkv", [(2000, 4, 4), (1300, 3, 1)])
 def test_prefill_claimed_items_repeated(S, Hq, Hkv):
-    # The second half of the grid claims its work items at run time from
+    # The last 30 % of the grid claims its work items at run time from
     # counters that each launch leaves at zero: more launches than counter
     # slots, each into a NaN-filled output, must all write every row and
     # agree bit for bit (grids of 32 and 18 blocks).

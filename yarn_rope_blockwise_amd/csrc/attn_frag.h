@@ -84,15 +84,22 @@ __device__ __forceinline__ void dma_lds_vaddr(unsigned m0_base, const void* g) {
                : "v"(g), "s"(m0_base), "i"(IMM)
                : "memory", "m0", "scc");
 }
-// Same with an SGPR base address and a 32-bit per-lane byte offset.
-template <int IMM>
-__device__ __forceinline__ void dma_lds_saddr(unsigned m0_base, const void* rows, unsigned off) {
-  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(rows), "s"(m0_base), "i"(IMM)
-               : "memory", "m0", "scc");
-}
 #pragma clang diagnostic pop
+
+// The fast tile DMA: SGPR base address, 32-bit per-lane byte offset, m0
+// held by the compiler (one value per K or V group, set once and kept across
+// the group's instructions).  The instruction offset IMM (below 4 KiB) moves
+// both addresses: lane i reads rows + off + IMM and writes m0 + IMM + 16 i.
+// FIRST: the group's first instruction, one wait state after the m0 write.
+template <int IMM, bool FIRST>
+__device__ __forceinline__ void dma_lds_m0(unsigned m0, const void* rows, unsigned off) {
+  static_assert(IMM >= 0 && IMM < 4096, "global instruction offset range");
+  if constexpr (FIRST)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%2" : : "v"(off), "s"(rows), "i"(IMM), "{m0}"(m0)
+                 : "memory");
+  else
+    asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" : : "v"(off), "s"(rows), "i"(IMM), "{m0}"(m0) : "memory");
+}
 
 template <int D, int BN, int NW, bool IS_V>
 __device__ __forceinline__ void load_tile(YRB_LDS char* dst, const __bf16* src, int stride, int k0,
@@ -114,22 +121,28 @@ __device__ __forceinline__ void load_tile(YRB_LDS char* dst, const __bf16* src, 
   });
 }
 
-// Tiles that need no row clamp: each lane's byte offsets (relative to the
-// tile's first row) of its 16-byte chunks in this wave's share of the DMA,
+// Tiles that need no row clamp (the fast path): wave w fills the tile's
+// 1 KiB blocks w LO .. w LO + LO - 1, its n-th instruction with offset
+// n KiB (dma_lds_m0).  Each lane's byte offsets of its 16-byte chunks,
+// relative to the tile's first row and less that instruction offset, are
 // fixed for the whole launch; the tile's row base then goes in SGPRs.
+// The token stride must be at least D (then each offset is at least n KiB:
+// a row is 2D bytes, which divides 1 KiB).  PLACEHOLDER: offsets 16 lane
+// only, for instructions that read a small dummy buffer.
 template <int D, int BN, int NW, bool IS_V>
-__device__ __forceinline__ void tile_offsets(int stride, int wave, int lane,
+__device__ __forceinline__ void tile_offsets(int stride, int wave, int lane, bool placeholder,
                                              unsigned (&off)[TileLoads<D, BN, NW>::LO]) {
   using TL = TileLoads<D, BN, NW>;
   static_assert(TL::EXTRA == 0, "tile DMA must split evenly over the waves");
   constexpr int ROWB = Tile<D, BN>::ROWB;
+  static_assert(1024 % ROWB == 0, "rows tile the 1 KiB blocks");
 #pragma unroll
   for (int n = 0; n < TL::LO; ++n) {
-    const int o = (n * NW + wave) * 1024 + lane * 16;
+    const int o = (wave * TL::LO + n) * 1024 + lane * 16;
     const int r = o / ROWB;
     const int p = (o % ROWB) >> 4;
     const int c = IS_V ? (p ^ vsw<D>(r)) : (p ^ ksw<D>(r));
-    off[n] = (unsigned)(r * stride + c * 8) * 2u;
+    off[n] = placeholder ? (unsigned)(lane * 16) : (unsigned)(r * stride + c * 8) * 2u - (unsigned)(n * 1024);
   }
 }
 
@@ -149,10 +162,10 @@ __device__ __forceinline__ void load_tile_rows(YRB_LDS char* dst, const __bf16* 
                                                int wave) {
   using TL = TileLoads<D, BN, NW>;
   const __bf16* const rows = wave_uniform(tile_rows);
-  const unsigned m0w = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst + wave * 1024);
+  const unsigned m0w = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst + wave * TL::LO * 1024);
   static_for<TL::LO>([&](auto n_tag) YRB_INLINE {
     constexpr int n = decltype(n_tag)::value;
-    dma_lds_saddr<n * NW * 1024>(m0w, rows, off[n]);
+    dma_lds_m0<n * 1024, n == 0>(m0w, rows, off[n]);
   });
 }
 

@@ -54,7 +54,7 @@ constexpr int kPPWaves = 4;    // one per SIMD
 constexpr int kPPBN = 64;      // keys per tile (two quarters)
 constexpr int kPPBufs = 4;     // LDS tile buffers (the tile loop is unrolled by this)
 
-// Work items of the second half of the grid are claimed at run time.  Blocks
+// Work items of the last 30 % of the grid are claimed at run time.  Blocks
 // go round robin over the 8 XCDs and each XCD runs its share at its own
 // clock, which under load differs from XCD to XCD by a few percent: with a
 // fixed item per block the slowest XCD finishes last while the others idle.
@@ -72,6 +72,10 @@ struct ClaimSlot {
   unsigned pad[15];   // one 64-byte line per slot
 };
 __device__ ClaimSlot g_claims[kClaimSlots];
+
+// Source of the placeholder DMA when the fast path is off: 16 lane + n KiB
+// stays inside it.
+__device__ __attribute__((aligned(1024))) unsigned char g_dma_dummy[4096];
 
 // The item of this block: blockIdx.x below claim_from, else claimed.
 __device__ __forceinline__ int claim_item(int claim_from, unsigned slot, YRB_LDS int* cell) {
@@ -314,8 +318,8 @@ struct DmaPlan {
 // Plan of tile u, whose buffer is UB = u % kPPBufs (every argument
 // wave-uniform): tiles below n_fast come from k_rows/v_rows (that tile's
 // first key row) into buffer UB (k_m0/v_m0: buffer 0 plus this wave's
-// 1 KiB slot), the others are placeholders from the first key rows
-// (kb/vb) into the spare region.
+// LO KiB), the others are placeholders from kb/vb (the first key tile, or
+// the dummy buffer when the fast path is off) into the spare region.
 template <int D, int UB>
 __device__ __forceinline__ DmaPlan dma_plan(int u, int n_fast, int n_tiles, const __bf16* k_rows,
                                             const __bf16* v_rows, const __bf16* kb, const __bf16* vb,
@@ -372,8 +376,8 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
   static_assert(!ARRIVE || 2 * NL < D / 8, "the DMA pieces must fit the half step");
   auto dma_at = [&](auto i_tag) YRB_INLINE {   // DMA instruction of step i (1 .. 2 NL)
     constexpr int n = decltype(i_tag)::value - 1;
-    if constexpr (n >= 0 && n < NL) dma_lds_saddr<n * kPPWaves * 1024>(dp->k_m0, dp->k, koff[n]);
-    else if constexpr (n >= NL && n < 2 * NL) dma_lds_saddr<(n - NL) * kPPWaves * 1024>(dp->v_m0, dp->v, voff[n - NL]);
+    if constexpr (n >= 0 && n < NL) dma_lds_m0<n * 1024, n == 0>(dp->k_m0, dp->k, koff[n]);
+    else if constexpr (n >= NL && n < 2 * NL) dma_lds_m0<(n - NL) * 1024, n == NL>(dp->v_m0, dp->v, voff[n - NL]);
   };
   constexpr int NDS = D / 16, NDT = D / 32;
   using S = Steps<D>;
@@ -612,13 +616,17 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   const __bf16* const kbase_s = wave_uniform(kbase);
   const __bf16* const vbase_s = wave_uniform(vbase);
 
-  // Lane offsets of the fast DMA are 32-bit: (BN - 1) rows of stride plus a row.
-  // Without the fast path they are taken with stride 0, which keeps the
-  // placeholder DMA of DmaPlan on the first key row.
-  const bool fast_dma = (int64_t)max(kstride, vstride) * BN * 2 < ((int64_t)1 << 31);
+  // The fast DMA needs a whole first tile (its placeholders read it), and
+  // token strides of at least a row whose BN rows fit the 32-bit lane
+  // offsets.  Without it every tile takes the clamped load and the
+  // placeholders read a dummy buffer.
+  const bool fast_dma = Sk >= BN && min(kstride, vstride) >= D &&
+                        (int64_t)max(kstride, vstride) * BN * 2 < ((int64_t)1 << 31);
   unsigned koff[TL::LO], voff[TL::LO];
-  tile_offsets<D, BN, NW, false>(fast_dma ? kstride : 0, wave, lane, koff);
-  tile_offsets<D, BN, NW, true>(fast_dma ? vstride : 0, wave, lane, voff);
+  tile_offsets<D, BN, NW, false>(kstride, wave, lane, !fast_dma, koff);
+  tile_offsets<D, BN, NW, true>(vstride, wave, lane, !fast_dma, voff);
+  const __bf16* const ph_k = fast_dma ? kbase_s : reinterpret_cast<const __bf16*>(g_dma_dummy);
+  const __bf16* const ph_v = fast_dma ? vbase_s : reinterpret_cast<const __bf16*>(g_dma_dummy);
   auto issue = [&](int t) YRB_INLINE {
     if (fast_dma && (t + 1) * BN <= Sk) {
       load_tile_rows<D, BN, NW>(kbuf(t), kbase_s + (int64_t)t * BN * kstride, koff, wave);
@@ -690,7 +698,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   const int64_t kstep = fast_dma ? (int64_t)BN * kstride : 0, vstep = fast_dma ? (int64_t)BN * vstride : 0;
   const __bf16* k_rows = kbase_s + 2 * kstep;   // tile 2, then one tile further per pipeline tile
   const __bf16* v_rows = vbase_s + 2 * vstep;
-  const unsigned k0_m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds + wave * 1024);
+  const unsigned k0_m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds + wave * TL::LO * 1024);
   const unsigned v0_m0 = k0_m0 + LdsMap<D>::VBASE;
   const unsigned spare_m0 = k0_m0 + 2 * kPPBufs * T::TILEB;
 
@@ -718,12 +726,15 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
       if (n_tiles > 1) wait_vmcnt<DMA>();
       else wait_vmcnt<0>();
       tile_barrier();
-      const DmaPlan dp = dma_plan<D, 2 % kPPBufs>(2, n_fast, n_tiles, k_rows, v_rows, kbase_s, vbase_s, k0_m0,
+      const DmaPlan dp = dma_plan<D, 2 % kPPBufs>(2, n_fast, n_tiles, k_rows, v_rows, ph_k, ph_v, k0_m0,
                                                   v0_m0, spare_m0);
       static_for<TL::LO>([&](auto n_tag) YRB_INLINE {
         constexpr int n = decltype(n_tag)::value;
-        dma_lds_saddr<n * NW * 1024>(dp.k_m0, dp.k, koff[n]);
-        dma_lds_saddr<n * NW * 1024>(dp.v_m0, dp.v, voff[n]);
+        dma_lds_m0<n * 1024, n == 0>(dp.k_m0, dp.k, koff[n]);
+      });
+      static_for<TL::LO>([&](auto n_tag) YRB_INLINE {
+        constexpr int n = decltype(n_tag)::value;
+        dma_lds_m0<n * 1024, n == 0>(dp.v_m0, dp.v, voff[n]);
       });
       if (dp.slow) issue(2);
     }
@@ -753,7 +764,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
       // K(2t+2) from it, and the DMA of tile t+3 into the buffer of tile t-1
       k_rows += kstep;
       v_rows += vstep;
-      const DmaPlan dp = dma_plan<D, (BT + 3) % kPPBufs>(t + 3, n_fast, n_tiles, k_rows, v_rows, kbase_s, vbase_s,
+      const DmaPlan dp = dma_plan<D, (BT + 3) % kPPBufs>(t + 3, n_fast, n_tiles, k_rows, v_rows, ph_k, ph_v,
                                                          k0_m0, v0_m0, spare_m0);
       g = half_step<D, 1, 0, 0, BT1, 0, false, true, EXACT, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, mk,
                                                                   nd, &dp,
@@ -815,7 +826,7 @@ hipError_t launch_pp_as(const AttnArgs& a, hipStream_t stream) {
   }
   static std::atomic<unsigned> next_slot{0};
   const unsigned slot = next_slot.fetch_add(1, std::memory_order_relaxed) % kClaimSlots;
-  const int claim_from = blocks >= kClaimMinBlocks ? (int)(blocks / 2) : (int)blocks;
+  const int claim_from = blocks >= kClaimMinBlocks ? (int)(blocks * 7 / 10) : (int)blocks;
   hipLaunchKernelGGL((attn_bf16_pp_kernel<D, EXACT>), dim3((unsigned)blocks), dim3(kPPWaves * 64), LDS_BYTES,
                      stream, a, n_qtiles, claim_from, slot);
   return hipGetLastError();
