@@ -53,6 +53,9 @@ namespace {
 constexpr int kPPWaves = 4;    // one per SIMD
 constexpr int kPPBN = 64;      // keys per tile (two quarters)
 constexpr int kPPBufs = 4;     // LDS tile buffers (the tile loop is unrolled by this)
+// Issue step of the tile barrier in the arrival half step: the S-chain
+// MFMAs of the steps before it need no LDS and run while the waves meet.
+constexpr int kArriveStep = 2;
 
 // Work items of the last 30 % of the grid are claimed at run time.  Blocks
 // go round robin over the 8 XCDs and each XCD runs its share at its own
@@ -373,7 +376,9 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
                                           int wave = 0) {
   constexpr int X = 1 - Y;
   constexpr int NL = TileLoads<D, kPPBN, kPPWaves>::LO;   // DMA instructions per tile per wave, K or V
-  static_assert(!ARRIVE || 2 * NL < D / 8, "the DMA pieces must fit the half step");
+  constexpr int BS = ARRIVE ? kArriveStep : 0;              // barrier step; K reads and DMA follow it
+  static_assert(!ARRIVE || BS + 2 * NL < D / 8, "the DMA pieces must fit the half step");
+  static_assert(BS + D / 16 <= D / 8 - 2, "K reads end two steps before the next half step");
   auto dma_at = [&](auto i_tag) YRB_INLINE {   // DMA instruction of step i (1 .. 2 NL)
     constexpr int n = decltype(i_tag)::value - 1;
     if constexpr (n >= 0 && n < NL) dma_lds_m0<n * 1024, n == 0>(dp->k_m0, dp->k, koff[n]);
@@ -418,21 +423,21 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
       const int f = i - NDS;
       mfma_o(st.o[f % NDT][Y], vf[f / NDT][f % NDT], p_pv[f / NDT]);
     }
-    // Tile arrival (the step-0 MFMA runs meanwhile): this wave's DMA of the
-    // next tile is done, the barrier extends that to every wave; then the
-    // DMA of the tile two ahead, one instruction per step.
+    // Tile arrival (the MFMAs of the steps before run meanwhile): this
+    // wave's DMA of the next tile is done, the barrier extends that to every
+    // wave; then the DMA of the tile two ahead, one instruction per step.
     if (ARRIVE) {
-      if (i == 0) {
+      if (i == BS) {
         wait_vmcnt<2 * NL>();
         tile_barrier();
-      } else {
+      } else if (i > BS) {
         static_for<2 * NL + 1>([&](auto j_tag) YRB_INLINE {
-          if (decltype(j_tag)::value == i) dma_at(j_tag);
+          if (decltype(j_tag)::value + BS == i) dma_at(j_tag);
         });
       }
     }
-    // LDS fragment reads
-    if (READ_K && i >= 1 && i <= NDS) kf[i - 1] = read_k_at<D, BK, KQK>(lds, m, i - 1);
+    // LDS fragment reads (K fragment j after the MFMA of step j that used it)
+    if (READ_K && i >= 1 + BS && i <= NDS + BS) kf[i - 1 - BS] = read_k_at<D, BK, KQK>(lds, m, i - 1 - BS);
     if (READ_V && i < NDS) vf[i / NDT][i % NDT] = read_v_at<D, BV, KQV>(lds, m, i / NDT, i % NDT);
     // softmax of tile X
 #pragma unroll
