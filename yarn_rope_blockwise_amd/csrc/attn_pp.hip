@@ -390,7 +390,7 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
   const float base_x = of.base[X];
   float acc = st.l[X];
   of.l_prev[X] = acc;
-  float qs = 0.f;   // without EXACT: this quarter's P sum
+  float qs = 0.f;   // without EXACT: this quarter's P sum (set at its first pair)
   float p[16];
   unsigned w[8];
   float mx = 0.f;
@@ -449,7 +449,14 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (S::pack_at(u) == i) pack_pair(p, u, w);
-      if (S::dot_at(u) == i) add_pair(p, u, EXACT ? acc : qs);
+      if (S::dot_at(u) == i) {
+        if (!EXACT && u == 0) {   // the quarter sum starts at its first pair
+          qs = p[0] + p[1];
+          pin(qs);
+        } else {
+          add_pair(p, u, EXACT ? acc : qs);
+        }
+      }
     }
     if constexpr (EXACT) {
 #pragma unroll
@@ -595,6 +602,10 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
+  // The arguments the item's set-up reads go into SGPRs first, so their
+  // loads go out together with the claim's rather than after it.
+  asm volatile("" ::"s"(a.q), "s"(a.k), "s"(a.v), "s"(a.cos_sin), "s"(a.B), "s"(a.Sq), "s"(a.Sk), "s"(a.Hq),
+               "s"(a.Hkv), "s"(a.qs[0]), "s"(a.ks[0]), "s"(a.vs[0]));
   // (The claim's LDS cell is in the spare region, which no DMA reaches
   // before the first tile's barrier.)
   const int item = claim_item(claim_from, claim_slot, (YRB_LDS int*)(lds + 2 * kPPBufs * T::TILEB));
