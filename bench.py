@@ -44,7 +44,7 @@ METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HB
 MEASURED_TRAFFIC = {
     "attn_bf16_pp_kernel": {
         "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
-        "sha256": "2b733a6e13df4cbc6be32da547517dd81e96192589749d88718b4f8c5aca48f0",
+        "sha256": "1f22a44d9b5c5c3d7485257ba4abf0807f44f1e4b28d4077c886a0599571264e",
         "fetch_kib": 1042608, "write_kib": 131091},
     "decode_bf16_kernel": {
         "files": ("csrc/decode.hip", "csrc/common.h"),

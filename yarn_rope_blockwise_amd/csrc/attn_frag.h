@@ -59,9 +59,10 @@ __device__ __forceinline__ void tile_barrier() {
 }
 
 // One tile (BN rows of K or V) global -> LDS.  The tile is TILEB/1024
-// DMA instructions of 1 KiB; wave w issues instructions w, w+NW, ...  Rows
-// past the end are clamped to the last row: finite data, masked out of the
-// softmax.
+// DMA instructions of 1 KiB.  In the clamped load below wave w issues
+// instructions w, w+NW, ...; rows past the end are clamped to the last row:
+// finite data, masked out of the softmax.  (The fast path, tile_offsets and
+// dma_lds_m0, gives each wave LO consecutive blocks instead.)
 template <int D, int BN, int NW>
 struct TileLoads {
   static constexpr int INSTR = Tile<D, BN>::TILEB / 1024;
@@ -69,10 +70,10 @@ struct TileLoads {
   static constexpr int EXTRA = INSTR % NW;             // waves < EXTRA issue LO + 1
 };
 
-// global_load_lds_dwordx4: lane i's 16 bytes land at m0 + 16*i, with
-// m0 = m0_base + IMM.  The constant is added inside the asm, so the compiler
-// cannot hoist one m0 value per (buffer, instruction) out of a loop into
-// SGPRs.  Issued from asm so the compiler does not add a vmcnt(0) before
+// global_load_lds_dwordx4 with a per-lane 64-bit address: lane i's 16
+// bytes land at m0 + 16*i, with m0 = m0_base + IMM written inside the asm
+// (used off the hot loop: the clamped tile load and the table rows).  The
+// DMA is issued from asm so the compiler does not add a vmcnt(0) before
 // every LDS read of another buffer: ordering is by explicit vmcnt waits and
 // barriers.  No register outputs.
 #pragma clang diagnostic push

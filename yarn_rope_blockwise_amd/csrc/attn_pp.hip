@@ -307,10 +307,10 @@ __device__ __forceinline__ u32x2 read_v_part(const YRB_LDS char* lds, const LdsM
 // The DMA of one tile, spread over the issue steps of a half step: source
 // rows (SGPRs) and destination LDS addresses of K and V.  A tile that the
 // fast path cannot load (past the keys the workgroup needs, ragged, or
-// strides beyond the 32-bit lane offsets) still issues the same number of
-// instructions, from the first key rows into a spare LDS region, so the
-// vmcnt count per tile stays fixed; `slow` then asks for the clamped load
-// of a ragged tile after the half step.
+// strides outside the fast path's range) still issues the same number of
+// instructions, placeholders into a spare LDS region, so the vmcnt count
+// per tile stays fixed; `slow` then asks for the clamped load of a ragged
+// tile after the half step.
 struct DmaPlan {
   const __bf16* k;
   const __bf16* v;
