@@ -423,6 +423,9 @@ __device__ __forceinline__ bool half_step(WaveState<D, 2>& st, Offsets& of, cons
       const int f = i - NDS;
       mfma_o(st.o[f % NDT][Y], vf[f / NDT][f % NDT], p_pv[f / NDT]);
     }
+    // A PV MFMA issues first in its step: left free, the scheduler puts the
+    // step's DMA and LDS reads ahead of it, and the MFMA pipe waits.
+    if (i >= NDS) __builtin_amdgcn_sched_barrier(0);
     // Tile arrival (the MFMAs of the steps before run meanwhile): this
     // wave's DMA of the next tile is done, the barrier extends that to every
     // wave; then the DMA of the tile two ahead, one instruction per step.
