@@ -9,6 +9,9 @@
 // fp32 arithmetic, bf16 results rounded to nearest even.  HBM-bound: each
 // thread moves two 16-byte halves of one row and reads its table slice
 // (shared by all heads of a token, so it stays in L2).
+#include <algorithm>
+#include <cstdint>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -18,12 +21,13 @@ struct ThetaPack {
   double t[64];
 };
 
-__global__ __launch_bounds__(256) void rope_tables_kernel(ThetaPack th, int half, int64_t pos0,
+// half = d/2 is 32 or 64: row and pair index by shift and mask.
+__global__ __launch_bounds__(256) void rope_tables_kernel(ThetaPack th, int log2_half, int64_t pos0,
                                                           int64_t total, float2* out) {
   int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  int64_t r = idx / half;
-  int i = (int)(idx - r * half);
+  int64_t r = idx >> log2_half;
+  int i = (int)(idx & ((1 << log2_half) - 1));
   double a = (double)(pos0 + r) * th.t[i];
   double s, c;
   sincos(a, &s, &c);
@@ -32,12 +36,13 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(ThetaPack th, int half
 
 hipError_t launch_rope_tables(const double* theta, int half, int64_t pos0, int64_t n_pos,
                               float* cos_sin, hipStream_t stream) {
+  if (half != 32 && half != 64) return hipErrorInvalidValue;
   ThetaPack th;
   for (int i = 0; i < 64; ++i) th.t[i] = i < half ? theta[i] : 0.0;
   int64_t total = n_pos * half;
   if (total == 0) return hipSuccess;
   int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(rope_tables_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, th, half,
+  hipLaunchKernelGGL(rope_tables_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, th, half == 64 ? 6 : 5,
                      pos0, total, reinterpret_cast<float2*>(cos_sin));
   return hipGetLastError();
 }
@@ -68,18 +73,19 @@ struct Vec<float> {
   }
 };
 
+// Grid: x = token s, y = groups of 256 (head, chunk) threads of that token,
+// z = batch b (batch_base + blockIdx.z): no index divisions beyond the
+// constant PER_ROW.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t total) {
+__global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t batch_base) {
   constexpr int N = Vec<T>::N;
   constexpr int PER_ROW = (D / 2) / N;  // threads per (b, s, h) row
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int c = (int)(idx % PER_ROW);
-  int64_t row = idx / PER_ROW;
-  const int64_t h = row % a.H;
-  row /= a.H;
-  const int64_t s = row % a.S;
-  const int64_t b = row / a.S;
+  const int j = (int)blockIdx.y * 256 + (int)threadIdx.x;
+  if (j >= (int)a.H * PER_ROW) return;
+  const int c = j % PER_ROW;
+  const int64_t h = j / PER_ROW;
+  const int64_t s = blockIdx.x;
+  const int64_t b = batch_base + blockIdx.z;
   const int64_t pos = a.pos_ids ? (int64_t)a.pos_ids[b * a.S + s] : a.pos_offset + s;
   const T* xr = reinterpret_cast<const T*>(a.x) + b * a.xs[0] + s * a.xs[1] + h * a.xs[2];
   T* yr = reinterpret_cast<T*>(a.y) + b * a.ys[0] + s * a.ys[1] + h * a.ys[2];
@@ -108,12 +114,18 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t tot
 template <typename T, int D>
 static hipError_t launch_rope_t(const RopeArgs& a, hipStream_t stream) {
   constexpr int PER_ROW = (D / 2) / Vec<T>::N;
-  int64_t total = a.B * a.S * a.H * PER_ROW;
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL((rope_apply_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
-                     total);
-  return hipGetLastError();
+  if (a.B == 0 || a.S == 0 || a.H == 0) return hipSuccess;
+  // a dispatch's x extent (blocks x 256 work-items) is a 32-bit count
+  if (a.S > (int64_t)(UINT32_MAX / 256) || a.H * PER_ROW > INT32_MAX) return hipErrorInvalidValue;
+  const unsigned groups = (unsigned)((a.H * PER_ROW + 255) / 256);
+  constexpr int64_t kMaxZ = 65535;   // grid z limit: batches go in slices of it
+  for (int64_t b0 = 0; b0 < a.B; b0 += kMaxZ) {
+    const unsigned nb = (unsigned)std::min<int64_t>(kMaxZ, a.B - b0);
+    hipLaunchKernelGGL((rope_apply_kernel<T, D>), dim3((unsigned)a.S, groups, nb), dim3(256), 0, stream, a, b0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_rope_apply(int dtype, int D, const RopeArgs& a, hipStream_t stream) {
