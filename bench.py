@@ -50,8 +50,8 @@ METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HB
 MEASURED_TRAFFIC = {
     "attn_bf16_pp_kernel": {
         "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
-        "sha256": "1f22a44d9b5c5c3d7485257ba4abf0807f44f1e4b28d4077c886a0599571264e",
-        "fetch_kib": 1042608, "write_kib": 131091},
+        "sha256": "be06d95802b52113d8fa8852ec6f4da1c143513d763ccbd0ac4ac0027407dcda",
+        "fetch_kib": 1036651, "write_kib": 131091},
     "decode_bf16_kernel": {
         "files": ("csrc/decode.hip", "csrc/common.h"),
         "sha256": "ae8cf56a20c0a14593b206381671dabe73240b75c121f6dc18a0e1670b2692e2",
