@@ -95,6 +95,31 @@ def test_prefill_prerotated_and_strided():
     assert max_abs(host(o), ref) <= BF16_TOL
 
 
+@pytest.mark.parametrize("kv_tok_stride", [0, 64])
+def test_prefill_overlapping_key_rows(kv_tok_stride):
+    # K and V as views whose token stride is below a row (0: one row
+    # broadcast to every token; 64 elements: rows overlap by half).  The
+    # kernel's fast DMA needs a stride of at least a row, so every tile goes
+    # through the clamped load; the oracle sees the same overlapping values.
+    require_gpu()
+    import torch
+    S, H, D = 300, 2, 128
+    span = (S - 1) * kv_tok_stride + H * D
+    qv, q = draw((1, S, H, D), 31, "bf16")
+    kbuf_v, kbuf = draw((span,), 32, "bf16")
+    vbuf_v, vbuf = draw((span,), 33, "bf16")
+    shape, strides = (1, S, H, D), (span, kv_tok_stride, D, 1)
+    k = torch.as_strided(kbuf, shape, strides)
+    v = torch.as_strided(vbuf, shape, strides)
+    kv = np.lib.stride_tricks.as_strided(kbuf_v, shape, [x * kbuf_v.itemsize for x in strides])
+    vv = np.lib.stride_tricks.as_strided(vbuf_v, shape, [x * vbuf_v.itemsize for x in strides])
+    say(f"attn_prefill_blockwise key/value token stride {kv_tok_stride} S={S}")
+    o = api.attn_prefill_blockwise(q, k, v, 0.09)
+    torch.cuda.synchronize()
+    ref = A.prefill(qv, np.array(kv), np.array(vv), None, 0.09)
+    assert max_abs(host(o), ref) <= BF16_TOL
+
+
 def test_prefill_deterministic():
     require_gpu()
     import torch
