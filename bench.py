@@ -50,7 +50,7 @@ METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HB
 MEASURED_TRAFFIC = {
     "attn_bf16_pp_kernel": {
         "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
-        "sha256": "be06d95802b52113d8fa8852ec6f4da1c143513d763ccbd0ac4ac0027407dcda",
+        "sha256": "b9e3f833616e1b77c5097111593bdcbbb8b3e0ad68b1f5cd3ed92e1e63982cdc",
         "fetch_kib": 1036651, "write_kib": 131091},
     "decode_bf16_kernel": {
         "files": ("csrc/decode.hip", "csrc/common.h"),

@@ -33,12 +33,17 @@
 //    the MFMA hazards explicitly (xdl_drain, the s_nop after settle).
 //  * Key tiles of 64 go global -> LDS with LDS-DMA into four buffers, two
 //    tiles ahead, with one workgroup barrier per tile.  Both sit inside a
-//    half step: the barrier after its first MFMA, the tile's DMA
-//    instructions one per issue step after it, so the matrix pipe runs
-//    through them.  Tiles visible to
-//    every row of the workgroup run through the pipeline as they are; the
-//    few on the causal diagonal or at the ragged end of the keys run
-//    through it too, their scores masked to -inf before the softmax.
+//    half step: the barrier after its first kArriveStep MFMAs, the tile's
+//    DMA instructions one per issue step after it, so the matrix pipe runs
+//    through them.  Tiles visible to every row of the workgroup run through
+//    the pipeline as they are; the few on the causal diagonal or at the
+//    ragged end of the keys run through it too, their scores masked to
+//    -inf before the softmax.
+//  * Set-up per workgroup: the first two key tiles, the query rows' table
+//    rows (by LDS-DMA, coalesced, into buffers still free) and Q go out
+//    together, and Q is rotated from the table in fp32.  Work items run
+//    heaviest first; the last part of the grid claims its items from a
+//    counter so that XCDs running at different clocks finish together.
 #include "attn_frag.h"
 #include "common.h"
 #include "kernels.h"
