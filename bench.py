@@ -234,6 +234,27 @@ def run_ring(steps: int, warmup: int):
                 flops=ring_flops(blk, H, D, full))
 
 
+def run_factor_tables(steps: int, warmup: int):
+    """Tables from a per-pair factor vector, 262144 rows x 64 pairs (the ring share's
+    table size, 128 MiB), timed back to back; smaller tables time the host's call."""
+    import torch
+    from yarn_rope_blockwise_amd import api
+    S, D = 262144, 128
+    lam = np.sort(np.random.default_rng(7).uniform(1.0, 64.0, D // 2))
+    tab = torch.empty((S, D // 2, 2), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        api.rope_tables_build_factors(D, 1e4, lam, S, out=tab)
+    torch.cuda.synchronize()
+    ev = _events(2)
+    ev[0].record()
+    for _ in range(steps):
+        api.rope_tables_build_factors(D, 1e4, lam, S, out=tab)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    return dict(ms=ms, bytes=tab.numel() * 4)
+
+
 def run_copy(steps: int):
     """A plain 1 GiB device-to-device copy: the reference for HBM byte counters."""
     import torch
@@ -352,6 +373,10 @@ def main():
                                        "traffic": measured_traffic("decode_bf16_kernel"),
                                        "kernel": "decode_bf16_kernel",
                                        "bytes_per_launch": dec["bytes"]}}
+        ft = run_factor_tables(max(args.steps, 10), 10)
+        line["factor_tables"] = {"workload": "rope_tables_build_factors 262144 rows x 64 pairs",
+                                 "ms": round(ft["ms"], 4),
+                                 "GB/s": round(ft["bytes"] / (ft["ms"] * 1e-3) / 1e9, 1)}
         log("ring share: uploading blocks and timing")
         ring = run_ring(max(2, args.steps // 5), 2)
         log(f"ring share done: {ring['ms']:.3f} ms")

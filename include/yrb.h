@@ -114,6 +114,24 @@ int rope_tables_build(const yrb_rope_config* cfg, int64_t pos0, int64_t n_pos,
                       void* stream);
 
 /*
+ * rope_tables_build_factors -- cos/sin tables from a per-pair rescale
+ * vector: theta'_i = theta_i / lambda_i, theta_i = base^(-2i/d) ([T] Sec. 4:
+ * a non-uniform scale for each dimension, found by search, in place of one
+ * s or a ramp; the search itself is not here).  lambda_i = s for every i is
+ * PI; a vector per layer is one call per layer.  No temperature: the caller
+ * chooses softmax_scale.
+ *
+ *   head_dim       64 or 128 (else YRB_EUNSUPPORTED).
+ *   base           b > 1, finite.
+ *   factors        host [d/2] fp64, every lambda_i finite and > 0 (else
+ *                  YRB_EINVAL; nothing is launched).
+ *   pos0, n_pos, cos_sin, inv_freq_out   as for rope_tables_build.
+ */
+int rope_tables_build_factors(int32_t head_dim, double base, const double* factors,
+                              int64_t pos0, int64_t n_pos, float* cos_sin,
+                              double* inv_freq_out, void* stream);
+
+/*
  * rope_apply -- rotate every half-split pair (x_i, x_{i+d/2}) of x by the
  * angle of its token's position ([T] Sec. 2 rotation matrix
  * [[cos, -sin], [sin, cos]]):

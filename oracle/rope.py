@@ -110,6 +110,22 @@ def inv_freq(kind: int, head_dim: int, base: float, scale: float = 1.0,
     raise ValueError(f"unknown rope kind {kind}")
 
 
+def inv_freq_factors(head_dim: int, base: float, factors) -> np.ndarray:
+    """theta'_i = theta_i / lambda_i for a per-pair scale vector lambda.
+
+    tecvarsity Section 4 "Deep Dive into LongRoPE": one scale per dimension
+    (found by search) instead of a single s or a ramp.  Reading: lambda_i
+    stretches pair i's wavelength, as s does for every pair under PI, so
+    lambda_i = s for all i is PI exactly.
+    """
+    lam = np.asarray(factors, dtype=np.float64).reshape(-1)
+    if lam.size != head_dim // 2:
+        raise ValueError("one factor per pair")
+    if not np.all(np.isfinite(lam)) or not np.all(lam > 0):
+        raise ValueError("factors must be finite and > 0")
+    return base_inv_freq(head_dim, base) / lam
+
+
 def attn_factor(kind: int, scale: float) -> float:
     """Logit multiplier: (0.1 ln s + 1)**2 for YaRN with s > 1, else 1.
 

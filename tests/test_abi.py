@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_declares_the_five_calls():
     names = declared_functions()
-    for n in ("rope_tables_build", "rope_apply", "attn_prefill_blockwise",
+    for n in ("rope_tables_build", "rope_tables_build_factors", "rope_apply", "attn_prefill_blockwise",
               "attn_block_accumulate", "attn_decode_sink_window", "yrb_status_str"):
         assert n in names
 
@@ -87,6 +87,39 @@ def test_rope_tables_pointer_validation():
     assert _tables({}, n_pos=4, cos_sin=MISALIGNED) == EALIGN
     assert _tables({}, n_pos=-1) == EINVAL
     assert _tables({}, pos0=-5) == EINVAL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_host_factor_frequencies_match_oracle(d):
+    lam = np.random.default_rng(d).uniform(1.0, 64.0, d // 2)
+    th = api.rope_frequencies_factors(d, 5e5, lam)
+    np.testing.assert_allclose(th, R.inv_freq_factors(d, 5e5, lam), rtol=1e-14, atol=0)
+    # a uniform vector is PI, bitwise: the same fp64 division
+    pi, _ = api.rope_frequencies(api.RopeConfig(R.PI, d, 1e4, 8.0, 4096, 1.0, 32.0))
+    assert np.array_equal(api.rope_frequencies_factors(d, 1e4, np.full(d // 2, 8.0)), pi)
+
+
+def _factors(head_dim=128, base=1e4, lam="ones", pos0=0, n_pos=0, cos_sin=None):
+    if isinstance(lam, str):
+        lam = np.ones(head_dim // 2)
+    ptr = None if lam is None else np.ascontiguousarray(lam, np.float64).ctypes.data_as(api._dp)
+    return api.lib().rope_tables_build_factors(head_dim, base, ptr, pos0, n_pos, cos_sin, None,
+                                               None)
+
+
+def test_rope_tables_factors_validation():
+    assert _factors() == OK
+    assert _factors(head_dim=96) == EUNSUP
+    assert _factors(base=1.0) == EINVAL
+    assert _factors(base=float("inf")) == EINVAL
+    assert _factors(lam=None) == EINVAL
+    for bad in (0.0, -2.0, float("nan"), float("inf")):
+        lam = np.ones(64)
+        lam[7] = bad
+        assert _factors(lam=lam) == EINVAL
+    assert _factors(n_pos=4, cos_sin=None) == EINVAL
+    assert _factors(n_pos=4, cos_sin=MISALIGNED) == EALIGN
+    assert _factors(pos0=-1) == EINVAL
 
 
 def _strides(*v):

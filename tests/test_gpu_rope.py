@@ -37,6 +37,35 @@ def test_tables_match_oracle(name, rope, n):
     assert err <= TABLE_TOL, err
 
 
+@pytest.mark.parametrize("d,n,pos0", [(128, 16384, 0), (64, 4100, 12345)])
+def test_factor_tables_match_oracle(d, n, pos0):
+    # Per-pair factors (tecvarsity Section 4): a non-uniform vector, rows at
+    # an offset; every entry against the fp64 oracle.
+    require_gpu()
+    say(f"rope_tables_build_factors d={d} n_pos={n} pos0={pos0}")
+    lam = np.sort(np.random.default_rng(d + n).uniform(1.0, 64.0, d // 2))
+    tab, th = api.rope_tables_build_factors(d, 1e4, lam, n, pos0=pos0)
+    ref_th = R.inv_freq_factors(d, 1e4, lam)
+    np.testing.assert_allclose(th, ref_th, rtol=1e-14, atol=0)
+    got = host(tab)
+    c, s = R.tables(ref_th, np.arange(pos0, pos0 + n))
+    err = max(max_abs(got[..., 0], c), max_abs(got[..., 1], s))
+    assert err <= TABLE_TOL, err
+
+
+def test_factor_tables_uniform_equal_pi_tables():
+    # lambda_i = s for every pair is PI: the two entry points give the same table, bitwise.
+    require_gpu()
+    import torch
+    say("rope_tables_build_factors uniform vs PI")
+    rope = W.GQA_32K[W.PI].rope
+    tab_pi, _, _ = api.rope_tables_build(api.RopeConfig.of(rope), 8192)
+    tab_f, _ = api.rope_tables_build_factors(rope.head_dim, rope.base,
+                                             np.full(rope.head_dim // 2, rope.scale), 8192)
+    torch.cuda.synchronize()
+    assert torch.equal(tab_pi, tab_f)
+
+
 def test_tables_offset_rows():
     require_gpu()
     rope = W.RING_SHARE.rope

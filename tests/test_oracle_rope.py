@@ -223,3 +223,54 @@ def test_tables_bshd_positions():
     assert np.array_equal(y1, y2)
     c, s = R.tables(th, pos)
     np.testing.assert_allclose(y1[1, 4, 2], R.rotate_half(x[1, 4, 2], c[4], s[4]), atol=0)
+
+
+# --- per-pair factor vectors (tecvarsity Section 4, LongRoPE) ---------------
+
+def test_factor_vector_pi_worked_example(golden):
+    # A uniform vector lambda_i = s is PI: the same worked example holds
+    # bitwise (14cs17 "Position Interpolation": position 8000 behaves as 4000).
+    g = golden("pi_worked_example.json")
+    for d in (64, 128):
+        th = R.inv_freq_factors(d, 1e4, np.full(d // 2, g["scale"]))
+        assert np.array_equal(th, R.inv_freq(R.PI, d, 1e4, g["scale"]))
+        c_f, s_f = R.tables(th, [g["position"]])
+        c_pl, s_pl = R.tables(R.inv_freq(R.PLAIN, d, 1e4), [g["interpolated_position"]])
+        assert np.array_equal(c_f, c_pl) and np.array_equal(s_f, s_pl)
+
+
+def test_factor_vector_unit_is_plain_and_each_pair_is_its_own_pi():
+    d, b = 128, 1e4
+    assert np.array_equal(R.inv_freq_factors(d, b, np.ones(d // 2)), R.inv_freq(R.PLAIN, d, b))
+    # non-uniform: pair i interpolated by its own lambda_i, others untouched
+    lam = np.ones(d // 2)
+    lam[[3, 40, 63]] = [2.0, 8.0, 64.0]
+    th = R.inv_freq_factors(d, b, lam)
+    plain = R.inv_freq(R.PLAIN, d, b)
+    for i, s in ((3, 2.0), (40, 8.0), (63, 64.0)):
+        assert th[i] == R.inv_freq(R.PI, d, b, s)[i]
+    keep = np.setdiff1d(np.arange(d // 2), [3, 40, 63])
+    assert np.array_equal(th[keep], plain[keep])
+    # a position p with factor lambda sees the angle plain pair i has at p / lambda
+    c, s_ = R.tables(th, [640])
+    c2, s2 = R.tables(plain, [10])        # 640 / 64 for pair 63
+    assert c[0, 63] == c2[0, 63] and s_[0, 63] == s2[0, 63]
+
+
+def test_factor_vector_expresses_yarn():
+    # YaRN's theta' written as a per-pair vector lambda_i = theta_i / theta'_i
+    w = W.LLAMA_16K.rope
+    yarn = R.inv_freq(R.YARN, w.head_dim, w.base, w.scale, w.orig_ctx, w.alpha, w.beta)
+    lam = R.base_inv_freq(w.head_dim, w.base) / yarn
+    assert np.all(lam >= 1.0 - 1e-15) and np.all(lam <= w.scale * (1 + 1e-15))
+    np.testing.assert_allclose(R.inv_freq_factors(w.head_dim, w.base, lam), yarn, rtol=4.5e-16)
+
+
+@pytest.mark.parametrize("bad", [0.0, -1.0, float("nan"), float("inf")])
+def test_factor_vector_rejects_bad_values(bad):
+    lam = np.ones(64)
+    lam[5] = bad
+    with pytest.raises(ValueError):
+        R.inv_freq_factors(128, 1e4, lam)
+    with pytest.raises(ValueError):
+        R.inv_freq_factors(128, 1e4, np.ones(63))

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libyrb.so")
 PLAIN, PI, NTK, YARN = 0, 1, 2, 3
 BF16, F32 = 0, 1
 ACC_FIRST, ACC_FINALIZE = 1, 2
-EXPORTS = ("rope_tables_build", "rope_apply", "attn_prefill_blockwise",
+EXPORTS = ("rope_tables_build", "rope_tables_build_factors", "rope_apply", "attn_prefill_blockwise",
            "attn_block_accumulate", "attn_decode_sink_window", "yrb_status_str")
 
 _i64 = ctypes.c_int64
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.yrb_status_str.restype = ctypes.c_char_p
         L.rope_tables_build.argtypes = [ctypes.POINTER(YrbRopeConfig), _i64, _i64, _vp, _dp, _dp,
                                         _vp]
+        L.rope_tables_build_factors.argtypes = [_i32, ctypes.c_double, _dp, _i64, _i64, _vp, _dp,
+                                                _vp]
         L.rope_apply.argtypes = [_vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64p, _i64p, _vp, _i64,
                                  _i64, _vp, _vp]
         L.attn_prefill_blockwise.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64,
@@ -160,6 +162,35 @@ def rope_tables_build(cfg: RopeConfig, n_pos: int, pos0: int = 0, out=None, devi
     _check("rope_tables_build", lib().rope_tables_build(ctypes.byref(c), pos0, n_pos, _ptr(out),
                                                           th, ctypes.byref(af), _stream()))
     return out, np.array(th[:], dtype=np.float64), af.value
+
+
+def _factor_array(head_dim: int, factors):
+    f = np.ascontiguousarray(np.asarray(factors, dtype=np.float64).reshape(-1))
+    if f.size != head_dim // 2:
+        raise ValueError(f"need {head_dim // 2} factors, got {f.size}")
+    return f
+
+
+def rope_frequencies_factors(head_dim: int, base: float, factors):
+    """theta'_i = theta_i / lambda_i (fp64, host) from the library, no launch."""
+    f = _factor_array(head_dim, factors)
+    th = (ctypes.c_double * (head_dim // 2))()
+    _check("rope_tables_build_factors", lib().rope_tables_build_factors(
+        head_dim, base, f.ctypes.data_as(_dp), 0, 0, None, th, None))
+    return np.array(th[:], dtype=np.float64)
+
+
+def rope_tables_build_factors(head_dim: int, base: float, factors, n_pos: int, pos0: int = 0,
+                              out=None, device="cuda"):
+    """cos/sin table [n_pos, d/2, 2] fp32 from per-pair factors; returns (table, theta')."""
+    import torch
+    f = _factor_array(head_dim, factors)
+    if out is None:
+        out = torch.empty((n_pos, head_dim // 2, 2), dtype=torch.float32, device=device)
+    th = (ctypes.c_double * (head_dim // 2))()
+    _check("rope_tables_build_factors", lib().rope_tables_build_factors(
+        head_dim, base, f.ctypes.data_as(_dp), pos0, n_pos, _ptr(out), th, _stream()))
+    return out, np.array(th[:], dtype=np.float64)
 
 
 # ----------------------------------------------------------------------------

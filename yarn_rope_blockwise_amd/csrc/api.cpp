@@ -125,6 +125,30 @@ int rope_tables_build(const yrb_rope_config* cfg, int64_t pos0, int64_t n_pos, f
       yrb::launch_rope_tables(th, half, pos0, n_pos, cos_sin, static_cast<hipStream_t>(stream)));
 }
 
+// theta'_i = theta_i / lambda_i for a caller's per-pair vector (tecvarsity
+// Sec. 4, LongRoPE's non-uniform per-dimension scale).
+int rope_tables_build_factors(int32_t head_dim, double base, const double* factors, int64_t pos0,
+                              int64_t n_pos, float* cos_sin, double* inv_freq_out, void* stream) {
+  if (!dim_ok(head_dim)) return YRB_EUNSUPPORTED;
+  if (!(base > 1.0) || !std::isfinite(base)) return YRB_EINVAL;
+  if (!factors) return YRB_EINVAL;
+  const int half = head_dim / 2;
+  for (int i = 0; i < half; ++i)
+    if (!(factors[i] > 0.0) || !std::isfinite(factors[i])) return YRB_EINVAL;
+  if (pos0 < 0 || n_pos < 0) return YRB_EINVAL;
+  if (n_pos > 0 && !cos_sin) return YRB_EINVAL;
+  if (n_pos > 0 && !aligned16(cos_sin)) return YRB_EALIGN;
+  if (n_pos > (int64_t(1) << 40) || pos0 > (int64_t(1) << 50)) return YRB_EINVAL;
+  double th[64];
+  const double d = head_dim;
+  for (int i = 0; i < half; ++i) th[i] = std::pow(base, -2.0 * i / d) / factors[i];
+  if (inv_freq_out)
+    for (int i = 0; i < half; ++i) inv_freq_out[i] = th[i];
+  if (n_pos == 0) return YRB_OK;
+  return hip_status(
+      yrb::launch_rope_tables(th, half, pos0, n_pos, cos_sin, static_cast<hipStream_t>(stream)));
+}
+
 int rope_apply(const void* x, void* y, int32_t dtype, int64_t B, int64_t S, int64_t H, int64_t D,
                const int64_t x_strides[3], const int64_t y_strides[3], const float* cos_sin,
                int64_t n_table_rows, int64_t pos_offset, const int32_t* pos_ids, void* stream) {

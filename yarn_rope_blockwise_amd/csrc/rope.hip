@@ -28,10 +28,29 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(ThetaPack th, int log2
   if (idx >= total) return;
   int64_t r = idx >> log2_half;
   int i = (int)(idx & ((1 << log2_half) - 1));
-  double a = (double)(pos0 + r) * th.t[i];
-  double s, c;
-  sincos(a, &s, &c);
-  out[idx] = make_float2((float)c, (float)s);
+  const double a = (double)(pos0 + r) * th.t[i];
+  // Reduce a modulo 2 pi in fp64 (Cody and Waite's two-constant
+  // subtraction: 2 pi = P1 + P2, P1 with 33 significant bits so that k * P1
+  // is exact for |k| < 2^20), then take sin/cos of the reduced angle in fp32.
+  // The reduced angle keeps ~2^-45 absolute error in fp64 and ~2^-23 after
+  // rounding to fp32, far inside the table tolerance.  Larger angles take
+  // the fp64 library routine.
+  constexpr double kP1 = 0x1.921fb544p+2;           // 2 pi rounded to 33 significant bits
+  constexpr double kP2 = 0x1.0b4611a626331p-32;     // 2 pi - kP1 (rounded; 1.4e-26 left over)
+  constexpr double kInv2Pi = 0x1.45f306dc9c883p-3;  // 1 / (2 pi)
+  float s, c;
+  const double k = __builtin_rint(a * kInv2Pi);
+  if (__builtin_fabs(k) < 1048576.0) {
+    double t = __builtin_fma(-k, kP1, a);
+    t = __builtin_fma(-k, kP2, t);
+    sincosf((float)t, &s, &c);
+  } else {
+    double sd, cd;
+    sincos(a, &sd, &cd);
+    s = (float)sd;
+    c = (float)cd;
+  }
+  out[idx] = make_float2(c, s);
 }
 
 hipError_t launch_rope_tables(const double* theta, int half, int64_t pos0, int64_t n_pos,
