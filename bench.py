@@ -184,6 +184,42 @@ def run_decode(steps: int, warmup: int):
     return dict(ms=ms, bytes=kv_bytes + other, kv_bytes=kv_bytes)
 
 
+def run_decode_fp8(steps: int, warmup: int):
+    """The decode workload with E4M3 K/V caches and per-(sequence, head) scales."""
+    import torch
+    from yarn_rope_blockwise_amd import api, synth
+    from yarn_rope_blockwise_amd import workloads as W
+    w = W.SINK_DECODE
+    C = w.n_sink + w.window
+    q = _upload((w.batch, w.n_q_heads, w.head_dim), 0)
+    kc = torch.from_numpy(synth.e4m3_codes((w.batch, w.n_kv_heads, C, w.head_dim), 1)).cuda()
+    vc = torch.from_numpy(synth.e4m3_codes((w.batch, w.n_kv_heads, C, w.head_dim), 2)).cuda()
+    ks = torch.from_numpy(synth.uniform_scales((w.batch, w.n_kv_heads), 4)).cuda()
+    vs = torch.from_numpy(synth.uniform_scales((w.batch, w.n_kv_heads), 5)).cuda()
+    lens = torch.full((w.batch,), C, dtype=torch.int32, device="cuda")
+    rh = torch.from_numpy(synth.ring_heads(w.batch, w.window)).cuda()
+    tab, _, af = api.rope_tables_build(api.RopeConfig.of(w.rope), C)
+    scale = af / np.sqrt(w.head_dim)
+    out = torch.empty_like(q)
+
+    def call():
+        api.attn_decode_sink_window_fp8(q, kc, vc, lens, w.n_sink, w.window, tab, scale, rh,
+                                        out, k_scale=ks, v_scale=vs)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = _events(2)
+    ev[0].record()
+    for _ in range(steps):
+        call()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    kv_bytes = 2 * kc.numel()
+    other = q.numel() * 2 * 2 + lens.numel() * 4 * 2 + ks.numel() * 4 * 2
+    return dict(ms=ms, bytes=kv_bytes + other, kv_bytes=kv_bytes)
+
+
 def run_ring(steps: int, warmup: int):
     import torch
     from yarn_rope_blockwise_amd import api
@@ -306,7 +342,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip decode and ring share")
     ap.add_argument("--workload", default="all",
-                    choices=["all", "prefill", "decode", "ring", "copy"],
+                    choices=["all", "prefill", "decode", "decode_fp8", "ring", "copy"],
                     help="run one workload alone (for profiling); the JSON line needs 'all'")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -322,6 +358,7 @@ def main():
     if args.workload != "all":
         only = {"prefill": lambda: run_prefill(args.steps, args.warmup),
                 "decode": lambda: run_decode(args.steps, max(3 * args.warmup, 10)),
+                "decode_fp8": lambda: run_decode_fp8(args.steps, max(3 * args.warmup, 10)),
                 "ring": lambda: run_ring(args.steps, 2),
                 "copy": lambda: run_copy(args.steps)}[args.workload]()
         only.pop("per_call_ms", None)
@@ -373,6 +410,16 @@ def main():
                                        "traffic": measured_traffic("decode_bf16_kernel"),
                                        "kernel": "decode_bf16_kernel",
                                        "bytes_per_launch": dec["bytes"]}}
+        log("decode, fp8 cache: uploading caches and timing")
+        d8 = run_decode_fp8(max(args.steps, 10), max(3 * args.warmup, 10))
+        g8 = d8["bytes"] / (d8["ms"] * 1e-3) / 1e9
+        line["decode_fp8"] = {"workload": "sink_decode_b64_h32_4p4096_e4m3", "ms": round(d8["ms"], 4),
+                              "GB/s": round(g8, 1),
+                              "roofline": {"bound": "hbm", "achieved": round(g8, 1),
+                                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                           "frac": round(g8 / PEAK_HBM_GBS, 4), "traffic": None,
+                                           "kernel": "decode_bf16_kernel<fp8>",
+                                           "bytes_per_launch": d8["bytes"]}}
         ft = run_factor_tables(max(args.steps, 10), 10)
         line["factor_tables"] = {"workload": "rope_tables_build_factors 262144 rows x 64 pairs",
                                  "ms": round(ft["ms"], 4),

@@ -248,6 +248,34 @@ int attn_decode_sink_window(const void* q, const void* k_cache, const void* v_ca
                             const float* cos_sin, int64_t n_table_rows,
                             float softmax_scale, void* stream);
 
+/*
+ * attn_decode_sink_window_fp8 -- attn_decode_sink_window over an FP8 K/V
+ * cache, half the bytes of a bf16 one ([T] Sec. 7, FAQ 3: quantising the KV
+ * cache to FP8).  The pages fix no format.  This reading takes OCP E4M3
+ * codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities, S.1111.111 is NaN) and one fp32 dequantisation scale per
+ * (sequence, key/value head) for K and one for V: a cached value is
+ * scale * decode(code).  Everything else is as for attn_decode_sink_window.
+ *
+ *   q, o           device bf16 [B][Hq][D], q_strides / o_strides (b, h).
+ *   k_cache,
+ *   v_cache        device bytes [B][Hkv][C][D] of E4M3 codes, cache_strides
+ *                  (b, h, slot) in bytes, each a multiple of 16; base
+ *                  pointers 16-byte aligned (else YRB_EALIGN).
+ *   k_scale,
+ *   v_scale        device fp32 [B][Hkv] contiguous, or NULL (= 1).
+ * A NaN code reaches the output as NaN.
+ */
+int attn_decode_sink_window_fp8(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                int64_t n_sink, int64_t window,
+                                const int64_t q_strides[2], const int64_t cache_strides[3],
+                                const int64_t o_strides[2],
+                                const int32_t* cache_len, const int32_t* ring_head,
+                                const float* k_scale, const float* v_scale,
+                                const float* cos_sin, int64_t n_table_rows,
+                                float softmax_scale, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* yrb_status_str(int status);
 

@@ -232,6 +232,33 @@ def test_decode_validation():
     assert _decode(B=0) == OK
 
 
+def _decode_fp8(**over):
+    L = api.lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=2, Hq=4, Hkv=4, D=128, sink=4, win=60,
+             qs=_strides(512, 128), cs=_strides(4 * 64 * 128, 64 * 128, 128),
+             os=_strides(512, 128), len=FAKE, rh=None, ks=None, vs=None, tab=FAKE, rows=64,
+             scale=0.1)
+    a.update(over)
+    return L.attn_decode_sink_window_fp8(a["q"], a["k"], a["v"], a["o"], a["B"], a["Hq"],
+                                         a["Hkv"], a["D"], a["sink"], a["win"], a["qs"], a["cs"],
+                                         a["os"], a["len"], a["rh"], a["ks"], a["vs"], a["tab"],
+                                         a["rows"], ctypes.c_float(a["scale"]), None)
+
+
+def test_decode_fp8_validation():
+    # every call here fails validation (or has B = 0), so nothing is launched
+    assert _decode_fp8(B=0) == OK
+    assert _decode_fp8(D=96) == EUNSUP
+    assert _decode_fp8(Hq=12, Hkv=4) == EUNSUP
+    assert _decode_fp8(win=0) == EINVAL
+    assert _decode_fp8(rows=63) == EINVAL
+    assert _decode_fp8(len=None) == EINVAL
+    assert _decode_fp8(k=MISALIGNED) == EALIGN
+    assert _decode_fp8(cs=_strides(4 * 64 * 128, 64 * 128, 136)) == EALIGN   # 136-byte slot stride
+    assert _decode_fp8(ks=MISALIGNED) == EALIGN
+    assert _decode_fp8(o=MISALIGNED) == EALIGN
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(api, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(api, "_lib", None)

@@ -118,3 +118,102 @@ def test_decode_streaming_equals_masked_attention():
         ref[h] = A.attention_full(qq, kk, vseq[kept, h], scale, np.array([len(kept) - 1]), pos,
                                   A.all_visible)[0]
     assert max_abs(host(o[0]), ref) <= BF16_TOL
+
+
+# ---------------------------------------------------------------------------
+# attn_decode_sink_window_fp8: E4M3 K/V caches with per-(sequence, head) scales
+# ---------------------------------------------------------------------------
+
+def _fp8_case(B, Hq, Hkv, D, n_sink, window, lens, ring_heads, rope, seed=0, scales=True):
+    import torch
+    from oracle import fp8
+    C = n_sink + window
+    tab, th, _ = api.rope_tables_build(api.RopeConfig.of(rope), C)
+    qv, q = draw((B, Hq, D), seed + 0, "bf16")
+    kc = synth.e4m3_codes((B, Hkv, C, D), seed + 1)
+    vc = synth.e4m3_codes((B, Hkv, C, D), seed + 2)
+    ks = synth.uniform_scales((B, Hkv), seed + 4) if scales else np.ones((B, Hkv), np.float32)
+    vs = synth.uniform_scales((B, Hkv), seed + 5) if scales else np.ones((B, Hkv), np.float32)
+    kv = fp8.e4m3_decode(kc) * ks.astype(np.float64)[:, :, None, None]
+    vv = fp8.e4m3_decode(vc) * vs.astype(np.float64)[:, :, None, None]
+    dev = dict(k=torch.from_numpy(kc).cuda(), v=torch.from_numpy(vc).cuda(),
+               ks=torch.from_numpy(ks).cuda() if scales else None,
+               vs=torch.from_numpy(vs).cuda() if scales else None,
+               lens=torch.tensor(np.asarray(lens, np.int32), device="cuda"),
+               rh=None if ring_heads is None else torch.tensor(np.asarray(ring_heads, np.int32),
+                                                               device="cuda"))
+    scale = R.softmax_scale(rope.kind, rope.scale, D)
+    return tab, th, scale, (qv, kv, vv), q, dev
+
+
+def test_decode_fp8_full_sink_config():
+    # The 64 x 32 x (4 + 4096) decode with the cache in E4M3 (half the bytes).
+    require_gpu()
+    import torch
+    w = W.SINK_DECODE
+    C = w.n_sink + w.window
+    rh = synth.ring_heads(w.batch, w.window)
+    tab, th, scale, (qv, kv, vv), q, dv = _fp8_case(
+        w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_sink, w.window, [C] * w.batch, rh,
+        w.rope, seed=70)
+    say("attn_decode_sink_window_fp8 B=64 H=32 C=4100 full size")
+    o = api.attn_decode_sink_window_fp8(q, dv["k"], dv["v"], dv["lens"], w.n_sink, w.window, tab,
+                                        scale, ring_head=dv["rh"], k_scale=dv["ks"],
+                                        v_scale=dv["vs"])
+    torch.cuda.synchronize()
+    got = host(o)
+    bs = synth.sample_rows(w.batch, 6, 321, must=[0, w.batch - 1])
+    ref = A.decode_sink_window(qv[bs], kv[bs], vv[bs], th, scale, w.n_sink, w.window,
+                               [C] * len(bs), rh[bs])
+    err = max_abs(got[bs], ref)
+    assert err <= BF16_TOL, err
+
+
+@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_fp8_edge_cases(G, D):
+    # The same lengths and ring heads as the bf16 edge cases, every sequence
+    # checked; no scales given (1).
+    require_gpu()
+    import torch
+    n_sink, window = 4, 300
+    C = n_sink + window
+    lens = [0, 1, 3, 4, 5, 150, C, C, C, C + 1, C]
+    heads = [0, 0, 0, 0, 0, 7, 0, 123, window - 1, 0, window]
+    B, Hkv = len(lens), 2
+    rope = W.Rope(W.YARN, D, 1e4, 4.0, 128)
+    tab, th, scale, (qv, kv, vv), q, dv = _fp8_case(B, Hkv * G, Hkv, D, n_sink, window, lens,
+                                                    heads, rope, seed=80 + G + D, scales=False)
+    say(f"attn_decode_sink_window_fp8 edge cases G={G} D={D}")
+    o = api.attn_decode_sink_window_fp8(q, dv["k"], dv["v"], dv["lens"], n_sink, window, tab,
+                                        scale, ring_head=dv["rh"])
+    torch.cuda.synchronize()
+    got = host(o)
+    for b in range(B):
+        if lens[b] < 0 or lens[b] > C or heads[b] < 0 or heads[b] >= window:
+            assert np.isnan(got[b]).all(), b
+            continue
+        ref = A.decode_sink_window(qv[b:b + 1], kv[b:b + 1], vv[b:b + 1], th, scale, n_sink,
+                                   window, [lens[b]], [heads[b]])
+        if lens[b] == 0:
+            assert np.all(got[b] == 0)
+        assert max_abs(got[b], ref[0]) <= BF16_TOL, b
+
+
+def test_decode_fp8_nan_code_reaches_output():
+    # A NaN code in a visible value row makes that head's output NaN; the
+    # other heads of the sequence are untouched.
+    require_gpu()
+    import torch
+    n_sink, window, D = 4, 60, 128
+    C = n_sink + window
+    rope = W.Rope(W.PLAIN, D, 1e4, 1.0, 4096)
+    tab, th, scale, (qv, kv, vv), q, dv = _fp8_case(1, 2, 2, D, n_sink, window, [C], None, rope,
+                                                    seed=90)
+    dv["v"][0, 1, 10, 5] = 0x7F
+    say("attn_decode_sink_window_fp8 NaN code")
+    o = api.attn_decode_sink_window_fp8(q, dv["k"], dv["v"], dv["lens"], n_sink, window, tab,
+                                        scale, k_scale=dv["ks"], v_scale=dv["vs"])
+    torch.cuda.synchronize()
+    got = host(o)
+    assert np.isnan(got[0, 1, 5]) and not np.isnan(got[0, 0]).any()

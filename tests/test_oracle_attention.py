@@ -303,3 +303,29 @@ def test_planted_gqa_mapping_slip_fails_pin(monkeypatch):
     o = A.prefill(q, k, v, None, 0.3)
     o3 = A.prefill(q[:, :, 1:2], k[:, :, 0:1], v[:, :, 0:1], None, 0.3)
     assert not np.allclose(o[:, :, 1:2], o3)
+
+
+# --- E4M3 decoding for the fp8 KV cache (tecvarsity Section 7, FAQ 3) -------
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    # torch's float8_e4m3fn is the same OCP format: a library routine to pin against.
+    import torch
+    from oracle import fp8
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = fp8.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
+def test_e4m3_decode_closed_forms():
+    from oracle import fp8
+    d = fp8.e4m3_decode
+    assert d([0x7E])[0] == 448.0                 # largest finite: 1.75 * 2^8
+    assert d([0x08])[0] == 2.0 ** -6             # smallest normal
+    assert d([0x01])[0] == 2.0 ** -9             # smallest subnormal
+    assert d([0x38])[0] == 1.0 and d([0xB8])[0] == -1.0
+    assert d([0x00])[0] == 0.0 and np.signbit(d([0x80])[0])
+    assert np.isnan(d([0x7F])[0]) and np.isnan(d([0xFF])[0])
+    pos = d(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)              # codes 0 .. 0x7E increase strictly

@@ -20,7 +20,8 @@ PLAIN, PI, NTK, YARN = 0, 1, 2, 3
 BF16, F32 = 0, 1
 ACC_FIRST, ACC_FINALIZE = 1, 2
 EXPORTS = ("rope_tables_build", "rope_tables_build_factors", "rope_apply", "attn_prefill_blockwise",
-           "attn_block_accumulate", "attn_decode_sink_window", "yrb_status_str")
+           "attn_block_accumulate", "attn_decode_sink_window", "attn_decode_sink_window_fp8",
+           "yrb_status_str")
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -71,6 +72,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m yarn_rope_blockwise_amd.build`")
+        # torch first: libyrb.so then binds to the HIP runtime torch already
+        # loaded, so both work on the same devices, streams and allocations
+        # (loaded the other way round, a process ends up with two runtimes and
+        # the library's launches fail).
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         L.yrb_status_str.argtypes = [ctypes.c_int]
         L.yrb_status_str.restype = ctypes.c_char_p
@@ -89,6 +95,9 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_sink_window.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64,
                                               _i64, _i64, _i64p, _i64p, _i64p, _vp, _vp, _vp,
                                               _i64, ctypes.c_float, _vp]
+        L.attn_decode_sink_window_fp8.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                                  _i64, _i64, _i64p, _i64p, _i64p, _vp, _vp, _vp,
+                                                  _vp, _vp, _i64, ctypes.c_float, _vp]
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -300,4 +309,36 @@ def attn_decode_sink_window(q, k_cache, v_cache, cache_len, n_sink: int, window:
         _arr([k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)]),
         _arr([out.stride(0), out.stride(1)]), _ptr(cache_len), _ptr(ring_head), _ptr(cos_sin),
         cos_sin.shape[0], float(softmax_scale), _stream()))
+    return out
+
+
+def attn_decode_sink_window_fp8(q, k_codes, v_codes, cache_len, n_sink: int, window: int, cos_sin,
+                                softmax_scale: float, ring_head=None, out=None, k_scale=None,
+                                v_scale=None):
+    """q [B,Hq,D] bf16; caches [B,Hkv,C,D] uint8 OCP E4M3 codes (un-rotated keys);
+    k_scale / v_scale fp32 [B,Hkv] dequantisation scales or None (1)."""
+    import torch
+    B, Hq, D = q.shape
+    Hkv = k_codes.shape[1]
+    if k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise ValueError("fp8 caches are passed as uint8 codes")
+    if out is None:
+        out = torch.empty_like(q)
+    if q.stride(2) != 1 or k_codes.stride(3) != 1 or v_codes.stride(3) != 1 or out.stride(2) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    if tuple(k_codes.stride()) != tuple(v_codes.stride()):
+        raise ValueError("k and v caches must share strides")
+    cache_len = cache_len.to(torch.int32).contiguous()
+    if ring_head is not None:
+        ring_head = ring_head.to(torch.int32).contiguous()
+    if k_scale is not None:
+        k_scale = k_scale.to(torch.float32).contiguous()
+    if v_scale is not None:
+        v_scale = v_scale.to(torch.float32).contiguous()
+    _check("attn_decode_sink_window_fp8", lib().attn_decode_sink_window_fp8(
+        _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(out), B, Hq, Hkv, D, n_sink, window,
+        _arr([q.stride(0), q.stride(1)]),
+        _arr([k_codes.stride(0), k_codes.stride(1), k_codes.stride(2)]),
+        _arr([out.stride(0), out.stride(1)]), _ptr(cache_len), _ptr(ring_head), _ptr(k_scale),
+        _ptr(v_scale), _ptr(cos_sin), cos_sin.shape[0], float(softmax_scale), _stream()))
     return out

@@ -301,14 +301,17 @@ int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk, i
   return hip_status(yrb::launch_attention(dtype, (int)D, a, s));
 }
 
-int attn_decode_sink_window(const void* q, const void* k_cache, const void* v_cache, void* o,
-                            int32_t dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
-                            int64_t n_sink, int64_t window, const int64_t q_strides[2],
-                            const int64_t cache_strides[3], const int64_t o_strides[2],
-                            const int32_t* cache_len, const int32_t* ring_head,
-                            const float* cos_sin, int64_t n_table_rows, float softmax_scale,
-                            void* stream) {
-  if (dtype != YRB_BF16) return YRB_EUNSUPPORTED;
+namespace {
+
+// Shared by the bf16 and fp8 decode entry points: validation, then the
+// launch with the cache element type `cache_dtype` (q and o are bf16).
+int decode_common(int cache_dtype, const void* q, const void* k_cache, const void* v_cache, void* o,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t n_sink, int64_t window,
+                  const int64_t q_strides[2], const int64_t cache_strides[3],
+                  const int64_t o_strides[2], const int32_t* cache_len, const int32_t* ring_head,
+                  const float* k_scale, const float* v_scale, const float* cos_sin,
+                  int64_t n_table_rows, float softmax_scale, void* stream) {
+  const int32_t dtype = YRB_BF16;   // q and o
   if (!dim_ok(D)) return YRB_EUNSUPPORTED;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return YRB_EINVAL;
   const int64_t g = Hq / Hkv;
@@ -322,12 +325,17 @@ int attn_decode_sink_window(const void* q, const void* k_cache, const void* v_ca
   if (!strides_nonneg(q_strides, 2) || !strides_nonneg(cache_strides, 3) ||
       !strides_nonneg(o_strides, 2))
     return YRB_EINVAL;
-  if (!strides_aligned(q_strides, 2, dtype) || !strides_aligned(cache_strides, 3, dtype))
-    return YRB_EALIGN;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(cos_sin))
+  const int64_t cache_q = cache_dtype == yrb::kFP8E4M3 ? 16 : 8;   // elements per 16 bytes
+  for (int i = 0; i < 3; ++i)
+    if (cache_strides[i] % cache_q != 0) return YRB_EALIGN;
+  if (!strides_aligned(q_strides, 2, dtype) || !strides_aligned(o_strides, 2, dtype)) return YRB_EALIGN;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(cos_sin))
     return YRB_EALIGN;
   if (n_table_rows < n_sink + window) return YRB_EINVAL;
   yrb::DecodeArgs a{};
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.q = q;
   a.k = k_cache;
   a.v = v_cache;
@@ -346,7 +354,35 @@ int attn_decode_sink_window(const void* q, const void* k_cache, const void* v_ca
   a.ring_head = ring_head;
   a.cos_sin = cos_sin;
   a.softmax_scale = softmax_scale;
-  return hip_status(yrb::launch_decode(dtype, (int)D, a, static_cast<hipStream_t>(stream)));
+  return hip_status(yrb::launch_decode(cache_dtype, (int)D, a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int attn_decode_sink_window(const void* q, const void* k_cache, const void* v_cache, void* o,
+                            int32_t dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                            int64_t n_sink, int64_t window, const int64_t q_strides[2],
+                            const int64_t cache_strides[3], const int64_t o_strides[2],
+                            const int32_t* cache_len, const int32_t* ring_head,
+                            const float* cos_sin, int64_t n_table_rows, float softmax_scale,
+                            void* stream) {
+  if (dtype != YRB_BF16) return YRB_EUNSUPPORTED;
+  return decode_common(yrb::kBF16, q, k_cache, v_cache, o, B, Hq, Hkv, D, n_sink, window,
+                       q_strides, cache_strides, o_strides, cache_len, ring_head, nullptr,
+                       nullptr, cos_sin, n_table_rows, softmax_scale, stream);
+}
+
+int attn_decode_sink_window_fp8(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t n_sink,
+                                int64_t window, const int64_t q_strides[2],
+                                const int64_t cache_strides[3], const int64_t o_strides[2],
+                                const int32_t* cache_len, const int32_t* ring_head,
+                                const float* k_scale, const float* v_scale, const float* cos_sin,
+                                int64_t n_table_rows, float softmax_scale, void* stream) {
+  if ((k_scale && !aligned16(k_scale)) || (v_scale && !aligned16(v_scale))) return YRB_EALIGN;
+  return decode_common(yrb::kFP8E4M3, q, k_cache, v_cache, o, B, Hq, Hkv, D, n_sink, window,
+                       q_strides, cache_strides, o_strides, cache_len, ring_head, k_scale, v_scale,
+                       cos_sin, n_table_rows, softmax_scale, stream);
 }
 
 }  // extern "C"

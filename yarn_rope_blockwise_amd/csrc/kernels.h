@@ -7,7 +7,7 @@
 
 namespace yrb {
 
-enum DType { kBF16 = 0, kF32 = 1 };
+enum DType { kBF16 = 0, kF32 = 1, kFP8E4M3 = 2 };
 
 hipError_t launch_rope_tables(const double* theta, int half, int64_t pos0, int64_t n_pos,
                               float* cos_sin, hipStream_t stream);
@@ -65,7 +65,9 @@ struct DecodeArgs {
   const int32_t* ring_head;      // or null
   const float* cos_sin;
   float softmax_scale;
+  const float* k_scale;          // fp8 caches: [B][Hkv] dequantisation scales, or null (1)
+  const float* v_scale;
 };
-hipError_t launch_decode(int dtype, int D, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode(int cache_dtype, int D, const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace yrb

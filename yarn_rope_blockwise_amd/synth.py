@@ -72,3 +72,19 @@ def sample_rows(n_rows: int, count: int, seed: int, must=()) -> np.ndarray:
     extra = rng.choice(n_rows, size=count, replace=False)
     pick.update(int(r) for r in extra)
     return np.array(sorted(pick), dtype=np.int64)
+
+
+def e4m3_codes(shape, seed: int) -> np.ndarray:
+    """Random 8-bit E4M3 codes (uint8) of moderate magnitude: random sign and
+    mantissa, exponent field 4..9 (values between 2^-3 and about 7.5).  Only
+    bit patterns are drawn; decoding them is the consumer's business."""
+    rng = np.random.default_rng(seed)
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8)
+    exp = rng.integers(4, 10, size=shape, dtype=np.uint8)
+    man = rng.integers(0, 8, size=shape, dtype=np.uint8)
+    return (sign << 7) | (exp << 3) | man
+
+
+def uniform_scales(shape, seed: int, lo: float = 0.05, hi: float = 0.5) -> np.ndarray:
+    """fp32 values drawn uniformly from [lo, hi)."""
+    return np.random.default_rng(seed).uniform(lo, hi, size=shape).astype(np.float32)
