@@ -220,6 +220,56 @@ def run_decode_fp8(steps: int, warmup: int):
     return dict(ms=ms, bytes=kv_bytes + other, kv_bytes=kv_bytes)
 
 
+def run_interleaved(steps: int, warmup: int):
+    """The interleaved pair layout: rope_apply_ex on the 16k K (268 MB moved) and the
+    bf16 decode through attn_decode_sink_window_ex, each timed back to back."""
+    import torch
+    from yarn_rope_blockwise_amd import api, synth
+    from yarn_rope_blockwise_amd import workloads as W
+    w = W.LLAMA_16K
+    k = _upload((w.batch, w.seq, w.n_kv_heads, w.head_dim), 1)
+    tab, _, _ = api.rope_tables_build(api.RopeConfig.of(w.rope), w.seq)
+    kr = torch.empty_like(k)
+    for _ in range(warmup):
+        api.rope_apply_ex(k, tab, layout=api.LAYOUT_INTERLEAVED, out=kr)
+    torch.cuda.synchronize()
+    ev = _events(2)
+    ev[0].record()
+    for _ in range(steps):
+        api.rope_apply_ex(k, tab, layout=api.LAYOUT_INTERLEAVED, out=kr)
+    ev[1].record()
+    torch.cuda.synchronize()
+    rope_ms = ev[0].elapsed_time(ev[1]) / steps
+    rope_bytes = 2 * k.numel() * 2 + w.seq * w.head_dim * 4
+    del k, kr
+    d = W.SINK_DECODE
+    C = d.n_sink + d.window
+    q = _upload((d.batch, d.n_q_heads, d.head_dim), 0)
+    kc = _upload((d.batch, d.n_kv_heads, C, d.head_dim), 1)
+    vc = _upload((d.batch, d.n_kv_heads, C, d.head_dim), 2)
+    lens = torch.full((d.batch,), C, dtype=torch.int32, device="cuda")
+    rh = torch.from_numpy(synth.ring_heads(d.batch, d.window)).cuda()
+    dtab, _, af = api.rope_tables_build(api.RopeConfig.of(d.rope), C)
+    out = torch.empty_like(q)
+
+    def call():
+        api.attn_decode_sink_window_ex(q, kc, vc, lens, d.n_sink, d.window, dtab,
+                                       af / np.sqrt(d.head_dim), layout=api.LAYOUT_INTERLEAVED,
+                                       ring_head=rh, out=out)
+    for _ in range(3 * warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = _events(2)
+    ev[0].record()
+    for _ in range(steps):
+        call()
+    ev[1].record()
+    torch.cuda.synchronize()
+    dec_ms = ev[0].elapsed_time(ev[1]) / steps
+    dec_bytes = 2 * kc.numel() * 2 + q.numel() * 2 * 2 + lens.numel() * 4 * 2
+    return dict(rope_ms=rope_ms, rope_bytes=rope_bytes, dec_ms=dec_ms, dec_bytes=dec_bytes)
+
+
 def run_ring(steps: int, warmup: int):
     import torch
     from yarn_rope_blockwise_amd import api
@@ -420,6 +470,12 @@ def main():
                                            "frac": round(g8 / PEAK_HBM_GBS, 4), "traffic": None,
                                            "kernel": "decode_bf16_kernel<fp8>",
                                            "bytes_per_launch": d8["bytes"]}}
+        il = run_interleaved(max(args.steps, 10), max(args.warmup, 10))
+        line["interleaved_layout"] = {
+            "rope_apply_ex_k16k": {"ms": round(il["rope_ms"], 4),
+                                   "GB/s": round(il["rope_bytes"] / (il["rope_ms"] * 1e-3) / 1e9, 1)},
+            "decode_ex_bf16": {"ms": round(il["dec_ms"], 4),
+                               "GB/s": round(il["dec_bytes"] / (il["dec_ms"] * 1e-3) / 1e9, 1)}}
         ft = run_factor_tables(max(args.steps, 10), 10)
         line["factor_tables"] = {"workload": "rope_tables_build_factors 262144 rows x 64 pairs",
                                  "ms": round(ft["ms"], 4),

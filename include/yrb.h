@@ -70,8 +70,13 @@ extern "C" {
 #define YRB_ROPE_YARN  3      /* per-pair ramp between theta and theta/s, plus temperature  [R], [T] Sec. 3 */
 
 /* Storage types. */
-#define YRB_BF16 0
-#define YRB_F32  1
+#define YRB_BF16     0
+#define YRB_F32      1
+#define YRB_FP8_E4M3 2        /* K/V cache codes of attn_decode_sink_window_ex */
+
+/* Pair layouts of the rotation ([T] Sec. 2 pairs the d dimensions into d/2). */
+#define YRB_LAYOUT_HALF        0   /* (x_i, x_{i+d/2}): every other call */
+#define YRB_LAYOUT_INTERLEAVED 1   /* (x_{2i}, x_{2i+1}): the _ex calls    */
 
 /* attn_block_accumulate flags. */
 #define YRB_ACC_FIRST    1    /* ignore the incoming state: start from m=-inf, l=0, acc=0 */
@@ -152,6 +157,20 @@ int rope_apply(const void* x, void* y, int32_t dtype,
                const int64_t x_strides[3], const int64_t y_strides[3],
                const float* cos_sin, int64_t n_table_rows,
                int64_t pos_offset, const int32_t* pos_ids, void* stream);
+
+/*
+ * rope_apply_ex -- rope_apply with a choice of pair layout: YRB_LAYOUT_HALF
+ * is rope_apply; YRB_LAYOUT_INTERLEAVED rotates adjacent pairs,
+ *   y_{2i} = x_{2i} c - x_{2i+1} s,   y_{2i+1} = x_{2i} s + x_{2i+1} c,
+ * with the same table (pair i's angle).  Any other layout: YRB_EINVAL.
+ * A model in the interleaved layout rotates Q and K with this call and
+ * passes cos_sin = NULL to attn_prefill_blockwise / attn_block_accumulate.
+ */
+int rope_apply_ex(const void* x, void* y, int32_t dtype,
+                  int64_t B, int64_t S, int64_t H, int64_t D,
+                  const int64_t x_strides[3], const int64_t y_strides[3],
+                  const float* cos_sin, int64_t n_table_rows,
+                  int64_t pos_offset, const int32_t* pos_ids, int32_t layout, void* stream);
 
 /*
  * attn_prefill_blockwise -- o = softmax(scale * Q' K'^T + causal mask) V per
@@ -275,6 +294,26 @@ int attn_decode_sink_window_fp8(const void* q, const void* k_cache, const void* 
                                 const float* k_scale, const float* v_scale,
                                 const float* cos_sin, int64_t n_table_rows,
                                 float softmax_scale, void* stream);
+
+/*
+ * attn_decode_sink_window_ex -- the decode with both choices open: the cache
+ * element type (YRB_BF16, or YRB_FP8_E4M3 as in attn_decode_sink_window_fp8,
+ * with its scales) and the pair layout the keys and the query are rotated
+ * in (YRB_LAYOUT_HALF or YRB_LAYOUT_INTERLEAVED).  Values are not rotated,
+ * so the layout does not change how V or o are read and written.  Strides
+ * and alignment follow the cache type as in the two calls above; scales are
+ * ignored for bf16.
+ */
+int attn_decode_sink_window_ex(const void* q, const void* k_cache, const void* v_cache, void* o,
+                               int32_t cache_dtype, int32_t layout,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                               int64_t n_sink, int64_t window,
+                               const int64_t q_strides[2], const int64_t cache_strides[3],
+                               const int64_t o_strides[2],
+                               const int32_t* cache_len, const int32_t* ring_head,
+                               const float* k_scale, const float* v_scale,
+                               const float* cos_sin, int64_t n_table_rows,
+                               float softmax_scale, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* yrb_status_str(int status);

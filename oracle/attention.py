@@ -249,7 +249,7 @@ def cache_slot(e: int, n_sink: int, window: int, ring_head: int) -> int:
 
 
 def decode_sink_window(q, k_cache, v_cache, theta, softmax_scale, n_sink, window,
-                       cache_len, ring_head=None, heads=None):
+                       cache_len, ring_head=None, heads=None, layout="half"):
     """One new query per sequence against its sink + window cache.
 
     q [B, Hq, D] (un-rotated), k_cache/v_cache [B, Hkv, C, D] (un-rotated
@@ -263,6 +263,9 @@ def decode_sink_window(q, k_cache, v_cache, theta, softmax_scale, n_sink, window
     B, Hq, D = q.shape
     Hkv = k_cache.shape[1]
     heads = range(Hq) if heads is None else heads
+    # pairs (i, i + d/2), or (2i, 2i+1) for layout "interleaved" (tecvarsity
+    # Section 2 pairs the dimensions without fixing which)
+    rotate = _rope.rotate_interleaved if layout == "interleaved" else _rope.rotate_half
     out = np.zeros((B, len(heads), np.asarray(v_cache).shape[3]))
     for b in range(B):
         L = int(cache_len[b])
@@ -275,9 +278,9 @@ def decode_sink_window(q, k_cache, v_cache, theta, softmax_scale, n_sink, window
         cq, sq = _rope.tables(theta, [L - 1])
         for hi, h in enumerate(heads):
             g = kv_head(h, Hq, Hkv)
-            kk = _rope.rotate_half(np.asarray(k_cache[b, g], np.float64)[slots], ck, sk)
+            kk = rotate(np.asarray(k_cache[b, g], np.float64)[slots], ck, sk)
             vv = np.asarray(v_cache[b, g], np.float64)[slots]
-            qq = _rope.rotate_half(q[b, h][None, :], cq, sq)
+            qq = rotate(q[b, h][None, :], cq, sq)
             out[b, hi] = attention_full(qq, kk, vv, softmax_scale, np.array([L - 1]), pos,
                                         all_visible)[0]
     return out

@@ -259,6 +259,21 @@ def test_decode_fp8_validation():
     assert _decode_fp8(o=MISALIGNED) == EALIGN
 
 
+def test_layout_validation():
+    # an unknown layout or cache type is rejected before anything is launched
+    L = api.lib()
+    s = _strides(8 * 128 * 32, 128 * 32, 128)
+    assert L.rope_apply_ex(FAKE, FAKE, 0, 1, 8, 32, 128, s, s, FAKE, 8, 0, None, 2, None) == EINVAL
+    assert L.rope_apply_ex(FAKE, FAKE, 0, 0, 8, 32, 128, s, s, FAKE, 8, 0, None, 1, None) == OK
+    qs, cs, os_ = _strides(512, 128), _strides(4 * 64 * 128, 64 * 128, 128), _strides(512, 128)
+    args = (FAKE, FAKE, FAKE, FAKE)
+    tail = (4, 4, 128, 4, 60, qs, cs, os_, FAKE, None, None, None, FAKE, 64,
+            ctypes.c_float(0.1), None)
+    assert L.attn_decode_sink_window_ex(*args, 0, 2, 2, *tail) == EINVAL     # layout 2
+    assert L.attn_decode_sink_window_ex(*args, 1, 0, 2, *tail) == EUNSUP     # f32 cache
+    assert L.attn_decode_sink_window_ex(*args, 0, 1, 0, *tail) == OK         # B = 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(api, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(api, "_lib", None)

@@ -120,6 +120,27 @@ def test_prefill_overlapping_key_rows(kv_tok_stride):
     assert max_abs(host(o), ref) <= BF16_TOL
 
 
+def test_prefill_interleaved_layout_prerotated():
+    # A model in the interleaved pair layout: Q and K rotated by rope_apply_ex,
+    # then the prefill with cos_sin = NULL, against the oracle rotating
+    # (2i, 2i+1) pairs in fp64.
+    require_gpu()
+    import torch
+    B, S, Hq, Hkv, D = 1, 700, 4, 2, 128
+    rope = W.Rope(W.YARN, D, 1e4, 4.0, 128)
+    tab, th, scale, (qv, kv, vv), (q, k, v) = _setup(B, S, Hq, Hkv, D, "bf16", rope, seed_base=55)
+    say("attn_prefill_blockwise interleaved layout, pre-rotated S=700")
+    qr = api.rope_apply_ex(q, tab, layout=api.LAYOUT_INTERLEAVED)
+    kr = api.rope_apply_ex(k, tab, layout=api.LAYOUT_INTERLEAVED)
+    o = api.attn_prefill_blockwise(qr, kr, v, scale)
+    torch.cuda.synchronize()
+    c, s = R.tables(th, np.arange(S))
+    qi = R.rotate_interleaved(np.asarray(qv, np.float64), c[None, :, None, :], s[None, :, None, :])
+    ki = R.rotate_interleaved(np.asarray(kv, np.float64), c[None, :, None, :], s[None, :, None, :])
+    ref = A.prefill(qi, ki, vv, None, scale)
+    assert max_abs(host(o), ref) <= BF16_TOL
+
+
 def test_prefill_deterministic():
     require_gpu()
     import torch

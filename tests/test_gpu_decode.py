@@ -217,3 +217,37 @@ def test_decode_fp8_nan_code_reaches_output():
     torch.cuda.synchronize()
     got = host(o)
     assert np.isnan(got[0, 1, 5]) and not np.isnan(got[0, 0]).any()
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("G,D", [(1, 128), (4, 64)])
+def test_decode_interleaved_layout(fp8, G, D):
+    # Keys and the query rotated in the interleaved pair layout, bf16 or E4M3
+    # cache, through attn_decode_sink_window_ex; lengths and ring heads as in
+    # the edge cases.
+    require_gpu()
+    import torch
+    n_sink, window = 4, 300
+    C = n_sink + window
+    lens = [0, 1, 5, 150, C, C, C]
+    heads = [0, 0, 0, 7, 0, 123, window - 1]
+    B, Hkv = len(lens), 2
+    rope = W.Rope(W.YARN, D, 1e4, 4.0, 128)
+    if fp8:
+        tab, th, scale, (qv, kv, vv), q, dv = _fp8_case(B, Hkv * G, Hkv, D, n_sink, window, lens,
+                                                        heads, rope, seed=100 + G + D)
+        k, v, ks, vs, lens_t, rh_t = dv["k"], dv["v"], dv["ks"], dv["vs"], dv["lens"], dv["rh"]
+    else:
+        tab, th, scale, (qv, kv, vv), (q, k, v), lens_t, rh_t = _case(
+            B, Hkv * G, Hkv, D, n_sink, window, lens, heads, rope, seed=110 + G + D)
+        ks = vs = None
+    say(f"attn_decode_sink_window_ex interleaved fp8={fp8} G={G} D={D}")
+    o = api.attn_decode_sink_window_ex(q, k, v, lens_t, n_sink, window, tab, scale,
+                                       layout=api.LAYOUT_INTERLEAVED, ring_head=rh_t,
+                                       k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    got = host(o)
+    for b in range(B):
+        ref = A.decode_sink_window(qv[b:b + 1], kv[b:b + 1], vv[b:b + 1], th, scale, n_sink,
+                                   window, [lens[b]], [heads[b]], layout="interleaved")
+        assert max_abs(got[b], ref[0]) <= BF16_TOL, b

@@ -139,3 +139,29 @@ def test_rope_apply_full_size_keys():
     got = host(y[0, rows])
     ref = R.rotate_bshd(kv[:, rows], th, rows)[0]
     assert max_abs(got, ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_rope_apply_interleaved(dtype, D):
+    # Adjacent pairs (x_{2i}, x_{2i+1}) through rope_apply_ex, strided rows
+    # and per-token positions, against the oracle's interleaved rotation.
+    require_gpu()
+    import torch
+    rope = W.Rope(W.YARN, D, 1e4, 4.0, 128)
+    B, S, H = 2, 300, 3
+    say(f"rope_apply_ex interleaved {dtype} D={D}")
+    tab, th, _ = api.rope_tables_build(api.RopeConfig.of(rope), 700)
+    xv, xb = draw((B, S, 2 * H, D), 9, dtype)
+    x = xb[:, :, ::2]                                 # every other head: strided rows
+    pos = np.random.default_rng(3).integers(0, 700, size=(B, S)).astype(np.int32)
+    y = api.rope_apply_ex(x, tab, layout=api.LAYOUT_INTERLEAVED,
+                          pos_ids=torch.from_numpy(pos).cuda())
+    torch.cuda.synchronize()
+    ref = np.empty((B, S, H, D))
+    for b in range(B):
+        c, s = R.tables(th, pos[b])
+        ref[b] = R.rotate_interleaved(np.asarray(xv[b, :, ::2], np.float64), c[:, None, :],
+                                      s[:, None, :])
+    err = max_abs(host(y), ref)
+    assert err <= (BF16_TOL if dtype == "bf16" else F32_TOL), err

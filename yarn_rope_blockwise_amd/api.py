@@ -17,11 +17,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libyrb.so")
 
 PLAIN, PI, NTK, YARN = 0, 1, 2, 3
-BF16, F32 = 0, 1
+BF16, F32, FP8_E4M3 = 0, 1, 2
+LAYOUT_HALF, LAYOUT_INTERLEAVED = 0, 1
 ACC_FIRST, ACC_FINALIZE = 1, 2
 EXPORTS = ("rope_tables_build", "rope_tables_build_factors", "rope_apply", "attn_prefill_blockwise",
            "attn_block_accumulate", "attn_decode_sink_window", "attn_decode_sink_window_fp8",
-           "yrb_status_str")
+           "rope_apply_ex", "attn_decode_sink_window_ex", "yrb_status_str")
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -98,6 +99,11 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_sink_window_fp8.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                                   _i64, _i64, _i64p, _i64p, _i64p, _vp, _vp, _vp,
                                                   _vp, _vp, _i64, ctypes.c_float, _vp]
+        L.rope_apply_ex.argtypes = [_vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64p, _i64p, _vp,
+                                    _i64, _i64, _vp, _i32, _vp]
+        L.attn_decode_sink_window_ex.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i64,
+                                                 _i64, _i64, _i64, _i64p, _i64p, _i64p, _vp, _vp,
+                                                 _vp, _vp, _vp, _i64, ctypes.c_float, _vp]
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -339,6 +345,53 @@ def attn_decode_sink_window_fp8(q, k_codes, v_codes, cache_len, n_sink: int, win
         _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(out), B, Hq, Hkv, D, n_sink, window,
         _arr([q.stride(0), q.stride(1)]),
         _arr([k_codes.stride(0), k_codes.stride(1), k_codes.stride(2)]),
+        _arr([out.stride(0), out.stride(1)]), _ptr(cache_len), _ptr(ring_head), _ptr(k_scale),
+        _ptr(v_scale), _ptr(cos_sin), cos_sin.shape[0], float(softmax_scale), _stream()))
+    return out
+
+
+def rope_apply_ex(x, cos_sin, layout: int = LAYOUT_HALF, pos_offset: int = 0, pos_ids=None,
+                  out=None):
+    """rope_apply with a pair layout: LAYOUT_HALF (i, i+d/2) or LAYOUT_INTERLEAVED (2i, 2i+1)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(x)
+    B, S, H, D = x.shape
+    if pos_ids is not None:
+        pos_ids = pos_ids.to(torch.int32).contiguous()
+    _check("rope_apply_ex", lib().rope_apply_ex(
+        _ptr(x), _ptr(out), _dtype_code(x), B, S, H, D, _arr(_bsh_strides(x)),
+        _arr(_bsh_strides(out)), _ptr(cos_sin), cos_sin.shape[0], pos_offset, _ptr(pos_ids),
+        layout, _stream()))
+    return out
+
+
+def attn_decode_sink_window_ex(q, k_cache, v_cache, cache_len, n_sink: int, window: int, cos_sin,
+                               softmax_scale: float, layout: int = LAYOUT_HALF, ring_head=None,
+                               out=None, k_scale=None, v_scale=None):
+    """The decode with the cache type taken from k_cache (bf16, or uint8 E4M3 codes with
+    optional k_scale / v_scale [B,Hkv]) and the key/query pair layout."""
+    import torch
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    cache_dtype = FP8_E4M3 if k_cache.dtype == torch.uint8 else _dtype_code(k_cache)
+    if out is None:
+        out = torch.empty_like(q)
+    if q.stride(2) != 1 or k_cache.stride(3) != 1 or v_cache.stride(3) != 1 or out.stride(2) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    if tuple(k_cache.stride()) != tuple(v_cache.stride()):
+        raise ValueError("k and v caches must share strides")
+    cache_len = cache_len.to(torch.int32).contiguous()
+    if ring_head is not None:
+        ring_head = ring_head.to(torch.int32).contiguous()
+    if k_scale is not None:
+        k_scale = k_scale.to(torch.float32).contiguous()
+    if v_scale is not None:
+        v_scale = v_scale.to(torch.float32).contiguous()
+    _check("attn_decode_sink_window_ex", lib().attn_decode_sink_window_ex(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), cache_dtype, layout, B, Hq, Hkv, D,
+        n_sink, window, _arr([q.stride(0), q.stride(1)]),
+        _arr([k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)]),
         _arr([out.stride(0), out.stride(1)]), _ptr(cache_len), _ptr(ring_head), _ptr(k_scale),
         _ptr(v_scale), _ptr(cos_sin), cos_sin.shape[0], float(softmax_scale), _stream()))
     return out

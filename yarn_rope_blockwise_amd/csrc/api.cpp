@@ -152,6 +152,15 @@ int rope_tables_build_factors(int32_t head_dim, double base, const double* facto
 int rope_apply(const void* x, void* y, int32_t dtype, int64_t B, int64_t S, int64_t H, int64_t D,
                const int64_t x_strides[3], const int64_t y_strides[3], const float* cos_sin,
                int64_t n_table_rows, int64_t pos_offset, const int32_t* pos_ids, void* stream) {
+  return rope_apply_ex(x, y, dtype, B, S, H, D, x_strides, y_strides, cos_sin, n_table_rows,
+                       pos_offset, pos_ids, YRB_LAYOUT_HALF, stream);
+}
+
+int rope_apply_ex(const void* x, void* y, int32_t dtype, int64_t B, int64_t S, int64_t H,
+                  int64_t D, const int64_t x_strides[3], const int64_t y_strides[3],
+                  const float* cos_sin, int64_t n_table_rows, int64_t pos_offset,
+                  const int32_t* pos_ids, int32_t layout, void* stream) {
+  if (layout != YRB_LAYOUT_HALF && layout != YRB_LAYOUT_INTERLEAVED) return YRB_EINVAL;
   if (!dtype_ok(dtype)) return YRB_EUNSUPPORTED;
   if (!dim_ok(D)) return YRB_EUNSUPPORTED;
   if (B < 0 || S < 0 || H < 0 || n_table_rows < 0 || pos_offset < 0) return YRB_EINVAL;
@@ -177,7 +186,8 @@ int rope_apply(const void* x, void* y, int32_t dtype, int64_t B, int64_t S, int6
   r.n_rows = n_table_rows;
   r.pos_offset = pos_offset;
   r.pos_ids = pos_ids;
-  return hip_status(yrb::launch_rope_apply(dtype, (int)D, r, static_cast<hipStream_t>(stream)));
+  return hip_status(yrb::launch_rope_apply(dtype, (int)D, layout == YRB_LAYOUT_INTERLEAVED, r,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o, int32_t dtype,
@@ -305,7 +315,7 @@ namespace {
 
 // Shared by the bf16 and fp8 decode entry points: validation, then the
 // launch with the cache element type `cache_dtype` (q and o are bf16).
-int decode_common(int cache_dtype, const void* q, const void* k_cache, const void* v_cache, void* o,
+int decode_common(int cache_dtype, bool interleaved, const void* q, const void* k_cache, const void* v_cache, void* o,
                   int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t n_sink, int64_t window,
                   const int64_t q_strides[2], const int64_t cache_strides[3],
                   const int64_t o_strides[2], const int32_t* cache_len, const int32_t* ring_head,
@@ -354,7 +364,8 @@ int decode_common(int cache_dtype, const void* q, const void* k_cache, const voi
   a.ring_head = ring_head;
   a.cos_sin = cos_sin;
   a.softmax_scale = softmax_scale;
-  return hip_status(yrb::launch_decode(cache_dtype, (int)D, a, static_cast<hipStream_t>(stream)));
+  return hip_status(
+      yrb::launch_decode(cache_dtype, (int)D, interleaved, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -367,7 +378,7 @@ int attn_decode_sink_window(const void* q, const void* k_cache, const void* v_ca
                             const float* cos_sin, int64_t n_table_rows, float softmax_scale,
                             void* stream) {
   if (dtype != YRB_BF16) return YRB_EUNSUPPORTED;
-  return decode_common(yrb::kBF16, q, k_cache, v_cache, o, B, Hq, Hkv, D, n_sink, window,
+  return decode_common(yrb::kBF16, false, q, k_cache, v_cache, o, B, Hq, Hkv, D, n_sink, window,
                        q_strides, cache_strides, o_strides, cache_len, ring_head, nullptr,
                        nullptr, cos_sin, n_table_rows, softmax_scale, stream);
 }
@@ -380,9 +391,28 @@ int attn_decode_sink_window_fp8(const void* q, const void* k_cache, const void* 
                                 const float* k_scale, const float* v_scale, const float* cos_sin,
                                 int64_t n_table_rows, float softmax_scale, void* stream) {
   if ((k_scale && !aligned16(k_scale)) || (v_scale && !aligned16(v_scale))) return YRB_EALIGN;
-  return decode_common(yrb::kFP8E4M3, q, k_cache, v_cache, o, B, Hq, Hkv, D, n_sink, window,
+  return decode_common(yrb::kFP8E4M3, false, q, k_cache, v_cache, o, B, Hq, Hkv, D, n_sink, window,
                        q_strides, cache_strides, o_strides, cache_len, ring_head, k_scale, v_scale,
                        cos_sin, n_table_rows, softmax_scale, stream);
+}
+
+int attn_decode_sink_window_ex(const void* q, const void* k_cache, const void* v_cache, void* o,
+                               int32_t cache_dtype, int32_t layout, int64_t B, int64_t Hq,
+                               int64_t Hkv, int64_t D, int64_t n_sink, int64_t window,
+                               const int64_t q_strides[2], const int64_t cache_strides[3],
+                               const int64_t o_strides[2], const int32_t* cache_len,
+                               const int32_t* ring_head, const float* k_scale,
+                               const float* v_scale, const float* cos_sin, int64_t n_table_rows,
+                               float softmax_scale, void* stream) {
+  if (layout != YRB_LAYOUT_HALF && layout != YRB_LAYOUT_INTERLEAVED) return YRB_EINVAL;
+  if (cache_dtype != YRB_BF16 && cache_dtype != YRB_FP8_E4M3) return YRB_EUNSUPPORTED;
+  const bool fp8 = cache_dtype == YRB_FP8_E4M3;
+  if (fp8 && ((k_scale && !aligned16(k_scale)) || (v_scale && !aligned16(v_scale))))
+    return YRB_EALIGN;
+  return decode_common(fp8 ? yrb::kFP8E4M3 : yrb::kBF16, layout == YRB_LAYOUT_INTERLEAVED, q,
+                       k_cache, v_cache, o, B, Hq, Hkv, D, n_sink, window, q_strides,
+                       cache_strides, o_strides, cache_len, ring_head, fp8 ? k_scale : nullptr,
+                       fp8 ? v_scale : nullptr, cos_sin, n_table_rows, softmax_scale, stream);
 }
 
 }  // extern "C"

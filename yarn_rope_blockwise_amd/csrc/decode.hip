@@ -73,7 +73,27 @@ struct KVChunk {
   bool ok[R];
 };
 
-template <int D, int G, bool FP8>
+// The 8 pairs of one lane from its two chunks a, b (8 values each, at
+// elements 8cc and d/2 + 8cc in either layout): half-split, pairs
+// 8cc .. 8cc+7 with a the first elements and b their partners; interleaved
+// (IL), a holds pairs 4cc .. 4cc+3 and b pairs d/4 + 4cc .. +3, each pair
+// two adjacent values.
+template <bool IL>
+__device__ __forceinline__ void pairs_of(const float (&a)[8], const float (&b)[8], float (&x)[8],
+                                         float (&z)[8]) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if constexpr (IL) {
+      x[u] = u < 4 ? a[2 * u] : b[2 * u - 8];
+      z[u] = u < 4 ? a[2 * u + 1] : b[2 * u - 7];
+    } else {   // half-split
+      x[u] = a[u];
+      z[u] = b[u];
+    }
+  }
+}
+
+template <int D, int G, bool FP8, bool IL>
 __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) {
   using CT = CacheType<FP8>;
   using Chunk = typename CT::Chunk;
@@ -125,20 +145,23 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
   float qlo[G][8], qhi[G][8];
   {
     const int qpos = len > 0 ? len - 1 : 0;
-    const f32x4* t = reinterpret_cast<const f32x4*>(a.cos_sin + (int64_t)qpos * D + 16 * cc);
+    // (cos, sin) of the lane's pairs, two per f32x4 (see pairs_of)
+    const float* trow = a.cos_sin + (int64_t)qpos * D;
     float c[8], s[8];
 #pragma unroll
     for (int u2 = 0; u2 < 4; ++u2) {
-      const f32x4 tt = t[u2];
+      const int f = IL ? (u2 < 2 ? 8 * cc + 4 * u2 : D / 2 + 8 * cc + 4 * (u2 - 2)) : 16 * cc + 4 * u2;
+      const f32x4 tt = *reinterpret_cast<const f32x4*>(trow + f);
       c[2 * u2] = tt[0]; s[2 * u2] = tt[1]; c[2 * u2 + 1] = tt[2]; s[2 * u2 + 1] = tt[3];
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + b * a.qs[0] +
                          (int64_t)(hk * G + g) * a.qs[1];
-      float x[8], z[8];
-      unpack8(*reinterpret_cast<const u32x4*>(qp + 8 * cc), x);
-      unpack8(*reinterpret_cast<const u32x4*>(qp + D / 2 + 8 * cc), z);
+      float qa[8], qb[8], x[8], z[8];
+      unpack8(*reinterpret_cast<const u32x4*>(qp + 8 * cc), qa);
+      unpack8(*reinterpret_cast<const u32x4*>(qp + D / 2 + 8 * cc), qb);
+      pairs_of<IL>(qa, qb, x, z);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         qlo[g][u] = x[u] * c[u] - z[u] * s[u];
@@ -205,16 +228,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
     float sc_[G][kRounds];
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
-      const YRB_LDS f32x4* t =
-          reinterpret_cast<const YRB_LDS f32x4*>(tl + (r * KPW + kg) * TROWB + 64 * cc);
-      float c[8], s[8], x[8], z[8];
+      const YRB_LDS char* trow = tl + (r * KPW + kg) * TROWB;
+      float c[8], s[8], ka[8], kb_[8], x[8], z[8];
 #pragma unroll
       for (int u2 = 0; u2 < 4; ++u2) {
-        const f32x4 tt = t[u2];
+        const int off = IL ? (u2 < 2 ? 32 * cc + 16 * u2 : 2 * D + 32 * cc + 16 * (u2 - 2)) : 64 * cc + 16 * u2;
+        const f32x4 tt = *reinterpret_cast<const YRB_LDS f32x4*>(trow + off);
         c[2 * u2] = tt[0]; s[2 * u2] = tt[1]; c[2 * u2 + 1] = tt[2]; s[2 * u2 + 1] = tt[3];
       }
-      CT::unpack(ch.klo[r], x);
-      CT::unpack(ch.khi[r], z);
+      CT::unpack(ch.klo[r], ka);
+      CT::unpack(ch.khi[r], kb_);
+      pairs_of<IL>(ka, kb_, x, z);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float acc = 0.f;
@@ -329,32 +353,41 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
   }
 }
 
-template <int D, int G, bool FP8>
+template <int D, int G, bool FP8, bool IL>
 hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
   const int64_t blocks = a.B * ((a.Hkv + kWaves - 1) / kWaves);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_bf16_kernel<D, G, FP8>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
-                     stream, a);
+  hipLaunchKernelGGL((decode_bf16_kernel<D, G, FP8, IL>), dim3((unsigned)blocks), dim3(kWaves * 64),
+                     0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool IL>
 hipError_t launch_dec_g(const DecodeArgs& a, hipStream_t stream) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_dec<D, 1, FP8>(a, stream);
-    case 2: return launch_dec<D, 2, FP8>(a, stream);
-    case 4: return launch_dec<D, 4, FP8>(a, stream);
-    case 8: return launch_dec<D, 8, FP8>(a, stream);
+    case 1: return launch_dec<D, 1, FP8, IL>(a, stream);
+    case 2: return launch_dec<D, 2, FP8, IL>(a, stream);
+    case 4: return launch_dec<D, 4, FP8, IL>(a, stream);
+    case 8: return launch_dec<D, 8, FP8, IL>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <bool FP8, bool IL>
+hipError_t launch_dec_d(int D, const DecodeArgs& a, hipStream_t stream) {
+  return D == 64 ? launch_dec_g<64, FP8, IL>(a, stream) : launch_dec_g<128, FP8, IL>(a, stream);
+}
+
 }  // namespace
 
-// Cache dtype kBF16 or kFP8E4M3 (query and output are bf16 either way).
-hipError_t launch_decode(int cache_dtype, int D, const DecodeArgs& a, hipStream_t stream) {
-  if (cache_dtype == kBF16) return D == 64 ? launch_dec_g<64, false>(a, stream) : launch_dec_g<128, false>(a, stream);
-  if (cache_dtype == kFP8E4M3) return D == 64 ? launch_dec_g<64, true>(a, stream) : launch_dec_g<128, true>(a, stream);
+// Cache dtype kBF16 or kFP8E4M3 (query and output are bf16 either way);
+// interleaved: keys and query paired (2i, 2i+1) instead of (i, i + d/2).
+hipError_t launch_decode(int cache_dtype, int D, bool interleaved, const DecodeArgs& a,
+                         hipStream_t stream) {
+  if (cache_dtype == kBF16)
+    return interleaved ? launch_dec_d<false, true>(D, a, stream) : launch_dec_d<false, false>(D, a, stream);
+  if (cache_dtype == kFP8E4M3)
+    return interleaved ? launch_dec_d<true, true>(D, a, stream) : launch_dec_d<true, false>(D, a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -23,7 +23,7 @@ struct RopeArgs {
   int64_t pos_offset;
   const int32_t* pos_ids; // [B][S] or null
 };
-hipError_t launch_rope_apply(int dtype, int D, const RopeArgs& a, hipStream_t stream);
+hipError_t launch_rope_apply(int dtype, int D, bool interleaved, const RopeArgs& a, hipStream_t stream);
 
 // One attention launch: prefill (no incoming state, finalize) or one ring
 // step (optional incoming state, state out, optional finalize).
@@ -68,6 +68,7 @@ struct DecodeArgs {
   const float* k_scale;          // fp8 caches: [B][Hkv] dequantisation scales, or null (1)
   const float* v_scale;
 };
-hipError_t launch_decode(int cache_dtype, int D, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode(int cache_dtype, int D, bool interleaved, const DecodeArgs& a,
+                         hipStream_t stream);
 
 }  // namespace yrb

@@ -94,8 +94,12 @@ struct Vec<float> {
 
 // Grid: x = token s, y = groups of 256 (head, chunk) threads of that token,
 // z = batch b (batch_base + blockIdx.z): no index divisions beyond the
-// constant PER_ROW.
-template <typename T, int D>
+// constant PER_ROW.  Thread c of a row moves the chunks at c N and
+// D/2 + c N (coalesced the same way in both layouts).  Half-split, they hold
+// pairs c N .. c N + N-1 (first elements, then partners); interleaved (IL),
+// each chunk holds N/2 whole pairs (2p, 2p+1): pairs c N/2 .. and
+// D/4 + c N/2 ..
+template <typename T, int D, bool IL>
 __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t batch_base) {
   constexpr int N = Vec<T>::N;
   constexpr int PER_ROW = (D / 2) / N;  // threads per (b, s, h) row
@@ -110,27 +114,56 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t bat
   T* yr = reinterpret_cast<T*>(a.y) + b * a.ys[0] + s * a.ys[1] + h * a.ys[2];
   const int i0 = c * N;
   float x[N], z[N], lo[N], hi[N];
-  Vec<T>::load(xr + i0, x);
-  Vec<T>::load(xr + D / 2 + i0, z);
+  if constexpr (IL) {
+    float wa[N], wb[N];
+    Vec<T>::load(xr + i0, wa);
+    Vec<T>::load(xr + D / 2 + i0, wb);
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+      x[j] = wa[2 * j];
+      z[j] = wa[2 * j + 1];
+      x[N / 2 + j] = wb[2 * j];
+      z[N / 2 + j] = wb[2 * j + 1];
+    }
+  } else {
+    Vec<T>::load(xr + i0, x);
+    Vec<T>::load(xr + D / 2 + i0, z);
+  }
   if (pos < 0 || pos >= a.n_rows) {
     const float nan = __builtin_nanf("");
     for (int j = 0; j < N; ++j) lo[j] = hi[j] = nan;
   } else {
-    const f32x4* cs = reinterpret_cast<const f32x4*>(a.cos_sin + (pos * (D / 2) + i0) * 2);
+    // (cos, sin) of this thread's pairs: i0 .. i0+N-1 (half-split), or
+    // i0/2 .. and D/4 + i0/2 .. (interleaved), two pairs per f32x4
+    const float* row = a.cos_sin + pos * (D / 2) * 2;
 #pragma unroll
     for (int j = 0; j < N / 2; ++j) {
-      f32x4 t = cs[j];  // (cos, sin) of pairs i0+2j, i0+2j+1
+      const int pr = IL ? (2 * j < N / 2 ? i0 / 2 + 2 * j : D / 4 + i0 / 2 + 2 * j - N / 2) : i0 + 2 * j;
+      f32x4 t = *reinterpret_cast<const f32x4*>(row + 2 * pr);  // pairs pr, pr+1
       lo[2 * j] = x[2 * j] * t[0] - z[2 * j] * t[1];
       hi[2 * j] = x[2 * j] * t[1] + z[2 * j] * t[0];
       lo[2 * j + 1] = x[2 * j + 1] * t[2] - z[2 * j + 1] * t[3];
       hi[2 * j + 1] = x[2 * j + 1] * t[3] + z[2 * j + 1] * t[2];
     }
   }
-  Vec<T>::store(yr + i0, lo);
-  Vec<T>::store(yr + D / 2 + i0, hi);
+  if constexpr (IL) {
+    float wa[N], wb[N];
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+      wa[2 * j] = lo[j];
+      wa[2 * j + 1] = hi[j];
+      wb[2 * j] = lo[N / 2 + j];
+      wb[2 * j + 1] = hi[N / 2 + j];
+    }
+    Vec<T>::store(yr + i0, wa);
+    Vec<T>::store(yr + D / 2 + i0, wb);
+  } else {
+    Vec<T>::store(yr + i0, lo);
+    Vec<T>::store(yr + D / 2 + i0, hi);
+  }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool IL>
 static hipError_t launch_rope_t(const RopeArgs& a, hipStream_t stream) {
   constexpr int PER_ROW = (D / 2) / Vec<T>::N;
   if (a.B == 0 || a.S == 0 || a.H == 0) return hipSuccess;
@@ -140,17 +173,23 @@ static hipError_t launch_rope_t(const RopeArgs& a, hipStream_t stream) {
   constexpr int64_t kMaxZ = 65535;   // grid z limit: batches go in slices of it
   for (int64_t b0 = 0; b0 < a.B; b0 += kMaxZ) {
     const unsigned nb = (unsigned)std::min<int64_t>(kMaxZ, a.B - b0);
-    hipLaunchKernelGGL((rope_apply_kernel<T, D>), dim3((unsigned)a.S, groups, nb), dim3(256), 0, stream, a, b0);
+    hipLaunchKernelGGL((rope_apply_kernel<T, D, IL>), dim3((unsigned)a.S, groups, nb), dim3(256), 0, stream, a,
+                       b0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-hipError_t launch_rope_apply(int dtype, int D, const RopeArgs& a, hipStream_t stream) {
-  if (dtype == kBF16) return D == 64 ? launch_rope_t<__bf16, 64>(a, stream)
-                                     : launch_rope_t<__bf16, 128>(a, stream);
-  return D == 64 ? launch_rope_t<float, 64>(a, stream) : launch_rope_t<float, 128>(a, stream);
+template <bool IL>
+static hipError_t launch_rope_l(int dtype, int D, const RopeArgs& a, hipStream_t stream) {
+  if (dtype == kBF16) return D == 64 ? launch_rope_t<__bf16, 64, IL>(a, stream)
+                                     : launch_rope_t<__bf16, 128, IL>(a, stream);
+  return D == 64 ? launch_rope_t<float, 64, IL>(a, stream) : launch_rope_t<float, 128, IL>(a, stream);
+}
+
+hipError_t launch_rope_apply(int dtype, int D, bool interleaved, const RopeArgs& a, hipStream_t stream) {
+  return interleaved ? launch_rope_l<true>(dtype, D, a, stream) : launch_rope_l<false>(dtype, D, a, stream);
 }
 
 }  // namespace yrb
