@@ -13,11 +13,11 @@ A. ``attention_full`` materialises one query row's logits over all visible
    memory; each row's softmax is whole.
 B. ``attention_online`` walks key blocks in any given order, keeping a
    running max m, running sum l and an unnormalised accumulator per row, and
-   divides at the end.  The pages name this update ("online softmax (same as
-   FlashAttention)", 14cs17 "Ring Attention"; "accumulate its block's
-   contribution as blocks rotate", jovanaeducation guide "Ring attention")
-   without printing it; this is the textbook form (Milakov & Gimelshein
-   2018).
+   divides at the end.  The pages name this update without printing it
+   (14cs17 "Ring Attention" ties it to FlashAttention's online softmax; the
+   jovanaeducation guide, "Ring attention", has each device add in the
+   share of every block that passes it); this is the textbook form (Milakov
+   & Gimelshein 2018).
 
 Masks:
 * causal: key position <= query position (tecvarsity FAQ 2 states the
@@ -146,14 +146,18 @@ def kv_head(h: int, n_q_heads: int, n_kv_heads: int) -> int:
 
 
 def prefill(q, k, v, theta, softmax_scale, causal=True, rows=None, heads=None,
-            batches=None, q_offset: int = 0, k_offset: int = 0):
+            batches=None, q_offset: int = 0, k_offset: int = 0, n_sink: int = 0,
+            window: int = 0):
     """Rotate Q and K (fp64) and run form A per (b, h).
 
     q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D].  Query token s sits at position
     q_offset + s, key token j at k_offset + j.  ``theta`` is None when Q, K
     are already rotated.  ``rows`` restricts the query rows computed (the
-    result then has len(rows) rows).  Returns o [B', len(rows), H', D] over
-    the selected batches/heads.
+    result then has len(rows) rows).  ``window`` > 0 applies the sink+window
+    mask (sink_window_visible; causal implied) in place of ``causal``: the
+    prefill counterpart of the cache of 14cs17 "Sliding Window + Attention
+    Sinks".  Returns o [B', len(rows), H', D]
+    over the selected batches/heads.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -166,6 +170,8 @@ def prefill(q, k, v, theta, softmax_scale, causal=True, rows=None, heads=None,
     q_pos = q_offset + rows
     k_pos = k_offset + np.arange(Sk)
     vis = causal_visible if causal else all_visible
+    if window > 0:
+        vis = sink_window_visible(n_sink, window)
     if theta is not None:
         cq, sq = _rope.tables(theta, q_pos)
         ck, sk = _rope.tables(theta, k_pos)

@@ -329,3 +329,62 @@ def test_e4m3_decode_closed_forms():
     assert np.isnan(d([0x7F])[0]) and np.isnan(d([0xFF])[0])
     pos = d(np.arange(0x7F, dtype=np.uint8))
     assert np.all(np.diff(pos) > 0)              # codes 0 .. 0x7E increase strictly
+
+
+# --- sink+window mask on prefill --------------------------------------------
+
+def _sink_window_mask_loops(S, n_sink, window):
+    # The rule written out per (query t, key n) from 14cs17 "Sliding Window +
+    # Attention Sinks": the first n_sink tokens plus the last `window` ones up
+    # to t.
+    m = np.zeros((S, S), dtype=bool)
+    for t in range(S):
+        for n in range(S):
+            m[t, n] = n <= t and (n < n_sink or n >= t - window + 1)
+    return m
+
+
+@pytest.mark.parametrize("n_sink,window", [(0, 1), (4, 1), (4, 20), (0, 33), (10, 7), (90, 3)])
+def test_sink_window_prefill_matches_sdpa_bool_mask(n_sink, window):
+    S, H, D = 90, 2, 32
+    q, k, v = _rand((1, S, H, D), 81), _rand((1, S, H, D), 82), _rand((1, S, H, D), 83)
+    th = R.inv_freq(R.YARN, D, 1e4, 4.0, 16)
+    o = A.prefill(q, k, v, th, 0.2, n_sink=n_sink, window=window)[0]
+    c, s_ = R.tables(th, np.arange(S))
+    mask = torch.from_numpy(_sink_window_mask_loops(S, n_sink, window))
+    for h in range(H):
+        qr = torch.from_numpy(R.rotate_half(q[0, :, h], c, s_))
+        kr = torch.from_numpy(R.rotate_half(k[0, :, h], c, s_))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qr[None], kr[None], torch.from_numpy(v[0, :, h])[None], attn_mask=mask[None],
+            scale=0.2)[0].numpy()
+        np.testing.assert_allclose(o[:, h], ref, atol=1e-12)
+
+
+def test_sink_window_prefill_closed_forms():
+    S, H, D = 70, 1, 64
+    q, k, v = _rand((1, S, H, D), 84), _rand((1, S, H, D), 85), _rand((1, S, H, D), 86)
+    th = R.inv_freq(R.PLAIN, D, 1e4, 1.0)
+    # window 1, no sinks: each row sees only itself
+    o = A.prefill(q, k, v, th, 0.3, n_sink=0, window=1)
+    np.testing.assert_array_equal(o, v)
+    # a window of S or more is the causal mask
+    o = A.prefill(q, k, v, th, 0.3, n_sink=3, window=S)
+    np.testing.assert_allclose(o, A.prefill(q, k, v, th, 0.3), atol=1e-14)
+    # zero queries: mean of the visible values
+    o = A.prefill(np.zeros_like(q), k, v, None, 0.3, n_sink=2, window=5)[0, :, 0]
+    for t in (0, 3, 10, 69):
+        vis = sorted(set(range(min(2, t + 1))) | set(range(max(0, t - 4), t + 1)))
+        np.testing.assert_allclose(o[t], v[0, vis, 0].mean(axis=0), atol=1e-14)
+
+
+def test_planted_window_off_by_one_fails_pin(monkeypatch):
+    # A window that reaches one key too far back must fail the mask pin.
+    def wide(n_sink, window):
+        def f(q_pos, k_pos):
+            t, n = q_pos[:, None], k_pos[None, :]
+            return (n <= t) & ((n < n_sink) | (n >= t - window))
+        return f
+    monkeypatch.setattr(A, "sink_window_visible", wide)
+    with pytest.raises(AssertionError):
+        test_sink_window_prefill_matches_sdpa_bool_mask(4, 20)
