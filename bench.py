@@ -152,6 +152,45 @@ def run_prefill(steps: int, warmup: int):
                 k_bytes=2 * k.numel() * 2 + S * D * 4)
 
 
+def sink_window_pairs(seq: int, n_sink: int, window: int) -> int:
+    """Visible (query, key) pairs per head under the sink+window mask."""
+    t = np.arange(seq, dtype=np.int64)
+    return int(np.sum(np.minimum(t + 1, window) + np.clip(t - window + 1, 0, n_sink)))
+
+
+def run_sink_window_prefill(steps: int, warmup: int, n_sink: int = 4, window: int = 4096):
+    """The 16k prefill's attention under 4 sinks + a 4096-token window
+    (attn_prefill_sink_window), back-to-back launches, K rotated beforehand."""
+    import torch
+    from yarn_rope_blockwise_amd import api
+    from yarn_rope_blockwise_amd import workloads as W
+    w = W.LLAMA_16K
+    B, S, H, D = w.batch, w.seq, w.n_q_heads, w.head_dim
+    q = _upload((B, S, H, D), 0)
+    k = _upload((B, S, w.n_kv_heads, D), 1)
+    v = _upload((B, S, w.n_kv_heads, D), 2)
+    tab, _, af = api.rope_tables_build(api.RopeConfig.of(w.rope), S)
+    k_rot = api.rope_apply(k, tab)
+    out = torch.empty_like(q)
+    scale = af / np.sqrt(D)
+
+    def call():
+        api.attn_prefill_sink_window(q, k_rot, v, scale, n_sink, window, cos_sin=tab, out=out)
+
+    for _ in range(warmup):
+        call()
+    t0, t1 = _events(2)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    flops = 4.0 * D * H * B * sink_window_pairs(S, n_sink, window)
+    return dict(ms=ms, flops=flops, n_sink=n_sink, window=window)
+
+
 def run_decode(steps: int, warmup: int):
     import torch
     from yarn_rope_blockwise_amd import api, synth
@@ -392,7 +431,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip decode and ring share")
     ap.add_argument("--workload", default="all",
-                    choices=["all", "prefill", "decode", "decode_fp8", "ring", "copy"],
+                    choices=["all", "prefill", "decode", "decode_fp8", "sink_window", "ring",
+                             "copy"],
                     help="run one workload alone (for profiling); the JSON line needs 'all'")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -409,6 +449,7 @@ def main():
         only = {"prefill": lambda: run_prefill(args.steps, args.warmup),
                 "decode": lambda: run_decode(args.steps, max(3 * args.warmup, 10)),
                 "decode_fp8": lambda: run_decode_fp8(args.steps, max(3 * args.warmup, 10)),
+                "sink_window": lambda: run_sink_window_prefill(args.steps, args.warmup),
                 "ring": lambda: run_ring(args.steps, 2),
                 "copy": lambda: run_copy(args.steps)}[args.workload]()
         only.pop("per_call_ms", None)
@@ -480,6 +521,13 @@ def main():
         line["factor_tables"] = {"workload": "rope_tables_build_factors 262144 rows x 64 pairs",
                                  "ms": round(ft["ms"], 4),
                                  "GB/s": round(ft["bytes"] / (ft["ms"] * 1e-3) / 1e9, 1)}
+        sw = run_sink_window_prefill(max(args.steps, 10), args.warmup)
+        line["sink_window_prefill"] = {
+            "workload": "llama7b_prefill_16k_yarn4 attention, 4 sinks + 4096 window",
+            "ms": round(sw["ms"], 4), "flops_per_launch": sw["flops"],
+            "TFLOP/s": round(sw["flops"] / (sw["ms"] * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(sw["flops"] / (sw["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"sink+window prefill done: {sw['ms']:.3f} ms")
         log("ring share: uploading blocks and timing")
         ring = run_ring(max(2, args.steps // 5), 2)
         log(f"ring share done: {ring['ms']:.3f} ms")

@@ -2,10 +2,11 @@
  * yrb.h -- C ABI of libyrb.so: RoPE under a context-extension rescale, fused
  * into exact blockwise causal attention, for AMD Instinct MI355X (gfx950).
  *
- * Five calls make up the path:
+ * The calls of the path:
  *   rope_tables_build        frequencies theta'_i and fp32 cos/sin tables
  *   rope_apply               rotate half-split pairs of Q or K
  *   attn_prefill_blockwise   causal softmax attention with RoPE on load
+ *   attn_prefill_sink_window the same under the sink+window mask, skipping tiles
  *   attn_block_accumulate    fold one external key/value block into a
  *                            query block's online-softmax state (one ring step)
  *   attn_decode_sink_window  one query per sequence over a sink + sliding
@@ -15,7 +16,7 @@
  *  - Every device buffer is owned by the caller.  The library allocates no
  *    memory, never synchronises and calls are thread-safe.  Its one piece of
  *    mutable state is a static device array of 64 work-claim counters
- *    (4 KiB per GPU) that attn_prefill_blockwise and attn_block_accumulate
+ *    (4 KiB per GPU) that the two prefill calls and attn_block_accumulate
  *    use to balance the last 30 % of their grid across the XCDs: each
  *    launch takes the next counter in turn and leaves it at zero.  Two
  *    launches on one GPU that run at the same time with the same counter
@@ -201,6 +202,28 @@ int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o,
                            int64_t D, const int64_t strides[4][3],
                            const float* cos_sin, int64_t n_table_rows,
                            float softmax_scale, int32_t causal, float* lse, void* stream);
+
+/*
+ * attn_prefill_sink_window -- attn_prefill_blockwise under the attention-sink
+ * plus sliding-window mask, the prefill counterpart of the decode cache
+ * ([C] "Sliding Window + Attention Sinks": the first s tokens and the last w
+ * tokens; [J] "Attention sinks").  Key position n is visible to query
+ * position t iff n <= t and (n < n_sink or n > t - window).  Key tiles that
+ * no row of a query tile can see (between the sinks and the window) are
+ * skipped, not masked, so the work per query tile is bounded by
+ * n_sink + window + the tile, not by t.
+ *
+ * Arguments as attn_prefill_blockwise, causal implied, plus
+ *   n_sink         >= 0; values above S act as S (every key a sink).
+ *   window         >= 1; values above S act as S (plain causal).
+ * dtype must be YRB_BF16 (YRB_EUNSUPPORTED otherwise); S < 2^30.
+ */
+int attn_prefill_sink_window(const void* q, const void* k, const void* v, void* o,
+                             int32_t dtype, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                             int64_t D, const int64_t strides[4][3],
+                             const float* cos_sin, int64_t n_table_rows,
+                             float softmax_scale, int64_t n_sink, int64_t window,
+                             float* lse, void* stream);
 
 /*
  * attn_block_accumulate -- one ring-attention step on one device: fold the

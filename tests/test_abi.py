@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_declares_the_five_calls():
     names = declared_functions()
-    for n in ("rope_tables_build", "rope_tables_build_factors", "rope_apply", "attn_prefill_blockwise",
+    for n in ("rope_tables_build", "rope_tables_build_factors", "rope_apply", "attn_prefill_blockwise", "attn_prefill_sink_window",
               "attn_block_accumulate", "attn_decode_sink_window", "yrb_status_str"):
         assert n in names
 
@@ -178,6 +178,35 @@ def test_prefill_validation():
     assert _prefill(lse=MISALIGNED) == EALIGN
     assert _prefill(S=0) == OK
     assert _prefill(B=0) == OK
+
+
+def _prefill_sw(**over):
+    L = api.lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=0, B=1, S=64, Hq=4, Hkv=2, D=128,
+             strides=_strides(*([64 * 4 * 128, 4 * 128, 128] * 4)), cs=FAKE, rows=64,
+             scale=0.1, sink=4, win=32, lse=None)
+    a.update(over)
+    return L.attn_prefill_sink_window(a["q"], a["k"], a["v"], a["o"], a["dtype"], a["B"], a["S"],
+                                      a["Hq"], a["Hkv"], a["D"], a["strides"], a["cs"], a["rows"],
+                                      ctypes.c_float(a["scale"]), a["sink"], a["win"], a["lse"],
+                                      None)
+
+
+def test_prefill_sink_window_validation():
+    # Every call fails before a launch (or has nothing to do).
+    assert _prefill_sw(dtype=1) == EUNSUP      # bf16 only
+    assert _prefill_sw(sink=-1) == EINVAL
+    assert _prefill_sw(win=0) == EINVAL
+    assert _prefill_sw(win=-5) == EINVAL
+    assert _prefill_sw(S=1 << 30, rows=1 << 30) == EINVAL
+    assert _prefill_sw(Hq=3) == EINVAL
+    assert _prefill_sw(D=32) == EUNSUP
+    assert _prefill_sw(scale=0.0) == EINVAL
+    assert _prefill_sw(rows=63) == EINVAL
+    assert _prefill_sw(q=None) == EINVAL
+    assert _prefill_sw(o=MISALIGNED) == EALIGN
+    assert _prefill_sw(S=0) == OK
+    assert _prefill_sw(B=0, sink=1 << 40, win=1 << 40) == OK
 
 
 def _accum(**over):

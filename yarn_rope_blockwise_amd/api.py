@@ -21,6 +21,7 @@ BF16, F32, FP8_E4M3 = 0, 1, 2
 LAYOUT_HALF, LAYOUT_INTERLEAVED = 0, 1
 ACC_FIRST, ACC_FINALIZE = 1, 2
 EXPORTS = ("rope_tables_build", "rope_tables_build_factors", "rope_apply", "attn_prefill_blockwise",
+           "attn_prefill_sink_window",
            "attn_block_accumulate", "attn_decode_sink_window", "attn_decode_sink_window_fp8",
            "rope_apply_ex", "attn_decode_sink_window_ex", "yrb_status_str")
 
@@ -90,6 +91,9 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_blockwise.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64,
                                              _i64, _i64p, _vp, _i64, ctypes.c_float, _i32, _vp,
                                              _vp]
+        L.attn_prefill_sink_window.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64,
+                                               _i64, _i64p, _vp, _i64, ctypes.c_float, _i64, _i64,
+                                               _vp, _vp]
         L.attn_block_accumulate.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64,
                                             _i64, _i64p, _i64, _i64, _vp, _i64, ctypes.c_float,
                                             _i32, _vp, _vp, _vp, _i32, _vp, _i64p, _vp]
@@ -247,6 +251,24 @@ def attn_prefill_blockwise(q, k, v, softmax_scale: float, cos_sin=None, causal: 
     _check("attn_prefill_blockwise", lib().attn_prefill_blockwise(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), B, S, Hq, Hkv, D, strides,
         _ptr(cos_sin), n_rows, float(softmax_scale), int(bool(causal)), _ptr(lse), _stream()))
+    return out
+
+
+def attn_prefill_sink_window(q, k, v, softmax_scale: float, n_sink: int, window: int,
+                             cos_sin=None, out=None, lse=None):
+    """attn_prefill_blockwise under the sink+window mask: key n is visible to
+    query t iff n <= t and (n < n_sink or n > t - window); bf16 only."""
+    import torch
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    strides = _arr(_bsh_strides(q) + _bsh_strides(k) + _bsh_strides(v) + _bsh_strides(out))
+    n_rows = 0 if cos_sin is None else cos_sin.shape[0]
+    _check("attn_prefill_sink_window", lib().attn_prefill_sink_window(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), B, S, Hq, Hkv, D, strides,
+        _ptr(cos_sin), n_rows, float(softmax_scale), int(n_sink), int(window), _ptr(lse),
+        _stream()))
     return out
 
 

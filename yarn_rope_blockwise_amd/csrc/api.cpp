@@ -5,6 +5,7 @@
 // before the first launch, so an error return means nothing was queued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -190,11 +191,14 @@ int rope_apply_ex(const void* x, void* y, int32_t dtype, int64_t B, int64_t S, i
                                            static_cast<hipStream_t>(stream)));
 }
 
-int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o, int32_t dtype,
-                           int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
-                           const int64_t strides[4][3], const float* cos_sin,
-                           int64_t n_table_rows, float softmax_scale, int32_t causal, float* lse,
-                           void* stream) {
+namespace {
+
+// Validation and launch shared by the prefill entry points; window > 0
+// turns on the sink+window mask (bf16 pipelined kernel).
+int prefill_common(const void* q, const void* k, const void* v, void* o, int32_t dtype, int64_t B, int64_t S,
+                   int64_t Hq, int64_t Hkv, int64_t D, const int64_t strides[4][3], const float* cos_sin,
+                   int64_t n_table_rows, float softmax_scale, int32_t causal, int64_t n_sink, int64_t window,
+                   float* lse, void* stream) {
   if (!dtype_ok(dtype)) return YRB_EUNSUPPORTED;
   if (!dim_ok(D)) return YRB_EUNSUPPORTED;
   if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return YRB_EINVAL;
@@ -240,7 +244,37 @@ int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o,
   a.load_state = 0;
   a.store_state = 0;
   a.finalize = 1;
+  if (window > 0) {
+    a.n_sink = (int)n_sink;
+    a.window = (int)window;
+    return hip_status(yrb::launch_attention_bf16_pp((int)D, a, s));
+  }
   return hip_status(yrb::launch_attention(dtype, (int)D, a, s));
+}
+
+}  // namespace
+
+int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                           int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                           const int64_t strides[4][3], const float* cos_sin,
+                           int64_t n_table_rows, float softmax_scale, int32_t causal, float* lse,
+                           void* stream) {
+  return prefill_common(q, k, v, o, dtype, B, S, Hq, Hkv, D, strides, cos_sin, n_table_rows, softmax_scale,
+                        causal, 0, 0, lse, stream);
+}
+
+int attn_prefill_sink_window(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                             int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                             const int64_t strides[4][3], const float* cos_sin, int64_t n_table_rows,
+                             float softmax_scale, int64_t n_sink, int64_t window, float* lse,
+                             void* stream) {
+  if (dtype != YRB_BF16) return YRB_EUNSUPPORTED;
+  if (n_sink < 0 || window < 1) return YRB_EINVAL;
+  if (S >= (int64_t(1) << 30)) return YRB_EINVAL;
+  // A window of S or more reaches every earlier key: plain causal.  Sinks
+  // past S are all the keys there are.
+  return prefill_common(q, k, v, o, dtype, B, S, Hq, Hkv, D, strides, cos_sin, n_table_rows, softmax_scale,
+                        1, std::min(n_sink, S), std::min(window, std::max<int64_t>(S, 1)), lse, stream);
 }
 
 int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk, int32_t dtype,

@@ -150,22 +150,36 @@ __device__ __forceinline__ void offsets_from(const WaveState<D, 2>& st, Offsets&
   }
 }
 
-// Per lane, for masking: the last key index (less 4(lane/32), the lane's
-// row offset inside a quarter) inside the keys and, for each query tile,
-// visible to the lane's query row under the causal mask.
+// Per lane, for masking, all less 4(lane/32), the lane's row offset inside
+// a quarter: the last key index inside the keys; for each query tile, the
+// last key index visible to the lane's query row under the causal mask; the
+// end of the sink keys and the window length (both unused without a
+// window).
 struct MaskInfo {
   int key_last;
   int q_last[2];
+  int sink_end;
+  int window;
   bool causal;
 };
 
-// Causal / ragged mask of the quarter whose first key index is kbase, for
-// query tile X: lane element j holds key row 8(j/4) + (j%4) of the quarter
-// past 4(lane/32); keys past the lane's last visible one get -inf, so P = 0.
+// Mask of the quarter whose first key index is kbase, for query tile X:
+// lane element j holds key row 8(j/4) + (j%4) of the quarter past
+// 4(lane/32).  A key stays if it is inside the keys, not after the row
+// (causal), and either a sink or inside the row's window; the others get
+// -inf, so P = 0.
+template <bool WIN>
 __device__ __forceinline__ void mask_scores(f32x16& s, const MaskInfo& mi, int X, int kbase) {
-  const int lim = (mi.causal ? min(mi.key_last, mi.q_last[X]) : mi.key_last) - kbase;
+  const int hi = (mi.causal ? min(mi.key_last, mi.q_last[X]) : mi.key_last) - kbase;
+  const int lo = mi.q_last[X] - mi.window - kbase;   // window: keys after it
+  const int se = mi.sink_end - kbase;                 // sinks: keys before it
 #pragma unroll
-  for (int j = 0; j < 16; ++j) s[j] = (8 * (j >> 2) + (j & 3) <= lim) ? s[j] : -INFINITY;
+  for (int j = 0; j < 16; ++j) {
+    const int e = 8 * (j >> 2) + (j & 3);
+    bool keep = e <= hi;
+    if constexpr (WIN) keep = keep && (e < se || e > lo);
+    s[j] = keep ? s[j] : -INFINITY;
+  }
 }
 
 // Rare case, at the boundary after the last product into O of tile QT under
@@ -177,7 +191,9 @@ __device__ __forceinline__ void settle_rows(const f32x16& s, WaveState<D, 2>& st
                                             bf16x8 (&pf)[2], float t_max) {
   const float mu_old = st.m_use[QT];
   const float mu_new = grow ? t_max : mu_old;
-  const float shift = mu_new - of.base[QT];                          // 0 where kept
+  // 0 where kept; 0 too for a row still empty (every score so far -inf),
+  // whose P must come out 0, not exp2(-inf + inf)
+  const float shift = mu_new == -INFINITY ? 0.f : mu_new - of.base[QT];
   const float alpha = grow ? fast_exp2(mu_old - mu_new) : 1.0f;      // 0 from an empty row
   float acc = of.l_prev[QT] * alpha;
 #pragma unroll
@@ -211,7 +227,7 @@ __device__ __forceinline__ void settle_rows(const f32x16& s, WaveState<D, 2>& st
 // index kbase) when they come from a masked tile.  With EXACT the half step
 // tracked the exact row max and `grow` is final; without, `grow` is the sum
 // test's candidate and the exact max of the quarter is taken here.
-template <int D, int QT, bool EXACT>
+template <int D, int QT, bool EXACT, bool WIN>
 __device__ __forceinline__ void settle(const f32x16& s, WaveState<D, 2>& st, Offsets& of, bool grow, bool need,
                                        bf16x8 (&pf)[2], bool mask_next, f32x16& s_next, const MaskInfo& mi,
                                        int X_next, int kbase) {
@@ -229,7 +245,7 @@ __device__ __forceinline__ void settle(const f32x16& s, WaveState<D, 2>& st, Off
       if (__builtin_amdgcn_ballot_w64(g) != 0) settle_rows<D, QT>(s, st, of, g, pf, t_max);
     }
   }
-  if (mask_next) mask_scores(s_next, mi, X_next, kbase);
+  if (mask_next) mask_scores<WIN>(s_next, mi, X_next, kbase);
 }
 
 // Pin a value to the current issue step: an empty volatile asm that reads
@@ -589,7 +605,7 @@ __device__ __forceinline__ void table_from_lds(const YRB_LDS char* region, int l
 // EXACT: track the exact running max (calls that store the state, whose m
 // is that max); without it the grow test is the sum test and the output and
 // log-sum-exp use the reference in use, which gives the same values.
-template <int D, bool EXACT>
+template <int D, bool EXACT, bool WIN>
 __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs a, int64_t n_qtiles, int claim_from,
                                                                          unsigned claim_slot) {
   constexpr int NW = kPPWaves, BN = kPPBN, QW = 64, BM = NW * QW;
@@ -629,9 +645,30 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   const int q_last_wg = q_offset + min(Sq, (qtile + 1) * BM) - 1;
   int n_keys = Sk;
   if (a.causal) n_keys = max(0, min(Sk, q_last_wg - k_offset + 1));
-  const int n_tiles = (n_keys + BN - 1) / BN;
-  int n_full = min(n_tiles, Sk / BN);
+  const int n_key_tiles = (n_keys + BN - 1) / BN;
+  int n_full = min(n_key_tiles, Sk / BN);
   if (a.causal) n_full = min(n_full, max(0, q_first_wg - k_offset + 1) / BN);
+  // With a window the workgroup needs the sink tiles [0, n_sink_t) and the
+  // window tiles [tw0, n_key_tiles): the pipeline walks them in that order,
+  // its tile t being key tile t below n_sink_t and t + gap from there on.
+  // A key tile needs the mask unless it is below n_full and wholly among
+  // the sinks (its last key before sink_end) or wholly inside the window of
+  // the workgroup's last row (its first key after w_lo).  Without a window
+  // sink_end = 0 and w_lo = -1, so only n_full decides.
+  int n_sink_t = 0, gap = 0, sink_end = 0, w_lo = -1;
+  if constexpr (WIN) {
+    sink_end = (int)max((int64_t)0, min((int64_t)a.n_sink - k_offset, (int64_t)n_key_tiles * BN));
+    n_sink_t = (sink_end + BN - 1) / BN;
+    const int tw0 = min(n_key_tiles, max(0, q_first_wg - k_offset - a.window + 1) / BN);
+    gap = max(0, tw0 - n_sink_t);
+    w_lo = max(-1, q_last_wg - k_offset - a.window);
+    n_sink_t = __builtin_amdgcn_readfirstlane(n_sink_t);
+    gap = __builtin_amdgcn_readfirstlane(gap);
+    sink_end = __builtin_amdgcn_readfirstlane(sink_end);
+    w_lo = __builtin_amdgcn_readfirstlane(w_lo);
+  }
+  const int n_tiles = n_key_tiles - gap;   // pipeline tiles
+  auto key_tile = [&](int t) YRB_INLINE { return t < n_sink_t ? t : t + gap; };
   const bool wave_live = q0w < Sq;
 
   const __bf16* kbase = reinterpret_cast<const __bf16*>(a.k) + b * a.ks[0] + hk * a.ks[2];
@@ -651,13 +688,14 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   tile_offsets<D, BN, NW, true>(vstride, wave, lane, !fast_dma, voff);
   const __bf16* const ph_k = fast_dma ? kbase_s : reinterpret_cast<const __bf16*>(g_dma_dummy);
   const __bf16* const ph_v = fast_dma ? vbase_s : reinterpret_cast<const __bf16*>(g_dma_dummy);
-  auto issue = [&](int t) YRB_INLINE {
-    if (fast_dma && (t + 1) * BN <= Sk) {
-      load_tile_rows<D, BN, NW>(kbuf(t), kbase_s + (int64_t)t * BN * kstride, koff, wave);
-      load_tile_rows<D, BN, NW>(vbuf(t), vbase_s + (int64_t)t * BN * vstride, voff, wave);
+  auto issue = [&](int t) YRB_INLINE {   // pipeline tile t into buffer t % kPPBufs
+    const int kt = key_tile(t);
+    if (fast_dma && (kt + 1) * BN <= Sk) {
+      load_tile_rows<D, BN, NW>(kbuf(t), kbase_s + (int64_t)kt * BN * kstride, koff, wave);
+      load_tile_rows<D, BN, NW>(vbuf(t), vbase_s + (int64_t)kt * BN * vstride, voff, wave);
     } else {   // the ragged last tile: rows past the end read the last row
-      load_tile<D, BN, NW, false>(kbuf(t), kbase, kstride, t * BN, Sk, wave, lane);
-      load_tile<D, BN, NW, true>(vbuf(t), vbase, vstride, t * BN, Sk, wave, lane);
+      load_tile<D, BN, NW, false>(kbuf(t), kbase, kstride, kt * BN, Sk, wave, lane);
+      load_tile<D, BN, NW, true>(vbuf(t), vbase, vstride, kt * BN, Sk, wave, lane);
     }
   };
   // Q rotated and pre-multiplied by softmax_scale * log2(e): scores come out
@@ -716,12 +754,15 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   // The pipeline's DMA: every tile it asks for is one group of DMA
   // instructions (a placeholder when the tile is not a full one inside the
   // keys, plus the clamped load after the half step when it is ragged).
-  // Tiles [0, n_fast) are full tiles inside the keys the workgroup needs and
-  // go by the fast path; the pipeline walks their first rows tile by tile.
-  const int n_fast = fast_dma ? min(n_tiles, Sk / BN) : 0;
+  // Pipeline tiles [0, n_fast) are full key tiles inside the keys the
+  // workgroup needs and go by the fast path; the pipeline walks their first
+  // rows tile by tile, jumping the gap after the sink tiles.
+  const int n_full_k = min(n_key_tiles, Sk / BN);
+  const int n_fast = !fast_dma ? 0 : n_full_k <= n_sink_t ? n_full_k : max(n_sink_t, n_full_k - gap);
   const int64_t kstep = fast_dma ? (int64_t)BN * kstride : 0, vstep = fast_dma ? (int64_t)BN * vstride : 0;
-  const __bf16* k_rows = kbase_s + 2 * kstep;   // tile 2, then one tile further per pipeline tile
-  const __bf16* v_rows = vbase_s + 2 * vstep;
+  const int64_t kjump = (int64_t)gap * kstep, vjump = (int64_t)gap * vstep;
+  const __bf16* k_rows = kbase_s + key_tile(2) * kstep;   // tile 2, then one tile further per pipeline tile
+  const __bf16* v_rows = vbase_s + key_tile(2) * vstep;
   const unsigned k0_m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds + wave * TL::LO * 1024);
   const unsigned v0_m0 = k0_m0 + LdsMap<D>::VBASE;
   const unsigned spare_m0 = k0_m0 + 2 * kPPBufs * T::TILEB;
@@ -732,6 +773,8 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
     mi.key_last = Sk - 1 - 4 * (lane >> 5);
     mi.q_last[0] = q_offset + q0w + l32 - k_offset - 4 * (lane >> 5);
     mi.q_last[1] = mi.q_last[0] + 32;
+    mi.sink_end = sink_end - 4 * (lane >> 5);
+    mi.window = a.window;
     mi.causal = a.causal != 0;
     bf16x8 kf[NDS];           // K of the next S chain
     bf16x8 vf[2][NDT];        // V of the next PV products
@@ -766,7 +809,10 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
     for (int ds = 0; ds < NDS; ++ds) kf[ds] = read_k_at<D, 0, 0>(lds, m, ds);
     s0 = qk_tile<D>(kf, qf[0], of.negb[0]);
     const int n_full_s = __builtin_amdgcn_readfirstlane(n_full);
-    if (n_full_s == 0) mask_scores(s0, mi, 0, 0);
+    auto masked = [&](int kt) YRB_INLINE {
+      return kt >= n_full_s || (kt * BN + BN - 1 >= sink_end && kt * BN <= w_lo);
+    };
+    if (masked(key_tile(0))) mask_scores<WIN>(s0, mi, 0, BN * key_tile(0));
 
     // Tile t (buffer BT = t % 4, a compile-time constant here): quarters 2t
     // and 2t+1; tiles from n_full on (the causal diagonal, the ragged end)
@@ -776,28 +822,30 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
     auto tile = [&](int t, auto bt_tag) YRB_INLINE {
       constexpr int BT = decltype(bt_tag)::value;
       constexpr int BT1 = (BT + 1) % kPPBufs;
-      const bool mk = t >= n_full_s, mk1 = t + 1 >= n_full_s;   // quarters 2t, 2t+1 / 2t+2 masked
+      const int kb = BN * key_tile(t), kb1 = BN * key_tile(t + 1);   // first keys of tiles t, t+1
+      const bool mk = masked(kb / BN), mk1 = masked(kb1 / BN);         // quarters 2t, 2t+1 / 2t+2 masked
       bool g, nd;
       // H1(2t): S1(2t), PV1(2t-1); softmax 0; read K(2t+1)
       g = half_step<D, 1, 0, 0, BT, 1, false, true, EXACT>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, mk, nd);
-      settle<D, 0, EXACT>(s0, st, of, g, nd, p0, mk, s1, mi, 1, 64 * t);
+      settle<D, 0, EXACT, WIN>(s0, st, of, g, nd, p0, mk, s1, mi, 1, kb);
       // H2(2t): S0(2t+1), PV0(2t); softmax 1; read V(2t)
       g = half_step<D, 0, BT, 0, 0, 0, true, false, EXACT>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1, mk, nd);
-      settle<D, 1, EXACT>(s1, st, of, g, nd, p1, mk, s0, mi, 0, 64 * t + 32);
+      settle<D, 1, EXACT, WIN>(s1, st, of, g, nd, p1, mk, s0, mi, 0, kb + 32);
       // H1(2t+1): S1(2t+1), PV1(2t); softmax 0; arrival of tile t+1, read
       // K(2t+2) from it, and the DMA of tile t+3 into the buffer of tile t-1
-      k_rows += kstep;
-      v_rows += vstep;
+      const bool jump = t + 3 == n_sink_t;   // tile t+3 is the first past the gap
+      k_rows += jump ? kstep + kjump : kstep;
+      v_rows += jump ? vstep + vjump : vstep;
       const DmaPlan dp = dma_plan<D, (BT + 3) % kPPBufs>(t + 3, n_fast, n_tiles, k_rows, v_rows, ph_k, ph_v,
                                                          k0_m0, v0_m0, spare_m0);
       g = half_step<D, 1, 0, 0, BT1, 0, false, true, EXACT, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, mk,
                                                                   nd, &dp,
                                                            koff, voff, wave);
-      settle<D, 0, EXACT>(s0, st, of, g, nd, p0, mk, s1, mi, 1, 64 * t + 32);
+      settle<D, 0, EXACT, WIN>(s0, st, of, g, nd, p0, mk, s1, mi, 1, kb + 32);
       if (__builtin_expect(dp.slow, 0)) issue(t + 3);
       // H2(2t+1): S0(2t+2), PV0(2t+1); softmax 1; read V(2t+1)
       g = half_step<D, 0, BT, 1, 0, 0, true, false, EXACT>(st, of, lds, m, vf, p0, kf, qf[0], s0, s1, p1, mk1, nd);
-      settle<D, 1, EXACT>(s1, st, of, g, nd, p1, mk1, s0, mi, 0, 64 * t + 64);
+      settle<D, 1, EXACT, WIN>(s1, st, of, g, nd, p1, mk1, s0, mi, 0, kb1);
     };
     for (int t = 0;;) {
       tile(t, std::integral_constant<int, 0>{});
@@ -835,7 +883,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   finish_rows<D, 2>(a, b, h, q0w, lane, st);
 }
 
-template <int D, bool EXACT>
+template <int D, bool EXACT, bool WIN>
 hipError_t launch_pp_as(const AttnArgs& a, hipStream_t stream) {
   constexpr int BM = kPPWaves * 64;
   constexpr int LDS_BYTES = (kPPBufs * 2 + 1) * Tile<D, kPPBN>::TILEB;   // K, V tiles and a spare
@@ -844,21 +892,23 @@ hipError_t launch_pp_as(const AttnArgs& a, hipStream_t stream) {
   const int64_t blocks = n_qtiles * a.B * a.Hq;
   if (blocks == 0) return hipSuccess;
   if (LDS_BYTES > 65536) {   // above the default dynamic-LDS limit
-    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_pp_kernel<D, EXACT>),
+    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_pp_kernel<D, EXACT, WIN>),
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (attr != hipSuccess) return attr;
   }
   static std::atomic<unsigned> next_slot{0};
   const unsigned slot = next_slot.fetch_add(1, std::memory_order_relaxed) % kClaimSlots;
   const int claim_from = blocks >= kClaimMinBlocks ? (int)(blocks * 7 / 10) : (int)blocks;
-  hipLaunchKernelGGL((attn_bf16_pp_kernel<D, EXACT>), dim3((unsigned)blocks), dim3(kPPWaves * 64), LDS_BYTES,
+  hipLaunchKernelGGL((attn_bf16_pp_kernel<D, EXACT, WIN>), dim3((unsigned)blocks), dim3(kPPWaves * 64), LDS_BYTES,
                      stream, a, n_qtiles, claim_from, slot);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
-  return a.store_state ? launch_pp_as<D, true>(a, stream) : launch_pp_as<D, false>(a, stream);
+  // The sink+window mask comes only with a finalized output (the prefill).
+  if (a.window > 0) return a.store_state ? hipErrorInvalidValue : launch_pp_as<D, false, true>(a, stream);
+  return a.store_state ? launch_pp_as<D, true, false>(a, stream) : launch_pp_as<D, false, false>(a, stream);
 }
 
 }  // namespace

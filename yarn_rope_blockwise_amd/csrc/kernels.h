@@ -46,6 +46,11 @@ struct AttnArgs {
   int load_state;                // read (o_acc, m, l) first
   int store_state;               // write (o_acc, m, l) at the end
   int finalize;                  // write o (and lse) at the end
+  // Sink+window mask (bf16 pipelined kernel only; window 0 = off): key
+  // position n is visible to query position t iff n < n_sink or
+  // n > t - window, on top of the causal rule.
+  int n_sink;
+  int window;
 };
 hipError_t launch_attention(int dtype, int D, const AttnArgs& a, hipStream_t stream);
 // The software-pipelined bf16 kernel (attn_pp.hip); called by launch_attention.
