@@ -56,6 +56,14 @@ MEASURED_TRAFFIC = {
         "files": ("csrc/decode.hip", "csrc/common.h"),
         "sha256": "ae8cf56a20c0a14593b206381671dabe73240b75c121f6dc18a0e1670b2692e2",
         "fetch_kib": 2109599, "write_kib": 512},
+    "decode_bf16_kernel_fp8": {
+        "files": ("csrc/decode.hip", "csrc/common.h"),
+        "sha256": None,
+        "fetch_kib": None, "write_kib": None},
+    "attn_bf16_pp_kernel_window": {
+        "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
+        "sha256": None,
+        "fetch_kib": None, "write_kib": None},
 }
 FETCH_FACTOR, WRITE_FACTOR = 1.99994, 1.0
 
@@ -508,7 +516,8 @@ def main():
                               "GB/s": round(g8, 1),
                               "roofline": {"bound": "hbm", "achieved": round(g8, 1),
                                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                           "frac": round(g8 / PEAK_HBM_GBS, 4), "traffic": None,
+                                           "frac": round(g8 / PEAK_HBM_GBS, 4),
+                                           "traffic": measured_traffic("decode_bf16_kernel_fp8"),
                                            "kernel": "decode_bf16_kernel<fp8>",
                                            "bytes_per_launch": d8["bytes"]}}
         il = run_interleaved(max(args.steps, 10), max(args.warmup, 10))
@@ -526,7 +535,8 @@ def main():
             "workload": "llama7b_prefill_16k_yarn4 attention, 4 sinks + 4096 window",
             "ms": round(sw["ms"], 4), "flops_per_launch": sw["flops"],
             "TFLOP/s": round(sw["flops"] / (sw["ms"] * 1e-3) / 1e12, 2),
-            "frac_bf16_peak": round(sw["flops"] / (sw["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            "frac_bf16_peak": round(sw["flops"] / (sw["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("attn_bf16_pp_kernel_window")}
         log(f"sink+window prefill done: {sw['ms']:.3f} ms")
         log("ring share: uploading blocks and timing")
         ring = run_ring(max(2, args.steps // 5), 2)
