@@ -50,20 +50,20 @@ METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HB
 MEASURED_TRAFFIC = {
     "attn_bf16_pp_kernel": {
         "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
-        "sha256": "b9e3f833616e1b77c5097111593bdcbbb8b3e0ad68b1f5cd3ed92e1e63982cdc",
-        "fetch_kib": 1036651, "write_kib": 131091},
+        "sha256": "46e2ada3543708ae651cda4143339c2fa383fe1e5b6512ef91214690540fc479",
+        "fetch_kib": 1034654, "write_kib": 131091},
     "decode_bf16_kernel": {
         "files": ("csrc/decode.hip", "csrc/common.h"),
-        "sha256": "ae8cf56a20c0a14593b206381671dabe73240b75c121f6dc18a0e1670b2692e2",
-        "fetch_kib": 2109599, "write_kib": 512},
+        "sha256": "2b7ae4f19e9fb1a37ba0247168072493fa9dd55f049a5c856197b65d8d922fb9",
+        "fetch_kib": 2108854, "write_kib": 512},
     "decode_bf16_kernel_fp8": {
         "files": ("csrc/decode.hip", "csrc/common.h"),
-        "sha256": None,
-        "fetch_kib": None, "write_kib": None},
+        "sha256": "2b7ae4f19e9fb1a37ba0247168072493fa9dd55f049a5c856197b65d8d922fb9",
+        "fetch_kib": 1060098, "write_kib": 512},
     "attn_bf16_pp_kernel_window": {
         "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
-        "sha256": None,
-        "fetch_kib": None, "write_kib": None},
+        "sha256": "46e2ada3543708ae651cda4143339c2fa383fe1e5b6512ef91214690540fc479",
+        "fetch_kib": 1368408, "write_kib": 131091},
 }
 FETCH_FACTOR, WRITE_FACTOR = 1.99994, 1.0
 
