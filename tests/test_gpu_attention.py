@@ -290,6 +290,31 @@ def test_accumulate_bf16_ring_small(qi):
     assert max_abs(host(o2), o_ref) <= BF16_TOL
 
 
+def test_accumulate_rows_that_start_empty():
+    # Query rows at positions 0..255 against a key block at positions
+    # 100..399 (causal): rows below 100 see none of its keys while later rows
+    # of the same wave do.  Their state stays empty (m = -inf, l = 0, o = 0);
+    # the other rows match the oracle.
+    require_gpu()
+    import torch
+    Sq, Sk, H, D, scale = 256, 300, 2, 128, 0.09
+    qv, q = draw((1, Sq, H, D), 71, "bf16")
+    kv, k = draw((1, Sk, H, D), 72, "bf16")
+    vv, v = draw((1, Sk, H, D), 73, "bf16")
+    st = api.AccState.empty(1, Sq, H, D)
+    say("attn_block_accumulate rows that start empty: q 0..255, k 100..399")
+    o = api.attn_block_accumulate(q, k, v, st, 0, 100, scale, first=True, finalize=True)
+    torch.cuda.synchronize()
+    got_o, got_m, got_l = host(o), host(st.m), host(st.l)
+    for h in range(H):
+        ref, m, l = A.attention_full(qv[0, :, h], kv[0, :, h], vv[0, :, h], scale, np.arange(Sq),
+                                     100 + np.arange(Sk), A.causal_visible, return_state=True)
+        assert max_abs(got_o[0, :, h], ref) <= BF16_TOL
+        assert np.all(np.isneginf(got_m[0, h, :100])) and np.all(got_l[0, h, :100] == 0)
+        np.testing.assert_allclose(got_m[0, h, 100:], m[100:], atol=2e-2)
+        np.testing.assert_allclose(got_l[0, h, 100:], l[100:], rtol=2e-2)
+
+
 def test_accumulate_resume_from_host_snapshot():
     require_gpu()
     import torch
