@@ -649,13 +649,14 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   int n_full = min(n_key_tiles, Sk / BN);
   if (a.causal) n_full = min(n_full, max(0, q_first_wg - k_offset + 1) / BN);
   // With a window the workgroup needs the sink tiles [0, n_sink_t) and the
-  // window tiles [tw0, n_key_tiles): the pipeline walks them in that order,
-  // its tile t being key tile t below n_sink_t and t + gap from there on.
+  // window tiles [tw0, n_key_tiles): the pipeline walks the sink tiles
+  // first (its tile t is key tile t below n_sink_t), then the window tiles
+  // past them, skipping the gap between.
   // A key tile needs the mask unless it is below n_full and wholly among
   // the sinks (its last key before sink_end) or wholly inside the window of
   // the workgroup's last row (its first key after w_lo).  Without a window
   // sink_end = 0 and w_lo = -1, so only n_full decides.
-  int n_sink_t = 0, gap = 0, sink_end = 0, w_lo = -1;
+  int n_sink_t = 0, gap = 0, sink_end = 0, w_lo = -1, n_win = 0, rot = 0;
   if constexpr (WIN) {
     sink_end = (int)max((int64_t)0, min((int64_t)a.n_sink - k_offset, (int64_t)n_key_tiles * BN));
     n_sink_t = (sink_end + BN - 1) / BN;
@@ -666,9 +667,25 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
     gap = __builtin_amdgcn_readfirstlane(gap);
     sink_end = __builtin_amdgcn_readfirstlane(sink_end);
     w_lo = __builtin_amdgcn_readfirstlane(w_lo);
+    // The window tiles [wstart, n_key_tiles) start at a phase shared by the
+    // 8 query tiles of an aligned group (the first window tile of the
+    // group's last query tile) and wrap round to wstart: query tiles that
+    // run side by side then read the same key tiles at about the same time.
+    const int wstart = n_sink_t + gap;
+    n_win = n_key_tiles - wstart;
+    const int q_grp = q_offset + min((qtile | 7) * BM, (Sq - 1) / BM * BM);
+    const int phase = max(0, q_grp - k_offset - a.window + 1) / BN;
+    rot = max(0, min(phase - wstart, n_win - 1));
+    n_win = __builtin_amdgcn_readfirstlane(n_win);
+    rot = __builtin_amdgcn_readfirstlane(rot);
   }
   const int n_tiles = n_key_tiles - gap;   // pipeline tiles
-  auto key_tile = [&](int t) YRB_INLINE { return t < n_sink_t ? t : t + gap; };
+  auto key_tile = [&](int t) YRB_INLINE {
+    if constexpr (!WIN) return t;
+    if (t < n_sink_t) return t;
+    const int u = t - n_sink_t + rot;
+    return n_sink_t + gap + (u >= n_win ? u - n_win : u);
+  };
   const bool wave_live = q0w < Sq;
 
   const __bf16* kbase = reinterpret_cast<const __bf16*>(a.k) + b * a.ks[0] + hk * a.ks[2];
@@ -756,11 +773,16 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
   // keys, plus the clamped load after the half step when it is ragged).
   // Pipeline tiles [0, n_fast) are full key tiles inside the keys the
   // workgroup needs and go by the fast path; the pipeline walks their first
-  // rows tile by tile, jumping the gap after the sink tiles.
+  // rows tile by tile.  With a window the walk is not monotonic: a tile goes
+  // by the fast path if it is a pipeline tile and a full key tile, and its
+  // first row comes from its key tile.
   const int n_full_k = min(n_key_tiles, Sk / BN);
-  const int n_fast = !fast_dma ? 0 : n_full_k <= n_sink_t ? n_full_k : max(n_sink_t, n_full_k - gap);
+  const int n_fast = fast_dma ? min(n_tiles, Sk / BN) : 0;
+  auto fast_bound = [&](int u) YRB_INLINE {   // dma_plan takes u as real iff u < fast_bound(u)
+    if constexpr (!WIN) return n_fast;
+    return (fast_dma && u < n_tiles && key_tile(u) < n_full_k) ? u + 1 : 0;
+  };
   const int64_t kstep = fast_dma ? (int64_t)BN * kstride : 0, vstep = fast_dma ? (int64_t)BN * vstride : 0;
-  const int64_t kjump = (int64_t)gap * kstep, vjump = (int64_t)gap * vstep;
   const __bf16* k_rows = kbase_s + key_tile(2) * kstep;   // tile 2, then one tile further per pipeline tile
   const __bf16* v_rows = vbase_s + key_tile(2) * vstep;
   const unsigned k0_m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds + wave * TL::LO * 1024);
@@ -793,7 +815,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
       if (n_tiles > 1) wait_vmcnt<DMA>();
       else wait_vmcnt<0>();
       tile_barrier();
-      const DmaPlan dp = dma_plan<D, 2 % kPPBufs>(2, n_fast, n_tiles, k_rows, v_rows, ph_k, ph_v, k0_m0,
+      const DmaPlan dp = dma_plan<D, 2 % kPPBufs>(2, fast_bound(2), n_tiles, k_rows, v_rows, ph_k, ph_v, k0_m0,
                                                   v0_m0, spare_m0);
       static_for<TL::LO>([&](auto n_tag) YRB_INLINE {
         constexpr int n = decltype(n_tag)::value;
@@ -833,10 +855,14 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
       settle<D, 1, EXACT, WIN>(s1, st, of, g, nd, p1, mk, s0, mi, 0, kb + 32);
       // H1(2t+1): S1(2t+1), PV1(2t); softmax 0; arrival of tile t+1, read
       // K(2t+2) from it, and the DMA of tile t+3 into the buffer of tile t-1
-      const bool jump = t + 3 == n_sink_t;   // tile t+3 is the first past the gap
-      k_rows += jump ? kstep + kjump : kstep;
-      v_rows += jump ? vstep + vjump : vstep;
-      const DmaPlan dp = dma_plan<D, (BT + 3) % kPPBufs>(t + 3, n_fast, n_tiles, k_rows, v_rows, ph_k, ph_v,
+      if constexpr (WIN) {
+        k_rows = kbase_s + key_tile(t + 3) * kstep;
+        v_rows = vbase_s + key_tile(t + 3) * vstep;
+      } else {
+        k_rows += kstep;
+        v_rows += vstep;
+      }
+      const DmaPlan dp = dma_plan<D, (BT + 3) % kPPBufs>(t + 3, fast_bound(t + 3), n_tiles, k_rows, v_rows, ph_k, ph_v,
                                                          k0_m0, v0_m0, spare_m0);
       g = half_step<D, 1, 0, 0, BT1, 0, false, true, EXACT, true>(st, of, lds, m, vf, p1, kf, qf[1], s1, s0, p0, mk,
                                                                   nd, &dp,
