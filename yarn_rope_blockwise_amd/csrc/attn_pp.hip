@@ -830,9 +830,19 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) kf[ds] = read_k_at<D, 0, 0>(lds, m, ds);
     s0 = qk_tile<D>(kf, qf[0], of.negb[0]);
-    const int n_full_s = __builtin_amdgcn_readfirstlane(n_full);
+    // With a window the test is made per wave, for its own 64 rows: fewer
+    // tiles on the diagonal and at the window's lower edge need the mask
+    // than for the workgroup's 256 rows.
+    int n_full_m = n_full, w_lo_m = w_lo;
+    if constexpr (WIN) {
+      const int qf_w = q_offset + q0w - k_offset, ql_w = q_offset + min(Sq, q0w + QW) - 1 - k_offset;
+      n_full_m = min(min(n_key_tiles, Sk / BN), max(0, qf_w + 1) / BN);
+      w_lo_m = max(-1, ql_w - a.window);
+    }
+    const int n_full_s = __builtin_amdgcn_readfirstlane(n_full_m);
+    const int w_lo_s = __builtin_amdgcn_readfirstlane(w_lo_m);
     auto masked = [&](int kt) YRB_INLINE {
-      return kt >= n_full_s || (kt * BN + BN - 1 >= sink_end && kt * BN <= w_lo);
+      return kt >= n_full_s || (kt * BN + BN - 1 >= sink_end && kt * BN <= w_lo_s);
     };
     if (masked(key_tile(0))) mask_scores<WIN>(s0, mi, 0, BN * key_tile(0));
 
