@@ -128,16 +128,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
   const int len = bad_seq ? 0 : len_raw;
   const int rh = bad_seq ? 0 : rh_raw;
 
-  // Position of the entry in `slot`, or -1 when the slot holds none.
+  // Position of the entry in `slot`, or -1 when the slot holds none.  A
+  // window slot below C is less than `window` past n_sink and the head is
+  // below `window`, so one conditional add takes the offset mod window, with
+  // no integer division.
   auto position = [&](int slot) -> int {
-    int e;
-    if (slot < n_sink) {
-      e = slot;
-    } else {
-      int j = (slot - n_sink - rh) % window;
-      if (j < 0) j += window;
-      e = n_sink + j;
-    }
+    const int d = slot - n_sink - rh;
+    const int e = slot < n_sink ? slot : n_sink + (d < 0 ? d + window : d);
     return (slot < C && e < len) ? e : -1;
   };
 
@@ -273,15 +270,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
       }
 #pragma unroll
       for (int r = 0; r < kRounds; ++r) {
-        const float p = fast_exp2(sc_[g][r] - mn);
+        const float p = fast_exp2(sc_[g][r] - mn);   // 0 for a slot without an entry
         l[g] += p;
+        // Such a slot's values are zeroed as raw words (whatever the cache
+        // holds there, NaN codes included), so p * v adds 0.
         float v1[8], v2[8];
-        CT::unpack(ch.vlo[r], v1);
-        CT::unpack(ch.vhi[r], v2);
+        CT::unpack(ch.ok[r] ? ch.vlo[r] : Chunk{}, v1);
+        CT::unpack(ch.ok[r] ? ch.vhi[r] : Chunk{}, v2);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          o_lo[g][u] = __builtin_fmaf(p, ch.ok[r] ? v1[u] : 0.f, o_lo[g][u]);
-          o_hi[g][u] = __builtin_fmaf(p, ch.ok[r] ? v2[u] : 0.f, o_hi[g][u]);
+          o_lo[g][u] = __builtin_fmaf(p, v1[u], o_lo[g][u]);
+          o_hi[g][u] = __builtin_fmaf(p, v2[u], o_hi[g][u]);
         }
       }
     }
