@@ -50,20 +50,20 @@ METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HB
 MEASURED_TRAFFIC = {
     "attn_bf16_pp_kernel": {
         "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
-        "sha256": "46e2ada3543708ae651cda4143339c2fa383fe1e5b6512ef91214690540fc479",
-        "fetch_kib": 1034654, "write_kib": 131091},
+        "sha256": "37d8ba827eb24d4b8be628a3b0433492cbca0897932b17cbcba3679efa4c9ff0",
+        "fetch_kib": 1060865, "write_kib": 131091},
     "decode_bf16_kernel": {
         "files": ("csrc/decode.hip", "csrc/common.h"),
-        "sha256": "2b7ae4f19e9fb1a37ba0247168072493fa9dd55f049a5c856197b65d8d922fb9",
-        "fetch_kib": 2108854, "write_kib": 512},
+        "sha256": "e9d3cda8d5a31a43fa5949701d2e3957b448b27c4792b438c6a7b0b5404f7b9c",
+        "fetch_kib": 2108657, "write_kib": 512},
     "decode_bf16_kernel_fp8": {
         "files": ("csrc/decode.hip", "csrc/common.h"),
-        "sha256": "2b7ae4f19e9fb1a37ba0247168072493fa9dd55f049a5c856197b65d8d922fb9",
-        "fetch_kib": 1060098, "write_kib": 512},
+        "sha256": "e9d3cda8d5a31a43fa5949701d2e3957b448b27c4792b438c6a7b0b5404f7b9c",
+        "fetch_kib": 1060707, "write_kib": 512},
     "attn_bf16_pp_kernel_window": {
         "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
-        "sha256": "46e2ada3543708ae651cda4143339c2fa383fe1e5b6512ef91214690540fc479",
-        "fetch_kib": 1368408, "write_kib": 131091},
+        "sha256": "37d8ba827eb24d4b8be628a3b0433492cbca0897932b17cbcba3679efa4c9ff0",
+        "fetch_kib": 733819, "write_kib": 131091},
 }
 FETCH_FACTOR, WRITE_FACTOR = 1.99994, 1.0
 
