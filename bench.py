@@ -50,7 +50,7 @@ METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HB
 MEASURED_TRAFFIC = {
     "attn_bf16_pp_kernel": {
         "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
-        "sha256": "37d8ba827eb24d4b8be628a3b0433492cbca0897932b17cbcba3679efa4c9ff0",
+        "sha256": "ce8e6c36e22a7e2c76919f55ab83bb5006d79a7ef3bcad54fbf6a901c3916ea5",
         "fetch_kib": 1060865, "write_kib": 131091},
     "decode_bf16_kernel": {
         "files": ("csrc/decode.hip", "csrc/common.h"),
@@ -62,7 +62,7 @@ MEASURED_TRAFFIC = {
         "fetch_kib": 1060707, "write_kib": 512},
     "attn_bf16_pp_kernel_window": {
         "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
-        "sha256": "37d8ba827eb24d4b8be628a3b0433492cbca0897932b17cbcba3679efa4c9ff0",
+        "sha256": "ce8e6c36e22a7e2c76919f55ab83bb5006d79a7ef3bcad54fbf6a901c3916ea5",
         "fetch_kib": 733819, "write_kib": 131091},
 }
 FETCH_FACTOR, WRITE_FACTOR = 1.99994, 1.0

@@ -114,3 +114,28 @@ def test_prefill_sink_window_full_llama16k():
                         window=window)[0, :, 0]
         worst = max(worst, max_abs(got, ref))
     assert worst <= BF16_TOL, worst
+
+
+def test_prefill_sink_window_full_gqa32k():
+    # The 32k GQA prefill (YaRN s=8) with 4 sinks and an 8192-token window:
+    # sampled rows of query heads from different key groups.
+    require_gpu()
+    import torch
+    w = W.GQA_32K[W.YARN]
+    n_sink, window = 4, 8192
+    tab, th, scale, (qv, kv, vv), (q, k, v) = _setup(w.batch, w.seq, w.n_q_heads, w.n_kv_heads,
+                                                     w.head_dim, w.rope, 100)
+    say(f"attn_prefill_sink_window {w.name} sink={n_sink} window={window}")
+    kr = api.rope_apply(k, tab)
+    del k
+    o = api.attn_prefill_sink_window(q, kr, v, scale, n_sink, window, cos_sin=tab)
+    torch.cuda.synchronize()
+    edges = [0, 5, 255, 256, window - 1, window, window + 255, window + 256, w.seq - 1]
+    worst = 0.0
+    for h in (0, w.n_q_heads // 2 + 1, w.n_q_heads - 1):
+        rows = synth.sample_rows(w.seq, 20, 3000 + h, must=edges)
+        got = host(o[0, rows, h])
+        ref = A.prefill(qv, kv, vv, th, scale, rows=rows, heads=[h], n_sink=n_sink,
+                        window=window)[0, :, 0]
+        worst = max(worst, max_abs(got, ref))
+    assert worst <= BF16_TOL, worst

@@ -44,6 +44,11 @@
 //    together, and Q is rotated from the table in fp32.  Work items run
 //    heaviest first; the last part of the grid claims its items from a
 //    counter so that XCDs running at different clocks finish together.
+//  * A template flag adds the attention-sink plus sliding-window mask of
+//    the 14cs17 notes ("Sliding Window + Attention Sinks") on top of the
+//    causal rule: the pipeline walks the sink tiles, then only the tiles
+//    some row of the workgroup sees in its window, from a phase shared by
+//    neighbouring query tiles; the tiles between are never loaded.
 #include "attn_frag.h"
 #include "common.h"
 #include "kernels.h"
