@@ -73,6 +73,22 @@ def test_prefill_sink_window_small(B, S, Hq, Hkv, D, n_sink, window):
             assert max_abs(lse_h[b, h], m + np.log(l)) <= BF16_TOL
 
 
+def test_prefill_sink_window_packed_qkv_views():
+    # Pre-rotated Q, K, V as views into a packed [B, S, 3, H, D] buffer
+    # (strided tokens and heads), cos_sin = NULL.
+    require_gpu()
+    import torch
+    B, S, H, D = 2, 900, 2, 128
+    qkv_v, qkv = draw((B, S, 3, H, D), 78, "bf16")
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    say(f"attn_prefill_sink_window packed qkv views S={S} sink=8 window=300")
+    o = api.attn_prefill_sink_window(q, k, v, 0.1, 8, 300)
+    torch.cuda.synchronize()
+    ref = A.prefill(qkv_v[:, :, 0], qkv_v[:, :, 1], qkv_v[:, :, 2], None, 0.1, n_sink=8,
+                    window=300)
+    assert max_abs(host(o), ref) <= BF16_TOL
+
+
 def test_prefill_sink_window_wide_window_is_causal_prefill():
     # A window of S keys reaches every earlier key: the same tiles, masks and
     # order as the causal prefill, so the same bits.
