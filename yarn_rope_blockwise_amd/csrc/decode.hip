@@ -65,10 +65,15 @@ struct CacheType<true> {
   }
 };
 
-// K/V of one step for one lane: kRounds keys, two chunks each.
-template <bool FP8>
+// Key rounds per wave per step: the cache type's, halved for a bf16 cache
+// with 8 query heads per key head, whose per-head query and output
+// registers leave too few for four rounds of 16-byte chunks (it spilled).
+template <bool FP8, int G>
+constexpr int rounds_of() { return (!FP8 && G >= 8) ? 2 : CacheType<FP8>::kRounds; }
+
+// K/V of one step for one lane: R keys, two chunks each.
+template <bool FP8, int R>
 struct KVChunk {
-  static constexpr int R = CacheType<FP8>::kRounds;
   typename CacheType<FP8>::Chunk klo[R], khi[R], vlo[R], vhi[R];
   bool ok[R];
 };
@@ -98,7 +103,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
   using CT = CacheType<FP8>;
   using Chunk = typename CT::Chunk;
   using Elem = typename CT::Elem;
-  constexpr int kRounds = CT::kRounds;
+  constexpr int kRounds = rounds_of<FP8, G>();
+  using KV = KVChunk<FP8, kRounds>;
   constexpr int TPK = D / 16;              // lanes per key row
   constexpr int KPW = 64 / TPK;            // keys per wave per round
   constexpr int KPS = KPW * kRounds;       // slots per step (shared by the 4 waves)
@@ -206,7 +212,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
     }
   };
   // K/V loads of the step starting at `base`.
-  auto load_kv = [&](int base, KVChunk<FP8>& ch) {
+  auto load_kv = [&](int base, KV& ch) {
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
       const int slot = base + r * KPW + kg;
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
     }
   };
   // Fold one step's keys into (m, l, o); (cos, sin) come from the LDS tile.
-  auto fold = [&](const KVChunk<FP8>& ch, const YRB_LDS char* tl) {
+  auto fold = [&](const KV& ch, const YRB_LDS char* tl) {
     float sc_[G][kRounds];
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
@@ -304,9 +310,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
     store_tab(tab0, tv);
   }
   lds_barrier();
-  KVChunk<FP8> c0, c1;
+  KV c0, c1;
   if (n_slots > 0) load_kv(0, c0);
-  auto step = [&](int base, KVChunk<FP8>& cur, KVChunk<FP8>& nxt, const YRB_LDS char* tl,
+  auto step = [&](int base, KV& cur, KV& nxt, const YRB_LDS char* tl,
                   YRB_LDS char* tn) {
     const bool more = base + KPS < n_slots;
     u32x4 tv[TCH];
