@@ -54,12 +54,12 @@ MEASURED_TRAFFIC = {
         "fetch_kib": 1060865, "write_kib": 131091},
     "decode_bf16_kernel": {
         "files": ("csrc/decode.hip", "csrc/common.h"),
-        "sha256": "e9d3cda8d5a31a43fa5949701d2e3957b448b27c4792b438c6a7b0b5404f7b9c",
-        "fetch_kib": 2108657, "write_kib": 512},
+        "sha256": "bb86e0e7d62bfd147d1ef7163969d9f4cb27d1676997f5cb425c4230aea4a39b",
+        "fetch_kib": 2108966, "write_kib": 512},
     "decode_bf16_kernel_fp8": {
         "files": ("csrc/decode.hip", "csrc/common.h"),
-        "sha256": "e9d3cda8d5a31a43fa5949701d2e3957b448b27c4792b438c6a7b0b5404f7b9c",
-        "fetch_kib": 1060707, "write_kib": 512},
+        "sha256": "bb86e0e7d62bfd147d1ef7163969d9f4cb27d1676997f5cb425c4230aea4a39b",
+        "fetch_kib": 1060697, "write_kib": 512},
     "attn_bf16_pp_kernel_window": {
         "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
         "sha256": "ce8e6c36e22a7e2c76919f55ab83bb5006d79a7ef3bcad54fbf6a901c3916ea5",
