@@ -1,8 +1,8 @@
-// Fragment-level building blocks of the bf16 attention kernels (gfx950):
-// LDS tile geometry and swizzles, the LDS-DMA tile loader, the MFMA
-// fragment reads of K and V, the two products S^T = K Q^T and O^T += V^T P^T,
-// and the online-softmax update of one 32-key quarter.  Included by the
-// kernels' translation units; everything here has internal linkage.
+// Building blocks of the pipelined bf16 attention kernel (gfx950): LDS tile
+// geometry and swizzles, the LDS-DMA tile loaders, the per-wave state and
+// its inline-asm product O^T += V^T P^T, the work order, the query load and
+// rotation, and the state's set-up and epilogue.  Included by the kernel's
+// translation unit; everything here has internal linkage.
 #pragma once
 
 #include "common.h"
@@ -178,87 +178,6 @@ struct WaveState {
   float l[NQT];        // per-lane partial row sum (this half's keys)
 };
 
-// One K fragment (A operand of S^T = K Q^T) of quarter kq: lane holds key
-// 32kq + l32, dims 16ds + 8hh .. +7.
-template <int D>
-__device__ __forceinline__ bf16x8 read_k_frag(const YRB_LDS char* kt_lds, int kq, int lane, int ds) {
-  constexpr int ROWB = D * 2;
-  const int r = kq * 32 + (lane & 31);
-  const int c = 2 * ds + (lane >> 5);
-  return *reinterpret_cast<const YRB_LDS bf16x8*>(kt_lds + r * ROWB + ((c ^ ksw<D>(r)) << 4));
-}
-
-template <int D>
-__device__ __forceinline__ void read_k_quarter(const YRB_LDS char* kt_lds, int kq, int lane,
-                                               bf16x8 (&kf)[D / 16]) {
-#pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds) kf[ds] = read_k_frag<D>(kt_lds, kq, lane, ds);
-}
-
-// S^T for 32 keys against the wave's queries:
-// s[qt][j] = q(row qt*32 + l32) . k(key 32kq + 8(j/4) + 4hh + j%4).
-template <int D, int NQT>
-__device__ __forceinline__ void qk_mfma(const bf16x8 (&kf)[D / 16],
-                                        const bf16x8 (&qf)[NQT][D / 16], f32x16 (&s)[NQT]) {
-#pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) s[qt] = (f32x16){};
-#pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds)
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt)
-      s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[qt][ds], s[qt], 0, 0, 0);
-}
-
-// One V^T fragment (A operand of O^T += V^T P^T) of quarter kq: k-step
-// 2kq + half, d tile dt.  Lane i supplies the address of V[row][d..d+3]
-// with row = 16ks + 8*second + 4(i/32) + (i%16)/4 and d = 32dt +
-// 16((i/16)%2) + 4(i%4); ds_read_b64_tr_b16 hands lane l the column
-// d = 32dt + l%32 over keys 16ks + 8*second + 4(l/32) + 0..3, the key order
-// the packed P uses.
-template <int D>
-__device__ __forceinline__ bf16x8 read_v_frag(const YRB_LDS char* vt_lds, int kq, int lane, int half,
-                                              int dt) {
-  constexpr int ROWB = D * 2;
-  const int g = lane >> 4;
-  const int t4 = (lane & 15) >> 2;
-  const int s4 = lane & 3;
-  const int ks = 2 * kq + half;
-  const int row1 = 16 * ks + 4 * (g >> 1) + t4;
-  const int row2 = row1 + 8;
-  const int c = dt * 4 + 2 * (g & 1) + (s4 >> 1);
-  const int boff = 8 * (s4 & 1);
-  const YRB_LDS char* a1 = vt_lds + row1 * ROWB + ((c ^ vsw<D>(row1)) << 4) + boff;
-  const YRB_LDS char* a2 = vt_lds + row2 * ROWB + ((c ^ vsw<D>(row2)) << 4) + boff;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a1);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YRB_LDS i16x4*)a2);
-  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-  const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-  const u32x4 vw = {lo2[0], lo2[1], hi2[0], hi2[1]};
-  return __builtin_bit_cast(bf16x8, vw);
-}
-
-template <int D>
-__device__ __forceinline__ void read_v_quarter(const YRB_LDS char* vt_lds, int kq, int lane,
-                                               bf16x8 (&vf)[2][D / 32]) {
-#pragma unroll
-  for (int half = 0; half < 2; ++half)
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) vf[half][dt] = read_v_frag<D>(vt_lds, kq, lane, half, dt);
-}
-
-template <int D, int NQT>
-__device__ __forceinline__ void pv_mfma(const bf16x8 (&vf)[2][D / 32], const bf16x8 (&pf)[2][NQT],
-                                        WaveState<D, NQT>& st) {
-#pragma unroll
-  for (int half = 0; half < 2; ++half)
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt)
-        st.o[dt][qt] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][dt], pf[half][qt], st.o[dt][qt], 0, 0, 0);
-}
-
 // O^T(AGPR) += V^T P^T for one 32x32x16 step, as inline asm so that the
 // accumulator stays in AGPRs while the compiler keeps its own MFMAs in the
 // VGPR form.  The compiler does not see this MFMA: VALU code that touches
@@ -291,110 +210,6 @@ __device__ __forceinline__ void scale_o_agpr(f32x16& o, float alpha) {
   asm volatile("s_nop 4" ::: "memory");
 }
 
-// Online-softmax update for one quarter: mask, row max, (rare) rescale,
-// P = exp2(s * scale_log2 - m_use) packed to bf16 as the B operand of
-// O^T += V^T P^T (k-step 2kq + half takes j = 8*half .. 8*half+7).
-template <int D, int NQT, bool ASM_O = false>
-__device__ __forceinline__ void softmax_quarter(f32x16 (&s)[NQT], WaveState<D, NQT>& st,
-                                                bool need_mask, int kk0, int Sk, int kpos_base,
-                                                int qpos_lane0, bool causal, float scale_log2,
-                                                int lane, bf16x8 (&pf)[2][NQT]) {
-  const int hh = lane >> 5;
-  if (need_mask) {
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      const int qpos = qpos_lane0 + qt * 32;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int kk = kk0 + 8 * (j >> 2) + 4 * hh + (j & 3);   // key index in the block
-        const bool bad = (kk >= Sk) || (causal && kpos_base + kk > qpos);
-        if (bad) s[qt][j] = -INFINITY;
-      }
-    }
-  }
-  bool grow = false;
-#pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    float mx = s[qt][0];
-#pragma unroll
-    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[qt][j]);
-    mx = pair_max(mx) * scale_log2;     // scale > 0 commutes with max
-    st.m_true[qt] = fmaxf(st.m_true[qt], mx);
-    grow |= st.m_true[qt] > st.m_use[qt] + kTau;
-  }
-  if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      const float mn = st.m_true[qt];
-      const float alpha = (st.m_use[qt] == -INFINITY) ? 0.f : fast_exp2(st.m_use[qt] - mn);
-      if (mn != -INFINITY) {
-        st.l[qt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          if (ASM_O) scale_o_agpr(st.o[dt][qt], alpha);
-          else st.o[dt][qt] *= alpha;
-        }
-        st.m_use[qt] = mn;
-      }
-    }
-  }
-#pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    const float mu = (st.m_use[qt] == -INFINITY) ? 0.f : st.m_use[qt];
-    float acc = 0.f;
-    float p[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      p[j] = fast_exp2(__builtin_fmaf(s[qt][j], scale_log2, -mu));
-      acc += p[j];
-    }
-    st.l[qt] += acc;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4 w;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = pack_bf16x2(p[8 * half + 2 * u], p[8 * half + 2 * u + 1]);
-      pf[half][qt] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
-}
-
-// Fold one BN-key tile (already in LDS) into the wave's state, 32 keys
-// (one quarter) at a time: S = K Q^T on the MFMA, the online-softmax update
-// on the VALU, then O^T += V^T P^T.  With two waves per SIMD the matrix
-// core of one wave's MFMAs overlaps the other wave's softmax.  (Explicitly
-// pipelining quarters inside a wave measured no faster on gfx950.)
-// ASM_O: O lives in AGPRs and the PV products are the inline-asm MFMAs.
-template <int D, int BN, int NQT, bool ASM_O = false>
-__device__ __forceinline__ void fold_tile(const YRB_LDS char* kt_lds, const YRB_LDS char* vt_lds,
-                                          const bf16x8 (&qf)[NQT][D / 16],
-                                          WaveState<D, NQT>& st, bool need_mask, int k0, int Sk,
-                                          int kpos0, int qpos_lane0, bool causal,
-                                          float scale_log2, int lane) {
-#pragma unroll
-  for (int kq = 0; kq < BN / 32; ++kq) {
-    bf16x8 kf[D / 16];
-    f32x16 s[NQT];
-    read_k_quarter<D>(kt_lds, kq, lane, kf);
-    qk_mfma<D, NQT>(kf, qf, s);
-    bf16x8 pf[2][NQT];
-    softmax_quarter<D, NQT, ASM_O>(s, st, need_mask, k0 + 32 * kq, Sk, kpos0 - k0, qpos_lane0, causal,
-                                   scale_log2, lane, pf);
-    bf16x8 vf[2][D / 32];
-    read_v_quarter<D>(vt_lds, kq, lane, vf);
-    if (ASM_O) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int qt = 0; qt < NQT; ++qt) mfma_o(st.o[dt][qt], vf[half][dt], pf[half][qt]);
-    } else {
-      pv_mfma<D, NQT>(vf, pf, st);
-    }
-  }
-}
-
 // Work item of a workgroup: the heaviest (causal) query tiles are launched
 // first, and consecutive workgroups take heads that are 8 apart, so the
 // workgroups an XCD runs at once (blocks go round-robin over the 8 XCDs)
@@ -416,10 +231,6 @@ __device__ __forceinline__ WorkItem work_item_at(const AttnArgs& a, int64_t n_qt
   w.hk = w.h / (Hq / (int)a.Hkv);
   return w;
 }
-__device__ __forceinline__ WorkItem work_item(const AttnArgs& a, int64_t n_qtiles) {
-  return work_item_at(a, n_qtiles, (int)blockIdx.x);
-}
-
 // Q fragments and their table rows as loaded, before the rotation.
 template <int D, int NQT>
 struct QRaw {
@@ -499,19 +310,6 @@ __device__ __forceinline__ void rotate_q(const AttnArgs& a, QRaw<D, NQT>& qr, bf
   static_for<NQT>([&](auto qt_tag) YRB_INLINE {
     rotate_q_tile<D, NQT, decltype(qt_tag)::value>(a, qr, qf, qscale);
   });
-}
-
-// Query fragments (B operand of S^T = K Q^T) of one wave: lane holds query
-// row q0w + 32qt + l32 (clamped to the last row), dims 16ds + 8hh .. +7,
-// rotated here in fp32 from the table when one is given, multiplied by
-// qscale, and rounded once to bf16.
-template <int D, int NQT>
-__device__ __forceinline__ void load_q(const AttnArgs& a, int b, int h, int q0w, int lane,
-                                       bf16x8 (&qf)[NQT][D / 16], float qscale = 1.0f) {
-  QRaw<D, NQT> qr;
-  load_q_raw<D, NQT>(a, b, h, q0w, lane, qr);
-  __builtin_amdgcn_sched_barrier(0);
-  rotate_q<D, NQT>(a, qr, qf, qscale);
 }
 
 // Running state of one wave: empty, or read from (o_acc, m, l) of an
