@@ -125,6 +125,7 @@ def run_prefill(steps: int, warmup: int):
     out = torch.empty_like(q)
     _, _, af = api.rope_tables_build(cfg, S, out=tab)
     scale = af / np.sqrt(D)
+    ws = api.new_workspace()
 
     def step(ev=None):
         if ev is not None:
@@ -135,7 +136,7 @@ def run_prefill(steps: int, warmup: int):
         api.rope_apply(k, tab, out=k_rot)
         if ev is not None:
             ev[2].record()
-        api.attn_prefill_blockwise(q, k_rot, v, scale, cos_sin=tab, out=out)
+        api.attn_prefill_blockwise(q, k_rot, v, scale, cos_sin=tab, out=out, workspace=ws)
         if ev is not None:
             ev[3].record()
 
@@ -181,9 +182,11 @@ def run_sink_window_prefill(steps: int, warmup: int, n_sink: int = 4, window: in
     k_rot = api.rope_apply(k, tab)
     out = torch.empty_like(q)
     scale = af / np.sqrt(D)
+    ws = api.new_workspace()
 
     def call():
-        api.attn_prefill_sink_window(q, k_rot, v, scale, n_sink, window, cos_sin=tab, out=out)
+        api.attn_prefill_sink_window(q, k_rot, v, scale, n_sink, window, cos_sin=tab, out=out,
+                                     workspace=ws)
 
     for _ in range(warmup):
         call()
@@ -333,6 +336,7 @@ def run_ring(steps: int, warmup: int):
     k = api.rope_apply(k_raw, tab)          # every block is rotated once by its owner
     st = api.AccState.empty(1, blk, H, D)
     out = torch.empty_like(q)
+    ws = api.new_workspace()
     order = W.ring_order(w)
     qi = w.q_block_index
     qoff = qi * blk
@@ -349,7 +353,7 @@ def run_ring(steps: int, warmup: int):
                 ev[t + 1].record()
             api.attn_block_accumulate(q, k[:, j * blk:(j + 1) * blk], v[:, j * blk:(j + 1) * blk],
                                       st, qoff, j * blk, scale, cos_sin=tab, first=(t == 0),
-                                      finalize=(t == nb - 1), out=out)
+                                      finalize=(t == nb - 1), out=out, workspace=ws)
         if ev is not None:
             ev[nb + 1].record()
 

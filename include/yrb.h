@@ -14,14 +14,10 @@
  *
  * Conventions shared by every call
  *  - Every device buffer is owned by the caller.  The library allocates no
- *    memory, never synchronises and calls are thread-safe.  Its one piece of
- *    mutable state is a static device array of 64 work-claim counters
- *    (4 KiB per GPU) that the two prefill calls and attn_block_accumulate
- *    use to balance the last 30 % of their grid across the XCDs: each
- *    launch takes the next counter in turn and leaves it at zero.  Two
- *    launches on one GPU that run at the same time with the same counter
- *    (64 launches apart, or one captured graph replayed on two streams at
- *    once) race and may skip or repeat query tiles.
+ *    memory, never synchronises and keeps no mutable state between calls:
+ *    calls may be made from any thread, and calls queued on different
+ *    streams may run at the same time, as long as they do not write the
+ *    same buffers.  A workspace (below) counts as a written buffer.
  *  - Work is queued on `stream` (a hipStream_t; NULL = the default stream)
  *    and completes asynchronously.  A kernel fault surfaces at the caller's
  *    next synchronisation.
@@ -78,6 +74,17 @@ extern "C" {
 /* Pair layouts of the rotation ([T] Sec. 2 pairs the d dimensions into d/2). */
 #define YRB_LAYOUT_HALF        0   /* (x_i, x_{i+d/2}): every other call */
 #define YRB_LAYOUT_INTERLEAVED 1   /* (x_{2i}, x_{2i+1}): the _ex calls    */
+
+/* Bytes of the optional `workspace` of the prefill calls and
+ * attn_block_accumulate: a device buffer, 16-byte aligned, that holds zeros
+ * before its first use.  Given one, the last 30 % of the launch's grid
+ * takes its work items from a counter there, so that the XCDs, which under
+ * load run at clocks a few percent apart, finish together; each call leaves
+ * the workspace as it found it (zero), so one workspace serves any number
+ * of calls in sequence on a stream.  Calls that may run at the same time
+ * need workspaces of their own.  With workspace = NULL every block takes a
+ * fixed item; the results are the same bit for bit either way. */
+#define YRB_WORKSPACE_BYTES 64
 
 /* attn_block_accumulate flags. */
 #define YRB_ACC_FIRST    1    /* ignore the incoming state: start from m=-inf, l=0, acc=0 */
@@ -194,6 +201,8 @@ int rope_apply_ex(const void* x, void* y, int32_t dtype,
  *   causal         0 or 1.
  *   lse            device [B][Hq][S] fp32 or NULL: ln sum_j exp(scale q.k_j)
  *                  per row (-inf for a row that sees no key).
+ *   workspace      NULL or YRB_WORKSPACE_BYTES of device memory (see there);
+ *                  misaligned: YRB_EALIGN.
  * bf16: products on bf16 MFMA with fp32 accumulation; probabilities are
  * rounded to bf16 before the P V product; output rounded to nearest even.
  */
@@ -201,7 +210,8 @@ int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o,
                            int32_t dtype, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
                            int64_t D, const int64_t strides[4][3],
                            const float* cos_sin, int64_t n_table_rows,
-                           float softmax_scale, int32_t causal, float* lse, void* stream);
+                           float softmax_scale, int32_t causal, float* lse,
+                           void* workspace, void* stream);
 
 /*
  * attn_prefill_sink_window -- attn_prefill_blockwise under the attention-sink
@@ -213,7 +223,8 @@ int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o,
  * skipped, not masked, so the work per query tile is bounded by
  * n_sink + window + the tile, not by t.
  *
- * Arguments as attn_prefill_blockwise, causal implied, plus
+ * Arguments as attn_prefill_blockwise (workspace included), causal
+ * implied, plus
  *   n_sink         >= 0; values above S act as S (every key a sink).
  *   window         >= 1; values above S act as S (plain causal).
  * dtype must be YRB_BF16 (YRB_EUNSUPPORTED otherwise); S < 2^30.
@@ -223,7 +234,7 @@ int attn_prefill_sink_window(const void* q, const void* k, const void* v, void* 
                              int64_t D, const int64_t strides[4][3],
                              const float* cos_sin, int64_t n_table_rows,
                              float softmax_scale, int64_t n_sink, int64_t window,
-                             float* lse, void* stream);
+                             float* lse, void* workspace, void* stream);
 
 /*
  * attn_block_accumulate -- one ring-attention step on one device: fold the
@@ -247,6 +258,8 @@ int attn_prefill_sink_window(const void* q, const void* k, const void* v, void* 
  *   flags          YRB_ACC_FIRST and/or YRB_ACC_FINALIZE.
  *   o_out          device [B][Sq][Hq][D] of dtype, o_strides; required iff
  *                  FINALIZE; rows with l = 0 are written as 0.
+ *   workspace      NULL or YRB_WORKSPACE_BYTES of device memory, as for
+ *                  attn_prefill_blockwise (bf16 only; fp32 ignores it).
  * With causal = 1 a block wholly in the future of every local query
  * (k_offset > q_offset + Sq - 1) contributes nothing ([T] FAQ 2); the call
  * still initialises (FIRST) and finalises (FINALIZE) as asked.  Folding the
@@ -259,7 +272,8 @@ int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk,
                           const float* cos_sin, int64_t n_table_rows,
                           float softmax_scale, int32_t causal,
                           float* o_acc, float* m, float* l, int32_t flags,
-                          void* o_out, const int64_t o_strides[3], void* stream);
+                          void* o_out, const int64_t o_strides[3], void* workspace,
+                          void* stream);
 
 /*
  * attn_decode_sink_window -- one new query per sequence against a cache of

@@ -154,11 +154,12 @@ def _prefill(**over):
     L = api.lib()
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=0, B=1, S=64, Hq=4, Hkv=2, D=128,
              strides=_strides(*([64 * 4 * 128, 4 * 128, 128] * 4)), cs=FAKE, rows=64,
-             scale=0.1, causal=1, lse=None)
+             scale=0.1, causal=1, lse=None, ws=None)
     a.update(over)
     return L.attn_prefill_blockwise(a["q"], a["k"], a["v"], a["o"], a["dtype"], a["B"], a["S"],
                                     a["Hq"], a["Hkv"], a["D"], a["strides"], a["cs"], a["rows"],
-                                    ctypes.c_float(a["scale"]), a["causal"], a["lse"], None)
+                                    ctypes.c_float(a["scale"]), a["causal"], a["lse"], a["ws"],
+                                    None)
 
 
 def test_prefill_validation():
@@ -176,6 +177,7 @@ def test_prefill_validation():
     assert _prefill(strides=_strides(*([64 * 4 * 128, big, 128] + [64 * 4 * 128, 4 * 128, 128] * 3))) == EINVAL
     assert _prefill(strides=_strides(*([64 * 4 * 128, 4 * 128, 128] * 3 + [-128, 4 * 128, 128]))) == EINVAL
     assert _prefill(lse=MISALIGNED) == EALIGN
+    assert _prefill(ws=MISALIGNED) == EALIGN
     assert _prefill(S=0) == OK
     assert _prefill(B=0) == OK
 
@@ -184,12 +186,12 @@ def _prefill_sw(**over):
     L = api.lib()
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=0, B=1, S=64, Hq=4, Hkv=2, D=128,
              strides=_strides(*([64 * 4 * 128, 4 * 128, 128] * 4)), cs=FAKE, rows=64,
-             scale=0.1, sink=4, win=32, lse=None)
+             scale=0.1, sink=4, win=32, lse=None, ws=None)
     a.update(over)
     return L.attn_prefill_sink_window(a["q"], a["k"], a["v"], a["o"], a["dtype"], a["B"], a["S"],
                                       a["Hq"], a["Hkv"], a["D"], a["strides"], a["cs"], a["rows"],
                                       ctypes.c_float(a["scale"]), a["sink"], a["win"], a["lse"],
-                                      None)
+                                      a["ws"], None)
 
 
 def test_prefill_sink_window_validation():
@@ -205,6 +207,7 @@ def test_prefill_sink_window_validation():
     assert _prefill_sw(rows=63) == EINVAL
     assert _prefill_sw(q=None) == EINVAL
     assert _prefill_sw(o=MISALIGNED) == EALIGN
+    assert _prefill_sw(ws=MISALIGNED) == EALIGN
     assert _prefill_sw(S=0) == OK
     assert _prefill_sw(B=0, sink=1 << 40, win=1 << 40) == OK
 
@@ -213,13 +216,13 @@ def _accum(**over):
     L = api.lib()
     a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=0, B=1, Sq=64, Sk=64, Hq=2, Hkv=2, D=64,
              strides=_strides(*([64 * 2 * 64, 2 * 64, 64] * 3)), qo=64, ko=0, cs=FAKE, rows=128,
-             scale=0.1, causal=1, acc=FAKE, m=FAKE, l=FAKE, flags=1, out=None, os=None)
+             scale=0.1, causal=1, acc=FAKE, m=FAKE, l=FAKE, flags=1, out=None, os=None, ws=None)
     a.update(over)
     return L.attn_block_accumulate(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["Sq"], a["Sk"],
                                    a["Hq"], a["Hkv"], a["D"], a["strides"], a["qo"], a["ko"],
                                    a["cs"], a["rows"], ctypes.c_float(a["scale"]),
                                    a["causal"], a["acc"], a["m"], a["l"], a["flags"], a["out"],
-                                   a["os"], None)
+                                   a["os"], a["ws"], None)
 
 
 def test_accumulate_validation():
@@ -232,6 +235,7 @@ def test_accumulate_validation():
     assert _accum(m=None) == EINVAL
     assert _accum(acc=MISALIGNED) == EALIGN
     assert _accum(cs=MISALIGNED) == EALIGN
+    assert _accum(ws=MISALIGNED) == EALIGN
     assert _accum(dtype=2) == EUNSUP
     assert _accum(Sq=0) == OK
 

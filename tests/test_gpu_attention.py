@@ -156,29 +156,88 @@ def test_prefill_deterministic():
 
 @pytest.mark.parametrize("S,Hq,Hkv", [(2000, 4, 4), (1300, 3, 1)])
 def test_prefill_claimed_items_repeated(S, Hq, Hkv):
-    # The last 30 % of the grid claims its work items at run time from
-    # counters that each launch leaves at zero: more launches than counter
-    # slots, each into a NaN-filled output, must all write every row and
-    # agree bit for bit (grids of 32 and 18 blocks).
+    # With a workspace the last 30 % of the grid claims its work items at
+    # run time from a counter there, which each launch leaves as it found
+    # it.  70 launches in a row through one workspace, each into a NaN-filled
+    # output, must all write every row and equal the fixed schedule
+    # (workspace NULL) bit for bit (grids of 32 and 18 blocks).
     require_gpu()
     import torch
     rope = W.Rope(W.YARN, 128, 1e4, 4.0, 128)
     tab, th, scale, (qv, kv, vv), (q, k, v) = _setup(1, S, Hq, Hkv, 128, "bf16", rope, seed_base=9)
     say(f"attn_prefill_blockwise claimed items S={S} Hq={Hq} x70")
     kr = api.rope_apply(k, tab)
-    first = None
+    fixed = api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab)
+    ws = api.new_workspace()
+    torch.cuda.synchronize()
+    assert not torch.isnan(fixed).any()
+    rows = _sample_rows(S, 5, 24)
+    ref = A.prefill(qv, kv, vv, th, scale, rows=rows)
+    assert max_abs(host(fixed[0, rows]), ref[0]) <= BF16_TOL
     for i in range(70):
         o = torch.full_like(q, float("nan"))
-        api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab, out=o)
+        api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab, out=o, workspace=ws)
         torch.cuda.synchronize()
-        if first is None:
-            first = o.clone()
-            assert not torch.isnan(first).any()
-            rows = _sample_rows(S, 5, 24)
-            ref = A.prefill(qv, kv, vv, th, scale, rows=rows)
-            assert max_abs(host(first[0, rows]), ref[0]) <= BF16_TOL
-        else:
-            assert torch.equal(o, first), i
+        assert torch.equal(o, fixed), i
+    assert int(ws.abs().sum()) == 0
+
+
+def test_prefill_claims_from_a_nonzero_counter():
+    # Ticket c stands for claimed item c mod n: whatever the counter holds
+    # when the launch starts, every item is taken once, and the counter ends
+    # at its starting value mod n (n = claims per launch: 32 blocks, the
+    # last 10 claimed, here).
+    require_gpu()
+    import torch
+    S, Hq = 2000, 4
+    rope = W.Rope(W.YARN, 128, 1e4, 4.0, 128)
+    tab, th, scale, _, (q, k, v) = _setup(1, S, Hq, Hq, 128, "bf16", rope, seed_base=19)
+    say("attn_prefill_blockwise claims from a counter holding 1234567")
+    kr = api.rope_apply(k, tab)
+    fixed = api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab)
+    ws = api.new_workspace()
+    ws[0] = 1234567
+    o = torch.full_like(q, float("nan"))
+    api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, fixed)
+    n_blocks = 8 * Hq                      # 256-row query tiles x heads
+    n_claims = n_blocks - n_blocks * 7 // 10
+    assert int(ws[0]) == 1234567 % n_claims
+    assert int(ws[1:].abs().sum()) == 0
+
+
+def test_prefill_two_streams_at_once():
+    # Two streams of default priority, each with its own workspace, run
+    # prefills of different inputs at the same time (nothing orders one
+    # stream's launches against the other's); each result equals the same
+    # call run alone, bit for bit.  The library keeps no state between calls.
+    require_gpu()
+    import torch
+    S, Hq, Hkv = 4096, 8, 8
+    rope = W.Rope(W.YARN, 128, 1e4, 4.0, 1024)
+    tab, th, scale, _, (q1, k1, v1) = _setup(1, S, Hq, Hkv, 128, "bf16", rope, seed_base=120)
+    _, _, _, _, (q2, k2, v2) = _setup(1, S, Hq, Hkv, 128, "bf16", rope, seed_base=130)
+    kr1, kr2 = api.rope_apply(k1, tab), api.rope_apply(k2, tab)
+    say("attn_prefill_blockwise on two streams at once, S=4096 H=8")
+    alone1 = api.attn_prefill_blockwise(q1, kr1, v1, scale, cos_sin=tab)
+    alone2 = api.attn_prefill_blockwise(q2, kr2, v2, scale, cos_sin=tab)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ws1, ws2 = api.new_workspace(), api.new_workspace()
+    outs1 = [torch.full_like(q1, float("nan")) for _ in range(6)]
+    outs2 = [torch.full_like(q2, float("nan")) for _ in range(6)]
+    torch.cuda.synchronize()
+    for i in range(6):
+        with torch.cuda.stream(s1):
+            api.attn_prefill_blockwise(q1, kr1, v1, scale, cos_sin=tab, out=outs1[i], workspace=ws1)
+        with torch.cuda.stream(s2):
+            api.attn_prefill_blockwise(q2, kr2, v2, scale, cos_sin=tab, out=outs2[i], workspace=ws2)
+    torch.cuda.synchronize()
+    for i in range(6):
+        assert torch.equal(outs1[i], alone1), i
+        assert torch.equal(outs2[i], alone2), i
+    assert int(ws1.abs().sum()) == 0 and int(ws2.abs().sum()) == 0
 
 
 def _sample_rows(S, seed, count=40):
@@ -193,7 +252,7 @@ def _check_prefill_rows(w, heads, rows_per_head=40):
     say(f"attn_prefill_blockwise {w.name} full size")
     kr = api.rope_apply(k, tab)
     del k
-    o = api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab)
+    o = api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab, workspace=api.new_workspace())
     torch.cuda.synchronize()
     worst = 0.0
     for h in heads:

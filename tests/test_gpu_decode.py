@@ -40,14 +40,40 @@ def test_decode_full_sink_config():
     o = api.attn_decode_sink_window(q, k, v, lens, w.n_sink, w.window, tab, scale, ring_head=rht)
     torch.cuda.synchronize()
     got = host(o)
-    bs = synth.sample_rows(w.batch, 6, 123, must=[0, w.batch - 1])
-    ref = A.decode_sink_window(qv[bs], kv[bs], vv[bs], th, scale, w.n_sink, w.window,
-                               [C] * len(bs), rh[bs])
-    err = max_abs(got[bs], ref)
+    ref = A.decode_sink_window(qv, kv, vv, th, scale, w.n_sink, w.window, [C] * w.batch, rh)
+    err = max_abs(got, ref)
     assert err <= BF16_TOL, err
 
 
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("cache", ["bf16", "e4m3"])
+def test_decode_full_gqa_config(cache):
+    # The decode workload with grouped-query heads: 64 sequences x 32 query
+    # heads over 8 key/value heads (4 per group), 4 sinks + 4096 window, every
+    # sequence checked.
+    require_gpu()
+    import torch
+    w = W.SINK_DECODE
+    C = w.n_sink + w.window
+    Hq, Hkv = 32, 8
+    rh = synth.ring_heads(w.batch, w.window, seed_base=10)
+    if cache == "bf16":
+        tab, th, scale, (qv, kv, vv), (q, k, v), lens, rht = _case(
+            w.batch, Hq, Hkv, w.head_dim, w.n_sink, w.window, [C] * w.batch, rh, w.rope, seed=20)
+        ks = vs = None
+    else:
+        tab, th, scale, (qv, kv, vv), q, dv = _fp8_case(
+            w.batch, Hq, Hkv, w.head_dim, w.n_sink, w.window, [C] * w.batch, rh, w.rope, seed=24)
+        k, v, ks, vs, lens, rht = dv["k"], dv["v"], dv["ks"], dv["vs"], dv["lens"], dv["rh"]
+    say(f"attn_decode_sink_window_ex {cache} B=64 Hq=32 Hkv=8 C=4100 full size")
+    o = api.attn_decode_sink_window_ex(q, k, v, lens, w.n_sink, w.window, tab, scale,
+                                       ring_head=rht, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    ref = A.decode_sink_window(qv, kv, vv, th, scale, w.n_sink, w.window, [C] * w.batch, rh)
+    err = max_abs(host(o), ref)
+    assert err <= BF16_TOL, err
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("D", [64, 128])
 def test_decode_edge_cases(G, D):
     # len 0, len inside the sinks, a partly filled window, a full window with
@@ -162,14 +188,12 @@ def test_decode_fp8_full_sink_config():
                                         v_scale=dv["vs"])
     torch.cuda.synchronize()
     got = host(o)
-    bs = synth.sample_rows(w.batch, 6, 321, must=[0, w.batch - 1])
-    ref = A.decode_sink_window(qv[bs], kv[bs], vv[bs], th, scale, w.n_sink, w.window,
-                               [C] * len(bs), rh[bs])
-    err = max_abs(got[bs], ref)
+    ref = A.decode_sink_window(qv, kv, vv, th, scale, w.n_sink, w.window, [C] * w.batch, rh)
+    err = max_abs(got, ref)
     assert err <= BF16_TOL, err
 
 
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("D", [64, 128])
 def test_decode_fp8_edge_cases(G, D):
     # The same lengths and ring heads as the bf16 edge cases, every sequence
@@ -220,7 +244,7 @@ def test_decode_fp8_nan_code_reaches_output():
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("G,D", [(1, 128), (4, 64)])
+@pytest.mark.parametrize("G,D", [(1, 128), (2, 64), (4, 64), (8, 128)])
 def test_decode_interleaved_layout(fp8, G, D):
     # Keys and the query rotated in the interleaved pair layout, bf16 or E4M3
     # cache, through attn_decode_sink_window_ex; lengths and ring heads as in

@@ -20,6 +20,7 @@ PLAIN, PI, NTK, YARN = 0, 1, 2, 3
 BF16, F32, FP8_E4M3 = 0, 1, 2
 LAYOUT_HALF, LAYOUT_INTERLEAVED = 0, 1
 ACC_FIRST, ACC_FINALIZE = 1, 2
+WORKSPACE_BYTES = 64      # YRB_WORKSPACE_BYTES
 EXPORTS = ("rope_tables_build", "rope_tables_build_factors", "rope_apply", "attn_prefill_blockwise",
            "attn_prefill_sink_window",
            "attn_block_accumulate", "attn_decode_sink_window", "attn_decode_sink_window_fp8",
@@ -90,13 +91,13 @@ def lib() -> ctypes.CDLL:
                                  _i64, _vp, _vp]
         L.attn_prefill_blockwise.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64,
                                              _i64, _i64p, _vp, _i64, ctypes.c_float, _i32, _vp,
-                                             _vp]
+                                             _vp, _vp]
         L.attn_prefill_sink_window.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64,
                                                _i64, _i64p, _vp, _i64, ctypes.c_float, _i64, _i64,
-                                               _vp, _vp]
+                                               _vp, _vp, _vp]
         L.attn_block_accumulate.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64,
                                             _i64, _i64p, _i64, _i64, _vp, _i64, ctypes.c_float,
-                                            _i32, _vp, _vp, _vp, _i32, _vp, _i64p, _vp]
+                                            _i32, _vp, _vp, _vp, _i32, _vp, _i64p, _vp, _vp]
         L.attn_decode_sink_window.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64,
                                               _i64, _i64, _i64p, _i64p, _i64p, _vp, _vp, _vp,
                                               _i64, ctypes.c_float, _vp]
@@ -235,11 +236,21 @@ def rope_apply(x, cos_sin, pos_offset: int = 0, pos_ids=None, out=None):
 # attn_prefill_blockwise
 # ----------------------------------------------------------------------------
 
+def new_workspace(device="cuda"):
+    """A zeroed workspace for the prefill calls and attn_block_accumulate.
+    One serves any number of calls in sequence on a stream; calls that may
+    run at the same time need one each."""
+    import torch
+    return torch.zeros(WORKSPACE_BYTES // 4, dtype=torch.int32, device=device)
+
+
 def attn_prefill_blockwise(q, k, v, softmax_scale: float, cos_sin=None, causal: bool = True,
-                           out=None, lse=None):
+                           out=None, lse=None, workspace=None):
     """Causal (or full) attention, q rotated on load when ``cos_sin`` is given.
 
     q [B,S,Hq,D] (raw), k [B,S,Hkv,D] already rotated (rope_apply), v [B,S,Hkv,D].
+    ``workspace`` (new_workspace()) lets the grid balance its last items at
+    run time; None takes a fixed schedule with the same results.
     """
     import torch
     B, S, Hq, D = q.shape
@@ -250,12 +261,13 @@ def attn_prefill_blockwise(q, k, v, softmax_scale: float, cos_sin=None, causal: 
     n_rows = 0 if cos_sin is None else cos_sin.shape[0]
     _check("attn_prefill_blockwise", lib().attn_prefill_blockwise(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), B, S, Hq, Hkv, D, strides,
-        _ptr(cos_sin), n_rows, float(softmax_scale), int(bool(causal)), _ptr(lse), _stream()))
+        _ptr(cos_sin), n_rows, float(softmax_scale), int(bool(causal)), _ptr(lse),
+        _ptr(workspace), _stream()))
     return out
 
 
 def attn_prefill_sink_window(q, k, v, softmax_scale: float, n_sink: int, window: int,
-                             cos_sin=None, out=None, lse=None):
+                             cos_sin=None, out=None, lse=None, workspace=None):
     """attn_prefill_blockwise under the sink+window mask: key n is visible to
     query t iff n <= t and (n < n_sink or n > t - window); bf16 only."""
     import torch
@@ -268,7 +280,7 @@ def attn_prefill_sink_window(q, k, v, softmax_scale: float, n_sink: int, window:
     _check("attn_prefill_sink_window", lib().attn_prefill_sink_window(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), B, S, Hq, Hkv, D, strides,
         _ptr(cos_sin), n_rows, float(softmax_scale), int(n_sink), int(window), _ptr(lse),
-        _stream()))
+        _ptr(workspace), _stream()))
     return out
 
 
@@ -293,7 +305,8 @@ class AccState:
 
 def attn_block_accumulate(q, k_blk, v_blk, state: AccState, q_offset: int, k_offset: int,
                           softmax_scale: float, cos_sin=None, causal: bool = True,
-                          first: bool = False, finalize: bool = False, out=None):
+                          first: bool = False, finalize: bool = False, out=None,
+                          workspace=None):
     """Fold one (already rotated) key/value block into the state; q is rotated
     on load when ``cos_sin`` is given.  Returns ``out`` when finalizing."""
     import torch
@@ -307,8 +320,9 @@ def attn_block_accumulate(q, k_blk, v_blk, state: AccState, q_offset: int, k_off
     n_rows = 0 if cos_sin is None else cos_sin.shape[0]
     _check("attn_block_accumulate", lib().attn_block_accumulate(
         _ptr(q), _ptr(k_blk), _ptr(v_blk), _dtype_code(q), B, Sq, Sk, Hq, Hkv, D, strides,
-        q_offset, k_offset, _ptr(cos_sin), n_rows, float(softmax_scale), int(bool(causal)), _ptr(state.o_acc), _ptr(state.m), _ptr(state.l), flags, _ptr(out),
-        o_str, _stream()))
+        q_offset, k_offset, _ptr(cos_sin), n_rows, float(softmax_scale), int(bool(causal)),
+        _ptr(state.o_acc), _ptr(state.m), _ptr(state.l), flags, _ptr(out), o_str,
+        _ptr(workspace), _stream()))
     return out
 
 

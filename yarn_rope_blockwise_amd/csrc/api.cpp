@@ -1,8 +1,9 @@
 // C ABI of libyrb: argument validation on the host, then kernel launches.
 // Declarations and the contract of each call are in include/yrb.h.
 //
-// Nothing here allocates, synchronises or keeps state.  Every check runs
-// before the first launch, so an error return means nothing was queued.
+// Nothing here allocates, synchronises or keeps state between calls.  Every
+// check runs before the first launch, so an error return means nothing was
+// queued.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -198,7 +199,7 @@ namespace {
 int prefill_common(const void* q, const void* k, const void* v, void* o, int32_t dtype, int64_t B, int64_t S,
                    int64_t Hq, int64_t Hkv, int64_t D, const int64_t strides[4][3], const float* cos_sin,
                    int64_t n_table_rows, float softmax_scale, int32_t causal, int64_t n_sink, int64_t window,
-                   float* lse, void* stream) {
+                   float* lse, void* workspace, void* stream) {
   if (!dtype_ok(dtype)) return YRB_EUNSUPPORTED;
   if (!dim_ok(D)) return YRB_EUNSUPPORTED;
   if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return YRB_EINVAL;
@@ -211,7 +212,8 @@ int prefill_common(const void* q, const void* k, const void* v, void* o, int32_t
     if (!strides_nonneg(strides[t], 3)) return YRB_EINVAL;
     if (!strides_aligned(strides[t], 3, dtype)) return YRB_EALIGN;
   }
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(workspace))
     return YRB_EALIGN;
   if (S >= (int64_t(1) << 31)) return YRB_EINVAL;
   if (cos_sin) {
@@ -244,6 +246,7 @@ int prefill_common(const void* q, const void* k, const void* v, void* o, int32_t
   a.load_state = 0;
   a.store_state = 0;
   a.finalize = 1;
+  a.claims = static_cast<unsigned*>(workspace);
   if (window > 0) {
     a.n_sink = (int)n_sink;
     a.window = (int)window;
@@ -258,23 +261,24 @@ int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o,
                            int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
                            const int64_t strides[4][3], const float* cos_sin,
                            int64_t n_table_rows, float softmax_scale, int32_t causal, float* lse,
-                           void* stream) {
+                           void* workspace, void* stream) {
   return prefill_common(q, k, v, o, dtype, B, S, Hq, Hkv, D, strides, cos_sin, n_table_rows, softmax_scale,
-                        causal, 0, 0, lse, stream);
+                        causal, 0, 0, lse, workspace, stream);
 }
 
 int attn_prefill_sink_window(const void* q, const void* k, const void* v, void* o, int32_t dtype,
                              int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
                              const int64_t strides[4][3], const float* cos_sin, int64_t n_table_rows,
                              float softmax_scale, int64_t n_sink, int64_t window, float* lse,
-                             void* stream) {
+                             void* workspace, void* stream) {
   if (dtype != YRB_BF16) return YRB_EUNSUPPORTED;
   if (n_sink < 0 || window < 1) return YRB_EINVAL;
   if (S >= (int64_t(1) << 30)) return YRB_EINVAL;
   // A window of S or more reaches every earlier key: plain causal.  Sinks
   // past S are all the keys there are.
   return prefill_common(q, k, v, o, dtype, B, S, Hq, Hkv, D, strides, cos_sin, n_table_rows, softmax_scale,
-                        1, std::min(n_sink, S), std::min(window, std::max<int64_t>(S, 1)), lse, stream);
+                        1, std::min(n_sink, S), std::min(window, std::max<int64_t>(S, 1)), lse, workspace,
+                        stream);
 }
 
 int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk, int32_t dtype,
@@ -282,7 +286,8 @@ int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk, i
                           const int64_t strides[3][3], int64_t q_offset, int64_t k_offset,
                           const float* cos_sin, int64_t n_table_rows, float softmax_scale,
                           int32_t causal, float* o_acc, float* m, float* l,
-                          int32_t flags, void* o_out, const int64_t o_strides[3], void* stream) {
+                          int32_t flags, void* o_out, const int64_t o_strides[3], void* workspace,
+                          void* stream) {
   if (!dtype_ok(dtype)) return YRB_EUNSUPPORTED;
   if (!dim_ok(D)) return YRB_EUNSUPPORTED;
   if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return YRB_EINVAL;
@@ -304,7 +309,7 @@ int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk, i
   if (fin && (!strides_nonneg(o_strides, 3))) return YRB_EINVAL;
   if (fin && !strides_aligned(o_strides, 3, dtype)) return YRB_EALIGN;
   if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o_acc) ||
-      !aligned16(o_out))
+      !aligned16(o_out) || !aligned16(workspace))
     return YRB_EALIGN;
   const int64_t lim = int64_t(1) << 31;
   if (q_offset + Sq >= lim || k_offset + Sk >= lim) return YRB_EINVAL;
@@ -342,6 +347,7 @@ int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk, i
   a.load_state = (flags & YRB_ACC_FIRST) ? 0 : 1;
   a.store_state = 1;
   a.finalize = fin ? 1 : 0;
+  a.claims = static_cast<unsigned*>(workspace);
   return hip_status(yrb::launch_attention(dtype, (int)D, a, s));
 }
 

@@ -42,8 +42,9 @@
 //  * Set-up per workgroup: the first two key tiles, the query rows' table
 //    rows (by LDS-DMA, coalesced, into buffers still free) and Q go out
 //    together, and Q is rotated from the table in fp32.  Work items run
-//    heaviest first; the last part of the grid claims its items from a
-//    counter so that XCDs running at different clocks finish together.
+//    heaviest first; given a counter in caller memory, the last part of the
+//    grid claims its items from it so that XCDs running at different clocks
+//    finish together.
 //  * A template flag adds the attention-sink plus sliding-window mask of
 //    the 14cs17 notes ("Sliding Window + Attention Sinks") on top of the
 //    causal rule: the pipeline walks the sink tiles, then only the tiles
@@ -53,7 +54,6 @@
 #include "common.h"
 #include "kernels.h"
 
-#include <atomic>
 #include <type_traits>
 
 namespace yrb {
@@ -67,38 +67,36 @@ constexpr int kPPBufs = 4;     // LDS tile buffers (the tile loop is unrolled by
 // MFMAs of the steps before it need no LDS and run while the waves meet.
 constexpr int kArriveStep = 2;
 
-// Work items of the last 30 % of the grid are claimed at run time.  Blocks
-// go round robin over the 8 XCDs and each XCD runs its share at its own
-// clock, which under load differs from XCD to XCD by a few percent: with a
-// fixed item per block the slowest XCD finishes last while the others idle.
-// A block from claim_from on takes the next item of a counter instead, so an
-// XCD that runs ahead takes the heavier items (they come first).  The counter
-// of a launch is one of kClaimSlots, taken in turn by successive launches;
-// the block that claims the launch's last item sets it back to zero.
-// Launches that run at the same time on one GPU must not share a slot (more
-// than kClaimSlots launches apart, or a captured graph replayed on two
-// streams at once).
-constexpr int kClaimSlots = 64;
+// Work items of the last 30 % of the grid may be claimed at run time.
+// Blocks go round robin over the 8 XCDs and each XCD runs its share at its
+// own clock, which under load differs from XCD to XCD by a few percent: with
+// a fixed item per block the slowest XCD finishes last while the others
+// idle.  Given a counter in caller memory, a block from claim_from on takes
+// the next ticket instead, so an XCD that runs ahead takes the heavier items
+// (they come first).  Without a counter every block takes its own item.
 constexpr int kClaimMinBlocks = 16;   // smaller grids take every item statically
-struct ClaimSlot {
-  unsigned next;      // items claimed so far
-  unsigned pad[15];   // one 64-byte line per slot
-};
-__device__ ClaimSlot g_claims[kClaimSlots];
 
 // Source of the placeholder DMA when the fast path is off: 16 lane + n KiB
 // stays inside it.
 __device__ __attribute__((aligned(1024))) unsigned char g_dma_dummy[4096];
 
-// The item of this block: blockIdx.x below claim_from, else claimed.
-__device__ __forceinline__ int claim_item(int claim_from, unsigned slot, YRB_LDS int* cell) {
+// The item of this block: blockIdx.x below claim_from, else claimed from
+// the counter `ctr`.  The n = gridDim.x - claim_from claims of a launch take
+// n consecutive tickets, and ticket c stands for item claim_from + c mod n:
+// n consecutive integers cover every residue once, so every item is taken
+// exactly once whatever the counter held.  The block whose ticket completes
+// a multiple of n takes that multiple back off the counter, which keeps the
+// residues of the tickets still to come and leaves the counter, once the
+// launch's claims are made, at its starting value mod n: a counter that
+// starts at zero ends at zero.
+__device__ __forceinline__ int claim_item(int claim_from, unsigned* ctr, YRB_LDS int* cell) {
   if ((int)blockIdx.x < claim_from) return (int)blockIdx.x;
   if (threadIdx.x == 0) {
-    unsigned* next = &g_claims[slot].next;
-    const unsigned c = __hip_atomic_fetch_add(next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((int)c == (int)gridDim.x - claim_from - 1)   // every claim of the launch is made
-      __hip_atomic_store(next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *cell = claim_from + (int)c;
+    const unsigned n = gridDim.x - (unsigned)claim_from;
+    const unsigned c = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned r = c % n;
+    if (r == n - 1) __hip_atomic_fetch_sub(ctr, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *cell = claim_from + (int)r;
   }
   __syncthreads();
   return __builtin_amdgcn_readfirstlane(*cell);
@@ -611,8 +609,8 @@ __device__ __forceinline__ void table_from_lds(const YRB_LDS char* region, int l
 // is that max); without it the grow test is the sum test and the output and
 // log-sum-exp use the reference in use, which gives the same values.
 template <int D, bool EXACT, bool WIN>
-__global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs a, int64_t n_qtiles, int claim_from,
-                                                                         unsigned claim_slot) {
+__global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs a, int64_t n_qtiles,
+                                                                         int claim_from) {
   constexpr int NW = kPPWaves, BN = kPPBN, QW = 64, BM = NW * QW;
   constexpr int NDS = D / 16, NDT = D / 32;
   using T = Tile<D, BN>;
@@ -637,7 +635,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
                "s"(a.Hkv), "s"(a.qs[0]), "s"(a.ks[0]), "s"(a.vs[0]));
   // (The claim's LDS cell is in the spare region, which no DMA reaches
   // before the first tile's barrier.)
-  const int item = claim_item(claim_from, claim_slot, (YRB_LDS int*)(lds + 2 * kPPBufs * T::TILEB));
+  const int item = claim_item(claim_from, a.claims, (YRB_LDS int*)(lds + 2 * kPPBufs * T::TILEB));
   const WorkItem wi = work_item_at(a, n_qtiles, item);
   const int b = wi.b, h = wi.h, hk = wi.hk, qtile = wi.qtile;
   const int q0w = qtile * BM + wave * QW;
@@ -937,11 +935,9 @@ hipError_t launch_pp_as(const AttnArgs& a, hipStream_t stream) {
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (attr != hipSuccess) return attr;
   }
-  static std::atomic<unsigned> next_slot{0};
-  const unsigned slot = next_slot.fetch_add(1, std::memory_order_relaxed) % kClaimSlots;
-  const int claim_from = blocks >= kClaimMinBlocks ? (int)(blocks * 7 / 10) : (int)blocks;
+  const int claim_from = (a.claims && blocks >= kClaimMinBlocks) ? (int)(blocks * 7 / 10) : (int)blocks;
   hipLaunchKernelGGL((attn_bf16_pp_kernel<D, EXACT, WIN>), dim3((unsigned)blocks), dim3(kPPWaves * 64), LDS_BYTES,
-                     stream, a, n_qtiles, claim_from, slot);
+                     stream, a, n_qtiles, claim_from);
   return hipGetLastError();
 }
 

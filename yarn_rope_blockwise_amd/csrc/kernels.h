@@ -51,6 +51,9 @@ struct AttnArgs {
   // n > t - window, on top of the causal rule.
   int n_sink;
   int window;
+  // Work-claim counter in caller memory (bf16 pipelined kernel), or null:
+  // every block then takes the work item of its index.
+  unsigned* claims;
 };
 hipError_t launch_attention(int dtype, int D, const AttnArgs& a, hipStream_t stream);
 // The software-pipelined bf16 kernel (attn_pp.hip); called by launch_attention.
