@@ -31,7 +31,8 @@ def _qkv(B, S, Hq, Hkv, D, pattern, seed):
     qv, qb = synth.normal((B, S, Hq, D), seed, "bf16")
     k0, _ = synth.normal((B, S, Hkv, D), seed + 1, "bf16")
     kv, kb = SI.scaled_bf16(k0, SI.quarter_multipliers(S, pattern), axis=1)
-    vv, vb = synth.normal((B, S, Hkv, D), seed + 2, "bf16")
+    v0, _ = synth.normal((B, S, Hkv, D), seed + 2, "bf16")
+    vv, vb = SI.scaled_bf16(v0, np.full(S, SI.V_SCALE), axis=1)
     return (qv, kv, vv), (qb, kb, vb)
 
 
@@ -123,7 +124,8 @@ def test_accumulate_rescale_forced_in_later_calls(D):
     qv, qb = synth.normal((1, blk, Hq, D), 400 + D, "bf16")
     k0, _ = synth.normal((1, S, Hkv, D), 401 + D, "bf16")
     kv, kb = SI.scaled_bf16(k0, np.repeat([mult_of_block[j] for j in range(nb)], blk), axis=1)
-    vv, vb = synth.normal((1, S, Hkv, D), 402 + D, "bf16")
+    v0, _ = synth.normal((1, S, Hkv, D), 402 + D, "bf16")
+    vv, vb = SI.scaled_bf16(v0, np.full(S, SI.V_SCALE), axis=1)
     scale = SI.SCALE_EXACT
     order = [3, 2, 1, 0]
     qpos = qi * blk + np.arange(blk)

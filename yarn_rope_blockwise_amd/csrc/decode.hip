@@ -10,21 +10,32 @@
 // at position len - 1.
 //
 // gfx950 design: the call is HBM-bound (every cached K and V byte is read
-// once, ~1 flop per byte), so the kernel is a streaming reduction.
-//  * One workgroup (4 waves) per (sequence, 4 key/value heads): wave w owns
-//    head 4g + w and the G query heads that share it.  All four waves walk
-//    the same slots in memory order, so the cos/sin row of each slot's
-//    position is fetched once per workgroup into LDS and shared (fetching
-//    it per head costs as many bytes as K and V together).
-//  * D/16 lanes share one key row: each lane reads the two 16-byte chunks
-//    holding pairs (i, i + d/2) for its 8 pairs, so the rotation is
-//    lane-local.  Each step a wave holds 4 rounds of K/V loads in flight,
-//    and the next step's loads are issued before this step is reduced
-//    (non-temporal: the cache is far larger than the L2/MALL).
-//  * The score of a rotated key is  sum_i c_i (q_i k_i + q_j k_j) +
-//    s_i (q_j k_i - q_i k_j), j = i + d/2.
-//  * Online softmax per wave in the exp2 domain; lanes of one head then
-//    combine their partial sums with cross-lane shuffles.
+// once, about one flop per byte), so the kernel is a streaming reduction
+// whose waves run independently.
+//  * A wave owns one (sequence, key/value head) and a range of its cache
+//    entries, walked by position in steps of KPS = 32 (entry e = A + j,
+//    A a multiple of 32, j < 32).  A head's entries may be split over
+//    `parts` waves of one workgroup (the host picks parts so that caches
+//    with few key/value heads still fill the chip); the parts' running
+//    (max, sum, output) merge through LDS at the end.
+//  * D/16 lanes share one key: each lane reads the two chunks holding
+//    pairs (i, i + d/2) for its 8 pairs (or, interleaved, adjacent pairs
+//    from the same two chunks), so the rotation is lane-local.  Loads are
+//    non-temporal (the cache is far larger than L2 and MALL), issued a
+//    step ahead.
+//  * Rotation by angle addition: R(A + j) = R(A) R(j).  The 32 rows R(j),
+//    j < 32, sit in LDS for the whole launch (read from the caller's table,
+//    XOR-swizzled so that the lanes of a read hit distinct banks), and
+//    only R(A), one table row per step, comes from L2.  With one or two
+//    query heads per key head the step instead re-anchors the query:
+//    q'.k' = (R(len-1-A) q) . (R(j) k), since R(a)^T R(b) = R(b - a);
+//    with more, it forms R(A + j) per key, once for all the key's heads.
+//    Reading a table row per key and head would move as many bytes as K
+//    and V together.
+//  * Online softmax per wave in the exp2 domain, with the reference max
+//    moved only when a step's max passes it by more than 8 (the same
+//    result in exact arithmetic, P <= 2^8); lanes of one head combine their
+//    partial sums with cross-lane shuffles at the end.
 #include "common.h"
 #include "kernels.h"
 
@@ -32,24 +43,23 @@ namespace yrb {
 
 namespace {
 
-constexpr int kWaves = 4;      // = key/value heads per workgroup
+constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kKPS = 32;         // cache positions per step
+constexpr float kDecTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
-// Cache element: bf16 (two 16-byte chunks of 8 values per lane and key) or
-// fp8 E4M3 (OCP; two 8-byte chunks).
+// Cache element: bf16 (a 16-byte chunk holds 8 values) or fp8 E4M3 (OCP; an
+// 8-byte chunk holds 8 codes).  A lane reads two chunks per key for K and
+// two for V.
 template <bool FP8>
 struct CacheType {
   using Chunk = u32x4;
   using Elem = __bf16;
-  static constexpr int kRounds = 4;   // key rounds per wave per step
   __device__ static void unpack(const Chunk& w, float (&f)[8]) { unpack8(w, f); }
 };
 template <>
 struct CacheType<true> {
   using Chunk = u32x2;
   using Elem = uint8_t;
-  // Four rounds, as for bf16: six measured the same and eight lost a wave
-  // per SIMD to registers (0.72 ms against 0.47 ms at 64 x 32 x 4100).
-  static constexpr int kRounds = 4;
   // v_cvt_pk_f32_fp8 decodes two bytes of a dword; on gfx950 its fp8 is the
   // OCP E4M3 format (checked against a host decoder for all 256 codes).
   __device__ static void unpack(const Chunk& w, float (&f)[8]) {
@@ -65,24 +75,47 @@ struct CacheType<true> {
   }
 };
 
-// Key rounds per wave per step: the cache type's, halved for a bf16 cache
-// with 8 query heads per key head, whose per-head query and output
-// registers leave too few for four rounds of 16-byte chunks (it spilled).
-template <bool FP8, int G>
-constexpr int rounds_of() { return (!FP8 && G >= 8) ? 2 : CacheType<FP8>::kRounds; }
-
-// K/V of one step for one lane: R keys, two chunks each.
-template <bool FP8, int R>
-struct KVChunk {
-  typename CacheType<FP8>::Chunk klo[R], khi[R], vlo[R], vhi[R];
-  bool ok[R];
+template <int D, int G>
+struct DecCfg {
+  static constexpr int TPK = D / 16;                 // lanes per key (8 pairs each)
+  static constexpr int KPW = 64 / TPK;               // keys per round
+  static constexpr int ROUNDS = kKPS / KPW;          // rounds per step of 32 positions
+  static constexpr int RPG = 16 / TPK;               // key rows per 16 lanes of an LDS read
+  static constexpr int LOG_RPG = RPG == 2 ? 1 : 2;
+  static constexpr int TROWB = 4 * D;                // bytes of a table row (d/2 pairs of (cos, sin))
+  static constexpr int TABB = 2 * kKPS * TROWB;      // LDS bytes of R(j) and R(32 j), j < 32
+  static constexpr bool ANCHOR_Q = G <= 2;           // re-anchor the query, else compose R(e) per key
+  // Rounds of K/V loads in flight (register sets of the ring): fewer when
+  // the per-head query and output registers leave less room.
+  static constexpr int PD = G <= 2 ? 4 : 2;
+  // Waves per SIMD the registers are sized for.
+  static constexpr int WAVES_PER_EU = G <= 4 ? 2 : 1;
+  static_assert(ROUNDS * KPW == kKPS, "a step is whole rounds");
+  static_assert(ROUNDS % PD == 0 || PD % ROUNDS == 0, "ring sets repeat within a step pair");
 };
 
+// 16-byte chunk k (2 pairs) of LDS table row j sits at chunk k ^ h(j, k):
+// within each 16 lanes of a ds_read_b128 (RPG key rows, 16/RPG lanes each,
+// every lane at its own chunk) the chunks land on 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int tab_phys(int j, int k) {
+  using C = DecCfg<D, 1>;
+  return k ^ ((j & (C::RPG - 1)) | (((k >> 4) & 1) << C::LOG_RPG));
+}
+
+// Chunk index (within a table row) of a lane's pair couple w < 4 (its pairs
+// 2w, 2w+1): half-split, pairs 8cc .. 8cc+7; interleaved (IL), pairs
+// 4cc .. 4cc+3 then d/4 + 4cc .. +3.
+template <int D, bool IL>
+__device__ __forceinline__ int tab_chunk(int cc, int w) {
+  if constexpr (!IL) return 4 * cc + w;
+  return w < 2 ? 2 * cc + w : D / 8 + 2 * cc + (w - 2);
+}
+
 // The 8 pairs of one lane from its two chunks a, b (8 values each, at
-// elements 8cc and d/2 + 8cc in either layout): half-split, pairs
-// 8cc .. 8cc+7 with a the first elements and b their partners; interleaved
-// (IL), a holds pairs 4cc .. 4cc+3 and b pairs d/4 + 4cc .. +3, each pair
-// two adjacent values.
+// elements 8cc and d/2 + 8cc in either layout): half-split, a the first
+// elements and b their partners; interleaved, a holds pairs 4cc .. 4cc+3
+// and b pairs d/4 + 4cc .. +3, each pair two adjacent values.
 template <bool IL>
 __device__ __forceinline__ void pairs_of(const float (&a)[8], const float (&b)[8], float (&x)[8],
                                          float (&z)[8]) {
@@ -91,38 +124,93 @@ __device__ __forceinline__ void pairs_of(const float (&a)[8], const float (&b)[8
     if constexpr (IL) {
       x[u] = u < 4 ? a[2 * u] : b[2 * u - 8];
       z[u] = u < 4 ? a[2 * u + 1] : b[2 * u - 7];
-    } else {   // half-split
+    } else {
       x[u] = a[u];
       z[u] = b[u];
     }
   }
 }
 
+// (cos, sin) of the lane's 8 pairs: from a table row in global memory, or
+// from LDS row j (swizzled).
+template <int D, bool IL>
+__device__ __forceinline__ void row_pairs(const float* row, int cc, float (&c)[8], float (&s)[8]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(row + 4 * tab_chunk<D, IL>(cc, w));
+    c[2 * w] = t[0];
+    s[2 * w] = t[1];
+    c[2 * w + 1] = t[2];
+    s[2 * w + 1] = t[3];
+  }
+}
+template <int D, bool IL>
+__device__ __forceinline__ void lds_pairs(const YRB_LDS char* tab, int j, int cc, float (&c)[8], float (&s)[8]) {
+  const YRB_LDS char* row = tab + j * DecCfg<D, 1>::TROWB;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f32x4 t = *reinterpret_cast<const YRB_LDS f32x4*>(row + 16 * tab_phys<D>(j, tab_chunk<D, IL>(cc, w)));
+    c[2 * w] = t[0];
+    s[2 * w] = t[1];
+    c[2 * w + 1] = t[2];
+    s[2 * w + 1] = t[3];
+  }
+}
+
+// Pair rotations: by the angle (c, s), by its negative (the transpose), and
+// the sum of two angles.
+__device__ __forceinline__ void rot(float& x, float& z, float c, float s) {
+  const float x0 = x;
+  x = x0 * c - z * s;
+  z = x0 * s + z * c;
+}
+__device__ __forceinline__ void rot_t(float& x, float& z, float c, float s) {
+  const float x0 = x;
+  x = x0 * c + z * s;
+  z = z * c - x0 * s;
+}
+__device__ __forceinline__ void add_angle(float& c, float& s, float c2, float s2) {
+  const float c0 = c;
+  c = c0 * c2 - s * s2;
+  s = s * c2 + c0 * s2;
+}
+
+// K/V chunks of one round for one lane, and whether its key counts.
+template <bool FP8>
+struct KVRound {
+  typename CacheType<FP8>::Chunk klo, khi, vlo, vhi;
+  bool ok;
+};
+
 template <int D, int G, bool FP8, bool IL>
-__global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(DecCfg<D, G>::WAVES_PER_EU)))
+void decode_kernel(DecodeArgs a, int parts) {
   using CT = CacheType<FP8>;
   using Chunk = typename CT::Chunk;
   using Elem = typename CT::Elem;
-  constexpr int kRounds = rounds_of<FP8, G>();
-  using KV = KVChunk<FP8, kRounds>;
-  constexpr int TPK = D / 16;              // lanes per key row
-  constexpr int KPW = 64 / TPK;            // keys per wave per round
-  constexpr int KPS = KPW * kRounds;       // slots per step (shared by the 4 waves)
-  constexpr int TROWB = 4 * D;             // bytes of one table row: D/2 pairs x (cos, sin)
-  constexpr int TABB = KPS * TROWB;        // table bytes per step
-  constexpr int TCH = TABB / 16 / (kWaves * 64);   // 16-byte table chunks per thread per step
-  static_assert(TCH * 16 * kWaves * 64 == TABB, "table tile must split over the threads");
-  __shared__ __attribute__((aligned(16))) char tab_raw[2 * TABB];
-  YRB_LDS char* const tab0 = (YRB_LDS char*)tab_raw;
-  YRB_LDS char* const tab1 = tab0 + TABB;
+  using Cfg = DecCfg<D, G>;
+  constexpr int TPK = Cfg::TPK, KPW = Cfg::KPW, ROUNDS = Cfg::ROUNDS, PD = Cfg::PD;
+  constexpr int MERGE_F = G * (D + 2);               // floats a wave leaves for the merge
+  // Steps per pass of the loop: the ring's set of a round is then known at
+  // compile time.
+  constexpr int U = PD > ROUNDS ? PD / ROUNDS : 1;
+  using KV = KVRound<FP8>;
+
+  // LDS rows 0..31: R(j); rows 32..63: R(32 j); then one row per wave for
+  // its current R(1024 a).
+  __shared__ __attribute__((aligned(16))) char tab_raw[Cfg::TABB + kWaves * Cfg::TROWB];
+  __shared__ __attribute__((aligned(16))) float merge[kWaves][MERGE_F];
+  YRB_LDS char* const tab = (YRB_LDS char*)tab_raw;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kg = lane / TPK;               // key within the round
   const int cc = lane % TPK;               // chunk: pairs 8cc .. 8cc+7
-  const int n_groups = (int)((a.Hkv + kWaves - 1) / kWaves);
+  const int heads_per_wg = kWaves / parts;
+  const int n_groups = (int)((a.Hkv + heads_per_wg - 1) / heads_per_wg);
   const int64_t b = blockIdx.x / n_groups;
-  const int hk_raw = (int)(blockIdx.x % n_groups) * kWaves + wave;
+  const int hk_raw = (int)(blockIdx.x % n_groups) * heads_per_wg + wave / parts;
+  const int part = wave % parts;
   const bool head_live = hk_raw < a.Hkv;
   const int hk = head_live ? hk_raw : (int)a.Hkv - 1;   // idle waves read a valid head
   const int C = (int)(a.n_sink + a.window);
@@ -134,42 +222,35 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
   const int len = bad_seq ? 0 : len_raw;
   const int rh = bad_seq ? 0 : rh_raw;
 
-  // Position of the entry in `slot`, or -1 when the slot holds none.  A
-  // window slot below C is less than `window` past n_sink and the head is
-  // below `window`, so one conditional add takes the offset mod window, with
-  // no integer division.
-  auto position = [&](int slot) -> int {
-    const int d = slot - n_sink - rh;
-    const int e = slot < n_sink ? slot : n_sink + (d < 0 ? d + window : d);
-    return (slot < C && e < len) ? e : -1;
-  };
+  // R(j) and R(32 j), j < 32, into LDS (rows past the cache are never used:
+  // clamped).
+  for (int idx = threadIdx.x; idx < 2 * kKPS * (D / 4); idx += kWaves * 64) {
+    const int j = idx / (D / 4), k = idx % (D / 4);
+    const int pos = j < kKPS ? j : kKPS * (j - kKPS);
+    const f32x4 t = *reinterpret_cast<const f32x4*>(a.cos_sin + (int64_t)min(pos, C - 1) * D + 4 * k);
+    *reinterpret_cast<YRB_LDS f32x4*>(tab + j * Cfg::TROWB + 16 * tab_phys<D>(j, k)) = t;
+  }
 
-  // Rotated query (fp32) for each of the G heads: pairs 8cc..8cc+7.
-  float qlo[G][8], qhi[G][8];
+  // This wave's steps: the head's ceil(len / 32) steps split over the parts.
+  const int n_steps = (len + kKPS - 1) / kKPS;
+  const int per_part = (n_steps + parts - 1) / parts;
+  const int s_begin = head_live ? min(n_steps, part * per_part) : 0;
+  const int s_end = head_live ? min(n_steps, s_begin + per_part) : 0;
+
+  // Query of each of the G heads rotated at len - 1, as fp32 pairs.
+  float qx[G][8], qz[G][8];
   {
-    const int qpos = len > 0 ? len - 1 : 0;
-    // (cos, sin) of the lane's pairs, two per f32x4 (see pairs_of)
-    const float* trow = a.cos_sin + (int64_t)qpos * D;
     float c[8], s[8];
-#pragma unroll
-    for (int u2 = 0; u2 < 4; ++u2) {
-      const int f = IL ? (u2 < 2 ? 8 * cc + 4 * u2 : D / 2 + 8 * cc + 4 * (u2 - 2)) : 16 * cc + 4 * u2;
-      const f32x4 tt = *reinterpret_cast<const f32x4*>(trow + f);
-      c[2 * u2] = tt[0]; s[2 * u2] = tt[1]; c[2 * u2 + 1] = tt[2]; s[2 * u2 + 1] = tt[3];
-    }
+    row_pairs<D, IL>(a.cos_sin + (int64_t)(len > 0 ? len - 1 : 0) * D, cc, c, s);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + b * a.qs[0] +
-                         (int64_t)(hk * G + g) * a.qs[1];
-      float qa[8], qb[8], x[8], z[8];
+      const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + b * a.qs[0] + (int64_t)(hk * G + g) * a.qs[1];
+      float qa[8], qb[8];
       unpack8(*reinterpret_cast<const u32x4*>(qp + 8 * cc), qa);
       unpack8(*reinterpret_cast<const u32x4*>(qp + D / 2 + 8 * cc), qb);
-      pairs_of<IL>(qa, qb, x, z);
+      pairs_of<IL>(qa, qb, qx[g], qz[g]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        qlo[g][u] = x[u] * c[u] - z[u] * s[u];
-        qhi[g][u] = x[u] * s[u] + z[u] * c[u];
-      }
+      for (int u = 0; u < 8; ++u) rot(qx[g][u], qz[g][u], c[u], s[u]);
     }
   }
 
@@ -189,181 +270,243 @@ __global__ __launch_bounds__(kWaves * 64) void decode_bf16_kernel(DecodeArgs a) 
 
   const Elem* kb = reinterpret_cast<const Elem*>(a.k) + b * a.cs[0] + hk * a.cs[1];
   const Elem* vb = reinterpret_cast<const Elem*>(a.v) + b * a.cs[0] + hk * a.cs[1];
-  const int n_slots = len <= n_sink ? len : C;   // slots worth scanning
 
-  // Table rows of the step starting at `base`: thread t fetches TCH 16-byte
-  // chunks; chunk k of the tile is row k / (TROWB/16), column k % (TROWB/16).
-  auto load_tab = [&](int base, u32x4 (&tv)[TCH]) {
-#pragma unroll
-    for (int n = 0; n < TCH; ++n) {
-      const int k = n * (kWaves * 64) + threadIdx.x;
-      const int row = k / (TROWB / 16);
-      const int col = k % (TROWB / 16);
-      const int pos = position(base + row);
-      tv[n] = *reinterpret_cast<const u32x4*>(a.cos_sin + (int64_t)(pos < 0 ? 0 : pos) * D +
-                                               4 * col);
-    }
+  // Round t covers positions t KPW .. t KPW + KPW - 1; this lane's key is
+  // entry e = t KPW + kg, in its slot: sinks first, then the ring buffer
+  // (the window offset and the head are both below `window`, so one
+  // conditional subtract takes their sum mod window).
+  auto load_round = [&](int t, KV& kv) {
+    const int e = t * KPW + kg;
+    kv.ok = e < len;
+    const int d = rh + e - n_sink;
+    const int slot = e >= len ? 0 : e < n_sink ? e : n_sink + (d >= window ? d - window : d);
+    const Elem* kp = kb + (int64_t)slot * a.cs[2];
+    const Elem* vp = vb + (int64_t)slot * a.cs[2];
+    kv.klo = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(kp + 8 * cc));
+    kv.khi = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(kp + D / 2 + 8 * cc));
+    kv.vlo = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(vp + 8 * cc));
+    kv.vhi = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(vp + D / 2 + 8 * cc));
   };
-  auto store_tab = [&](YRB_LDS char* dst, const u32x4 (&tv)[TCH]) {
+
+  __syncthreads();   // the tables are in LDS
+
+  if (s_begin < s_end) {
+    const int t_begin = s_begin * ROUNDS, t_end = s_end * ROUNDS;
+    KV ring[PD];
 #pragma unroll
-    for (int n = 0; n < TCH; ++n) {
-      const int k = n * (kWaves * 64) + threadIdx.x;
-      *reinterpret_cast<YRB_LDS u32x4*>(dst + 16 * k) = tv[n];
-    }
-  };
-  // K/V loads of the step starting at `base`.
-  auto load_kv = [&](int base, KV& ch) {
+    for (int i = 0; i < PD; ++i)
+      if (t_begin + i < t_end) load_round(t_begin + i, ring[i]);
+
+    // Entry e = 1024 a2 + 32 b1 + j: R(e) = R(1024 a2) R(32 b1) R(j).  The
+    // row of R(1024 a2) changes every 32 steps: it comes from global memory
+    // into the wave's LDS row (entry 2 kKPS + wave of the table's rows, the
+    // lanes of key group 0 writing it).
+    int a_cur = -1;
+    float rc[8], rs[8];              // compose: R(1024 a2 + 32 b1)
+
+    auto step = [&](int s, auto u_tag) YRB_INLINE {
+      constexpr int u = decltype(u_tag)::value;
+      const int A = s * kKPS;
+      const int a2 = A >> 10, b1 = (A >> 5) & 31;
+      const int jw = 2 * kKPS + wave;
+      if (a2 != a_cur) {
+        float c2[8], s2[8];
+        row_pairs<D, IL>(a.cos_sin + (int64_t)(a2 << 10) * D, cc, c2, s2);
+        if (kg == 0) {
+          YRB_LDS char* row = tab + jw * Cfg::TROWB;
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const int slot = base + r * KPW + kg;
-      ch.ok[r] = position(slot) >= 0 && head_live;
-      const int sc = slot < C ? slot : C - 1;
-      const Elem* kp = kb + (int64_t)sc * a.cs[2];
-      const Elem* vp = vb + (int64_t)sc * a.cs[2];
-      ch.klo[r] = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(kp + 8 * cc));
-      ch.khi[r] = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(kp + D / 2 + 8 * cc));
-      ch.vlo[r] = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(vp + 8 * cc));
-      ch.vhi[r] = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(vp + D / 2 + 8 * cc));
-    }
-  };
-  // Fold one step's keys into (m, l, o); (cos, sin) come from the LDS tile.
-  auto fold = [&](const KV& ch, const YRB_LDS char* tl) {
-    float sc_[G][kRounds];
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const YRB_LDS char* trow = tl + (r * KPW + kg) * TROWB;
-      float c[8], s[8], ka[8], kb_[8], x[8], z[8];
-#pragma unroll
-      for (int u2 = 0; u2 < 4; ++u2) {
-        const int off = IL ? (u2 < 2 ? 32 * cc + 16 * u2 : 2 * D + 32 * cc + 16 * (u2 - 2)) : 64 * cc + 16 * u2;
-        const f32x4 tt = *reinterpret_cast<const YRB_LDS f32x4*>(trow + off);
-        c[2 * u2] = tt[0]; s[2 * u2] = tt[1]; c[2 * u2 + 1] = tt[2]; s[2 * u2 + 1] = tt[3];
-      }
-      CT::unpack(ch.klo[r], ka);
-      CT::unpack(ch.khi[r], kb_);
-      pairs_of<IL>(ka, kb_, x, z);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float acc = 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float pc = qlo[g][u] * x[u] + qhi[g][u] * z[u];
-          const float ps = qhi[g][u] * x[u] - qlo[g][u] * z[u];
-          acc = __builtin_fmaf(c[u], pc, __builtin_fmaf(s[u], ps, acc));
+          for (int w = 0; w < 4; ++w) {
+            const f32x4 t = {c2[2 * w], s2[2 * w], c2[2 * w + 1], s2[2 * w + 1]};
+            *reinterpret_cast<YRB_LDS f32x4*>(row + 16 * tab_phys<D>(jw, tab_chunk<D, IL>(cc, w))) = t;
+          }
         }
-        // reduce over the TPK lanes of this key
-#pragma unroll
-        for (int off = 1; off < TPK; off <<= 1) acc += __shfl_xor(acc, off);
-        sc_[g][r] = ch.ok[r] ? acc * scale_log2 : -INFINITY;
+        a_cur = a2;
       }
-    }
+      float c2[8], s2[8], c1[8], s1[8];
+      lds_pairs<D, IL>(tab, jw, cc, c2, s2);
+      lds_pairs<D, IL>(tab, kKPS + b1, cc, c1, s1);
+      float qx_s[G][8], qz_s[G][8];   // ANCHOR_Q: the query this step's keys meet
+      if constexpr (Cfg::ANCHOR_Q) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = sc_[g][0];
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int r = 1; r < kRounds; ++r) mx = fmaxf(mx, sc_[g][r]);
+          for (int w = 0; w < 8; ++w) {
+            qx_s[g][w] = qx[g][w];
+            qz_s[g][w] = qz[g][w];
+            rot_t(qx_s[g][w], qz_s[g][w], c2[w], s2[w]);
+            rot_t(qx_s[g][w], qz_s[g][w], c1[w], s1[w]);
+          }
+      } else {
 #pragma unroll
-      for (int off = TPK; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      const float mn = fmaxf(m[g], mx);
-      if (mn == -INFINITY) continue;
-      const float alpha = m[g] == -INFINITY ? 0.f : fast_exp2(m[g] - mn);
-      m[g] = mn;
-      l[g] *= alpha;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        o_lo[g][u] *= alpha;
-        o_hi[g][u] *= alpha;
+        for (int w = 0; w < 8; ++w) {
+          rc[w] = c2[w];
+          rs[w] = s2[w];
+          add_angle(rc[w], rs[w], c1[w], s1[w]);
+        }
       }
 #pragma unroll
-      for (int r = 0; r < kRounds; ++r) {
-        const float p = fast_exp2(sc_[g][r] - mn);   // 0 for a slot without an entry
-        l[g] += p;
-        // Such a slot's values are zeroed as raw words (whatever the cache
-        // holds there, NaN codes included), so p * v adds 0.
+      for (int r = 0; r < ROUNDS; ++r) {
+        constexpr int dummy = 0;
+        (void)dummy;
+        KV& kv = ring[(u * ROUNDS + r) % PD];
+        const int t = s * ROUNDS + r;
+        const int j = r * KPW + kg;
+        float c[8], sn[8];
+        lds_pairs<D, IL>(tab, j, cc, c, sn);
+        if constexpr (!Cfg::ANCHOR_Q) {
+#pragma unroll
+          for (int w = 0; w < 8; ++w) add_angle(c[w], sn[w], rc[w], rs[w]);
+        }
+        float ka[8], kb2[8], x[8], z[8];
+        CT::unpack(kv.klo, ka);
+        CT::unpack(kv.khi, kb2);
+        pairs_of<IL>(ka, kb2, x, z);
+#pragma unroll
+        for (int w = 0; w < 8; ++w) rot(x[w], z[w], c[w], sn[w]);
+        float p[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float acc = 0.f;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const float qxw = Cfg::ANCHOR_Q ? qx_s[g][w] : qx[g][w];
+            const float qzw = Cfg::ANCHOR_Q ? qz_s[g][w] : qz[g][w];
+            acc = __builtin_fmaf(qxw, x[w], __builtin_fmaf(qzw, z[w], acc));
+          }
+#pragma unroll
+          for (int off = 1; off < TPK; off <<= 1) acc += __shfl_xor(acc, off);
+          const float sc = kv.ok ? acc * scale_log2 : -INFINITY;
+          // the round's max is the same in every lane: a wave-uniform branch
+          float mx = sc;
+#pragma unroll
+          for (int off = TPK; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+          if (mx > m[g] + kDecTau) {
+            const float alpha = fast_exp2(m[g] - mx);   // 0 from the empty state
+            m[g] = mx;
+            l[g] *= alpha;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+              o_lo[g][w] *= alpha;
+              o_hi[g][w] *= alpha;
+            }
+          }
+          p[g] = fast_exp2(sc - m[g]);   // 0 for a slot without an entry
+          l[g] += p[g];
+        }
+        // P V (a slot without an entry adds 0: its raw words are zeroed,
+        // whatever the cache holds there, NaN codes included)
         float v1[8], v2[8];
-        CT::unpack(ch.ok[r] ? ch.vlo[r] : Chunk{}, v1);
-        CT::unpack(ch.ok[r] ? ch.vhi[r] : Chunk{}, v2);
+        CT::unpack(kv.ok ? kv.vlo : Chunk{}, v1);
+        CT::unpack(kv.ok ? kv.vhi : Chunk{}, v2);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          o_lo[g][u] = __builtin_fmaf(p, v1[u], o_lo[g][u]);
-          o_hi[g][u] = __builtin_fmaf(p, v2[u], o_hi[g][u]);
-        }
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            o_lo[g][w] = __builtin_fmaf(p[g], v1[w], o_lo[g][w]);
+            o_hi[g][w] = __builtin_fmaf(p[g], v2[w], o_hi[g][w]);
+          }
+        // the set is free: the round PD ahead goes out into it
+        if (t + PD < t_end) load_round(t + PD, kv);
       }
+    };
+    for (int s = s_begin;; s += U) {
+      bool more = true;
+      static_for<U>([&](auto u_tag) YRB_INLINE {
+        if (more && s + decltype(u_tag)::value < s_end) step(s + decltype(u_tag)::value, u_tag);
+        else more = false;
+      });
+      if (!more || s + U >= s_end) break;
     }
-  };
-  // LDS-only barrier: the table writes are done (lgkmcnt), the K/V prefetch
-  // in flight (vmcnt) is not waited for.
-  auto lds_barrier = [&]() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt left at their maximum
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-
-  // Step: tables and K/V of the next step are issued (tables first), this
-  // step is reduced, then the next table tile is written to the other LDS
-  // buffer.  One barrier per step: all waves are done with the current tile
-  // before anyone overwrites the buffer it sits in.
-  if (n_slots > 0) {
-    u32x4 tv[TCH];
-    load_tab(0, tv);
-    store_tab(tab0, tv);
-  }
-  lds_barrier();
-  KV c0, c1;
-  if (n_slots > 0) load_kv(0, c0);
-  auto step = [&](int base, KV& cur, KV& nxt, const YRB_LDS char* tl,
-                  YRB_LDS char* tn) {
-    const bool more = base + KPS < n_slots;
-    u32x4 tv[TCH];
-    if (more) {
-      load_tab(base + KPS, tv);
-      load_kv(base + KPS, nxt);
-    }
-    fold(cur, tl);
-    if (more) store_tab(tn, tv);
-    lds_barrier();
-    return more;
-  };
-  for (int base = 0; base < n_slots; base += 2 * KPS) {
-    if (!step(base, c0, c1, tab0, tab1)) break;
-    if (!step(base + KPS, c1, c0, tab1, tab0)) break;
   }
 
-  // Reduce across the key groups of the wave (lanes with equal cc), then
-  // write the G output rows of this head.
+  // Sum over the key groups of the wave (lanes with equal cc).
 #pragma unroll
   for (int g = 0; g < G; ++g) {
 #pragma unroll
     for (int off = TPK; off < 64; off <<= 1) {
       l[g] += __shfl_xor(l[g], off);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        o_lo[g][u] += __shfl_xor(o_lo[g][u], off);
-        o_hi[g][u] += __shfl_xor(o_hi[g][u], off);
+      for (int w = 0; w < 8; ++w) {
+        o_lo[g][w] += __shfl_xor(o_lo[g][w], off);
+        o_hi[g][w] += __shfl_xor(o_hi[g][w], off);
       }
     }
-    if (head_live && kg == 0) {
-      const float inv = l[g] > 0.f ? v_deq / l[g] : 0.f;
-      float lo[8], hi[8];
+  }
+
+  auto store = [&](int g, float lsum, const float (&lo)[8], const float (&hi)[8]) {
+    const float inv = lsum > 0.f ? v_deq / lsum : 0.f;
+    float ol[8], oh[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        lo[u] = bad_seq ? __builtin_nanf("") : o_lo[g][u] * inv;
-        hi[u] = bad_seq ? __builtin_nanf("") : o_hi[g][u] * inv;
-      }
-      __bf16* op = reinterpret_cast<__bf16*>(a.o) + b * a.os[0] + (int64_t)(hk * G + g) * a.os[1];
-      *reinterpret_cast<u32x4*>(op + 8 * cc) = pack8(lo);
-      *reinterpret_cast<u32x4*>(op + D / 2 + 8 * cc) = pack8(hi);
+    for (int w = 0; w < 8; ++w) {
+      ol[w] = bad_seq ? __builtin_nanf("") : lo[w] * inv;
+      oh[w] = bad_seq ? __builtin_nanf("") : hi[w] * inv;
     }
+    __bf16* op = reinterpret_cast<__bf16*>(a.o) + b * a.os[0] + (int64_t)(hk * G + g) * a.os[1];
+    *reinterpret_cast<u32x4*>(op + 8 * cc) = pack8(ol);
+    *reinterpret_cast<u32x4*>(op + D / 2 + 8 * cc) = pack8(oh);
+  };
+
+  if (parts == 1) {
+    if (head_live && kg == 0)
+#pragma unroll
+      for (int g = 0; g < G; ++g) store(g, l[g], o_lo[g], o_hi[g]);
+    return;
+  }
+
+  // Merge the parts of each head: every wave leaves (m, l, o) in LDS, then
+  // the wave of part 0 rescales the parts to their common max and adds.
+  // merge[wave]: per head, m and l, then o (8cc + w, d/2 + 8cc + w).
+  if (kg == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float* mg = &merge[wave][g * (D + 2)];
+      if (cc == 0) {
+        mg[0] = m[g];
+        mg[1] = l[g];
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        mg[2 + 8 * cc + w] = o_lo[g][w];
+        mg[2 + D / 2 + 8 * cc + w] = o_hi[g][w];
+      }
+    }
+  }
+  __syncthreads();
+  if (part != 0 || !head_live || kg != 0) return;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mt = -INFINITY;
+    for (int p = 0; p < parts; ++p) mt = fmaxf(mt, merge[wave + p][g * (D + 2)]);
+    float lsum = 0.f, lo[8], hi[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) lo[w] = hi[w] = 0.f;
+    for (int p = 0; p < parts; ++p) {
+      const float* mg = &merge[wave + p][g * (D + 2)];
+      const float wt = mg[0] == -INFINITY ? 0.f : fast_exp2(mg[0] - mt);
+      lsum += wt * mg[1];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        lo[w] += wt * mg[2 + 8 * cc + w];
+        hi[w] += wt * mg[2 + D / 2 + 8 * cc + w];
+      }
+    }
+    store(g, lsum, lo, hi);
   }
 }
 
+// Waves that split one head's entries: enough (sequence, head, part) units
+// to give every SIMD two waves, at most 4.
+constexpr int64_t kTargetWaves = 2048;
+
 template <int D, int G, bool FP8, bool IL>
 hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t blocks = a.B * ((a.Hkv + kWaves - 1) / kWaves);
+  int parts = 1;
+  while (parts < kWaves && a.B * a.Hkv * parts < kTargetWaves) parts *= 2;
+  const int heads_per_wg = kWaves / parts;
+  const int64_t blocks = a.B * ((a.Hkv + heads_per_wg - 1) / heads_per_wg);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_bf16_kernel<D, G, FP8, IL>), dim3((unsigned)blocks), dim3(kWaves * 64),
-                     0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<D, G, FP8, IL>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a,
+                     parts);
   return hipGetLastError();
 }
 
