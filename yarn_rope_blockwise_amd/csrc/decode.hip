@@ -13,29 +13,33 @@
 // once, about one flop per byte), so the kernel is a streaming reduction
 // whose waves run independently.
 //  * A wave owns one (sequence, key/value head) and a range of its cache
-//    entries, walked by position in steps of KPS = 32 (entry e = A + j,
-//    A a multiple of 32, j < 32).  A head's entries may be split over
-//    `parts` waves of one workgroup (the host picks parts so that caches
-//    with few key/value heads still fill the chip); the parts' running
-//    (max, sum, output) merge through LDS at the end.
+//    entries, walked by position in steps of 32 (entry e = A + j, A a
+//    multiple of 32, j < 32), each step a few rounds of D/16-lane keys.  A
+//    head's entries may be split over `parts` waves of one workgroup (the
+//    host picks parts so that caches with few key/value heads still fill
+//    the chip); the parts' (max, sum, output) merge through LDS at the end.
 //  * D/16 lanes share one key: each lane reads the two chunks holding
 //    pairs (i, i + d/2) for its 8 pairs (or, interleaved, adjacent pairs
 //    from the same two chunks), so the rotation is lane-local.  Loads are
-//    non-temporal (the cache is far larger than L2 and MALL), issued a
-//    step ahead.
-//  * Rotation by angle addition: R(A + j) = R(A) R(j).  The 32 rows R(j),
-//    j < 32, sit in LDS for the whole launch (read from the caller's table,
-//    XOR-swizzled so that the lanes of a read hit distinct banks), and
-//    only R(A), one table row per step, comes from L2.  With one or two
-//    query heads per key head the step instead re-anchors the query:
-//    q'.k' = (R(len-1-A) q) . (R(j) k), since R(a)^T R(b) = R(b - a);
-//    with more, it forms R(A + j) per key, once for all the key's heads.
-//    Reading a table row per key and head would move as many bytes as K
-//    and V together.
-//  * Online softmax per wave in the exp2 domain, with the reference max
-//    moved only when a step's max passes it by more than 8 (the same
-//    result in exact arithmetic, P <= 2^8); lanes of one head combine their
-//    partial sums with cross-lane shuffles at the end.
+//    non-temporal (the cache is far larger than L2 and MALL) and pipelined
+//    by round: a ring of register sets keeps a step's worth of rounds in
+//    flight, each set reloaded as soon as its round is folded.
+//  * Rotation by angle addition: with e = 1024 a + 32 b + j,
+//    R(e) = R(1024 a) R(32 b) R(j).  The 32 rows R(j) and the 32 rows
+//    R(32 b) sit in LDS for the whole launch (read from the caller's table,
+//    XOR-swizzled so that the lanes of a read hit distinct banks); R(1024 a)
+//    comes from the table in global memory once every 32 steps.  With one
+//    or two query heads per key head each step re-anchors the query
+//    instead, q'.k' = (R(32 b)^T R(1024 a)^T q') . (R(j) k); with more, it
+//    forms R(e) per key, once for all the key's heads.  Reading a table row
+//    per key and head would move as many bytes as K and V together.
+//  * Online softmax in the exp2 domain, the logit scale folded into the
+//    query.  The running max is kept per key group (the lanes that share a
+//    key agree on it), and a group moves its reference only when a key
+//    beats it by more than 8: the same result in exact arithmetic, P <= 2^8,
+//    and no cross-lane max per round.  The groups merge at the end with
+//    DPP row rotations and the permlane swaps, which also do the per-key
+//    sums; none of these goes through the LDS crossbar.
 #include "common.h"
 #include "kernels.h"
 
@@ -85,13 +89,62 @@ struct DecCfg {
   static constexpr int TROWB = 4 * D;                // bytes of a table row (d/2 pairs of (cos, sin))
   static constexpr int TABB = 2 * kKPS * TROWB;      // LDS bytes of R(j) and R(32 j), j < 32
   static constexpr bool ANCHOR_Q = G <= 2;           // re-anchor the query, else compose R(e) per key
-  // Rounds of K/V loads in flight (register sets of the ring): fewer when
-  // the per-head query and output registers leave less room.
-  static constexpr int PD = G <= 2 ? 4 : 2;
+  // Rounds of K/V loads in flight (register sets of the ring): a step's
+  // worth, half of it when the per-head query and output registers leave
+  // less room.
+  static constexpr int PD = G <= 2 ? ROUNDS : (ROUNDS > 1 ? ROUNDS / 2 : 1);
   // Waves per SIMD the registers are sized for.
   static constexpr int WAVES_PER_EU = G <= 4 ? 2 : 1;
   static_assert(ROUNDS * KPW == kKPS, "a step is whole rounds");
-  static_assert(ROUNDS % PD == 0 || PD % ROUNDS == 0, "ring sets repeat within a step pair");
+  static_assert(ROUNDS % PD == 0, "ring sets repeat within a step");
+};
+
+// Cross-lane reductions without the LDS crossbar (ds_bpermute, which a
+// __shfl_xor becomes, costs an LDS round trip per step): DPP within rows of
+// 16 lanes, and the gfx950 permlane swaps across rows and half-waves.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <- 7 - i within 8 lanes
+constexpr int kDppRowRor4 = 0x124;      // lane i <- (i + 4) mod 16 within a row
+constexpr int kDppRowRor8 = 0x128;      // lane i <- (i + 8) mod 16 within a row
+
+// Sum over the N lanes of an aligned group (N = 1, 2, 4 or 8).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<kDppQuadXor1>(x);
+  if constexpr (N >= 4) x += dpp<kDppQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);   // the quads are uniform by now
+  return x;
+}
+// op (symmetric) of x over the lanes l, l + N, l + 2N, ... (mod 64), i.e.
+// over the aligned groups of N lanes (N = 4 or 8), for each position in a
+// group: every lane ends with the combination for its position.  Row
+// rotations by multiples of N keep the position; the permlane swaps pair
+// lanes 16 and 32 apart.
+template <int N, typename Op>
+__device__ __forceinline__ float across_groups(float x, Op op) {
+  static_assert(N == 4 || N == 8, "groups of 4 or 8 lanes");
+  x = op(x, dpp<kDppRowRor8>(x));
+  if constexpr (N == 4) x = op(x, dpp<kDppRowRor4>(x));
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return x;
+}
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct AddOp {
+  __device__ float operator()(float a, float b) const { return a + b; }
 };
 
 // 16-byte chunk k (2 pairs) of LDS table row j sits at chunk k ^ h(j, k):
@@ -191,9 +244,6 @@ void decode_kernel(DecodeArgs a, int parts) {
   using Cfg = DecCfg<D, G>;
   constexpr int TPK = Cfg::TPK, KPW = Cfg::KPW, ROUNDS = Cfg::ROUNDS, PD = Cfg::PD;
   constexpr int MERGE_F = G * (D + 2);               // floats a wave leaves for the merge
-  // Steps per pass of the loop: the ring's set of a round is then known at
-  // compile time.
-  constexpr int U = PD > ROUNDS ? PD / ROUNDS : 1;
   using KV = KVRound<FP8>;
 
   // LDS rows 0..31: R(j); rows 32..63: R(32 j); then one row per wave for
@@ -237,7 +287,14 @@ void decode_kernel(DecodeArgs a, int parts) {
   const int s_begin = head_live ? min(n_steps, part * per_part) : 0;
   const int s_end = head_live ? min(n_steps, s_begin + per_part) : 0;
 
-  // Query of each of the G heads rotated at len - 1, as fp32 pairs.
+  // fp8: per (sequence, kv head) dequantisation scales; K's folds into the
+  // logit scale, V's into the final normalisation.
+  const float k_deq = (FP8 && a.k_scale) ? a.k_scale[b * a.Hkv + hk] : 1.0f;
+  const float v_deq = (FP8 && a.v_scale) ? a.v_scale[b * a.Hkv + hk] : 1.0f;
+  const float scale_log2 = a.softmax_scale * kLog2e * k_deq;
+
+  // Query of each of the G heads rotated at len - 1 and multiplied by the
+  // logit scale (log2 units), as fp32 pairs.
   float qx[G][8], qz[G][8];
   {
     float c[8], s[8];
@@ -250,15 +307,17 @@ void decode_kernel(DecodeArgs a, int parts) {
       unpack8(*reinterpret_cast<const u32x4*>(qp + D / 2 + 8 * cc), qb);
       pairs_of<IL>(qa, qb, qx[g], qz[g]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) rot(qx[g][u], qz[g][u], c[u], s[u]);
+      for (int u = 0; u < 8; ++u) {
+        rot(qx[g][u], qz[g][u], c[u], s[u]);
+        qx[g][u] *= scale_log2;
+        qz[g][u] *= scale_log2;
+      }
     }
   }
 
-  // fp8: per (sequence, kv head) dequantisation scales; K's folds into the
-  // logit scale, V's into the final normalisation.
-  const float k_deq = (FP8 && a.k_scale) ? a.k_scale[b * a.Hkv + hk] : 1.0f;
-  const float v_deq = (FP8 && a.v_scale) ? a.v_scale[b * a.Hkv + hk] : 1.0f;
-  const float scale_log2 = a.softmax_scale * kLog2e * k_deq;
+  // Running max, sum and output per head.  The max is kept per key group
+  // (the TPK lanes that share a key hold the same one) and the groups merge
+  // at the end, so no round needs a cross-lane max.
   float m[G], l[G], o_lo[G][8], o_hi[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -304,8 +363,10 @@ void decode_kernel(DecodeArgs a, int parts) {
     int a_cur = -1;
     float rc[8], rs[8];              // compose: R(1024 a2 + 32 b1)
 
-    auto step = [&](int s, auto u_tag) YRB_INLINE {
-      constexpr int u = decltype(u_tag)::value;
+    // MASK: the step reaches past the last entry (its missing keys are
+    // masked); the other steps skip the test.
+    auto step = [&](int s, auto mask_tag) YRB_INLINE {
+      constexpr bool MASK = decltype(mask_tag)::value;
       const int A = s * kKPS;
       const int a2 = A >> 10, b1 = (A >> 5) & 31;
       const int jw = 2 * kKPS + wave;
@@ -346,9 +407,7 @@ void decode_kernel(DecodeArgs a, int parts) {
       }
 #pragma unroll
       for (int r = 0; r < ROUNDS; ++r) {
-        constexpr int dummy = 0;
-        (void)dummy;
-        KV& kv = ring[(u * ROUNDS + r) % PD];
+        KV& kv = ring[r % PD];
         const int t = s * ROUNDS + r;
         const int j = r * KPW + kg;
         float c[8], sn[8];
@@ -373,16 +432,14 @@ void decode_kernel(DecodeArgs a, int parts) {
             const float qzw = Cfg::ANCHOR_Q ? qz_s[g][w] : qz[g][w];
             acc = __builtin_fmaf(qxw, x[w], __builtin_fmaf(qzw, z[w], acc));
           }
-#pragma unroll
-          for (int off = 1; off < TPK; off <<= 1) acc += __shfl_xor(acc, off);
-          const float sc = kv.ok ? acc * scale_log2 : -INFINITY;
-          // the round's max is the same in every lane: a wave-uniform branch
-          float mx = sc;
-#pragma unroll
-          for (int off = TPK; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-          if (mx > m[g] + kDecTau) {
-            const float alpha = fast_exp2(m[g] - mx);   // 0 from the empty state
-            m[g] = mx;
+          acc = group_sum<TPK>(acc);
+          const float sc = (!MASK || kv.ok) ? acc : -INFINITY;
+          // a group's reference moves when its key beats it by more than
+          // the threshold: rare once every group has seen a few keys
+          const bool grow = sc > m[g] + kDecTau;
+          if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float alpha = grow ? fast_exp2(m[g] - sc) : 1.0f;   // 0 from the empty state
+            m[g] = grow ? sc : m[g];
             l[g] *= alpha;
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
@@ -390,14 +447,15 @@ void decode_kernel(DecodeArgs a, int parts) {
               o_hi[g][w] *= alpha;
             }
           }
-          p[g] = fast_exp2(sc - m[g]);   // 0 for a slot without an entry
+          // 0 for a slot without an entry (whose group may have no reference yet)
+          p[g] = (!MASK || kv.ok) ? fast_exp2(sc - m[g]) : 0.f;
           l[g] += p[g];
         }
         // P V (a slot without an entry adds 0: its raw words are zeroed,
         // whatever the cache holds there, NaN codes included)
         float v1[8], v2[8];
-        CT::unpack(kv.ok ? kv.vlo : Chunk{}, v1);
-        CT::unpack(kv.ok ? kv.vhi : Chunk{}, v2);
+        CT::unpack((!MASK || kv.ok) ? kv.vlo : Chunk{}, v1);
+        CT::unpack((!MASK || kv.ok) ? kv.vhi : Chunk{}, v2);
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -409,27 +467,31 @@ void decode_kernel(DecodeArgs a, int parts) {
         if (t + PD < t_end) load_round(t + PD, kv);
       }
     };
-    for (int s = s_begin;; s += U) {
-      bool more = true;
-      static_for<U>([&](auto u_tag) YRB_INLINE {
-        if (more && s + decltype(u_tag)::value < s_end) step(s + decltype(u_tag)::value, u_tag);
-        else more = false;
-      });
-      if (!more || s + U >= s_end) break;
-    }
+    // Steps whose 32 entries all exist, then (the sequence's last step, if
+    // partial) the masked one, in a loop of its own so that the two bodies
+    // do not share registers.
+    const int s_full = max(s_begin, min(s_end, len / kKPS));
+    for (int s = s_begin; s < s_full; ++s) step(s, std::false_type{});
+    for (int s = s_full; s < s_end; ++s) step(s, std::true_type{});
   }
 
-  // Sum over the key groups of the wave (lanes with equal cc).
+  // Merge the key groups of the wave: each group's sums go to the wave's
+  // max, then add over the groups (lanes with equal cc).
 #pragma unroll
   for (int g = 0; g < G; ++g) {
+    const float mw = across_groups<TPK>(m[g], MaxOp{});
+    const float sc = m[g] == -INFINITY ? 0.f : fast_exp2(m[g] - mw);   // a group with no key: 0
+    m[g] = mw;
+    l[g] = across_groups<TPK>(l[g] * sc, AddOp{});
 #pragma unroll
-    for (int off = TPK; off < 64; off <<= 1) {
-      l[g] += __shfl_xor(l[g], off);
+    for (int w = 0; w < 8; ++w) {
+      o_lo[g][w] *= sc;
+      o_hi[g][w] *= sc;
+    }
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        o_lo[g][w] += __shfl_xor(o_lo[g][w], off);
-        o_hi[g][w] += __shfl_xor(o_hi[g][w], off);
-      }
+    for (int w = 0; w < 8; ++w) {
+      o_lo[g][w] = across_groups<TPK>(o_lo[g][w], AddOp{});
+      o_hi[g][w] = across_groups<TPK>(o_hi[g][w], AddOp{});
     }
   }
 
