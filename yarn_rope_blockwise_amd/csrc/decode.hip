@@ -79,7 +79,7 @@ struct CacheType<true> {
   }
 };
 
-template <int D, int G>
+template <int D, int G, bool FP8 = false>
 struct DecCfg {
   static constexpr int TPK = D / 16;                 // lanes per key (8 pairs each)
   static constexpr int KPW = 64 / TPK;               // keys per round
@@ -90,13 +90,15 @@ struct DecCfg {
   static constexpr int TABB = 2 * kKPS * TROWB;      // LDS bytes of R(j) and R(32 j), j < 32
   static constexpr bool ANCHOR_Q = G <= 2;           // re-anchor the query, else compose R(e) per key
   // Rounds of K/V loads in flight (register sets of the ring): a step's
-  // worth, half of it when the per-head query and output registers leave
-  // less room.
-  static constexpr int PD = G <= 2 ? ROUNDS : (ROUNDS > 1 ? ROUNDS / 2 : 1);
+  // worth, two for an fp8 cache with one query head per key head (its
+  // chunks are half the size; measured 3-4 % faster), half of one when the
+  // per-head query and output registers leave less room.
+  static constexpr int PD = (FP8 && G == 1) ? 2 * ROUNDS : G <= 2 ? ROUNDS : (ROUNDS > 1 ? ROUNDS / 2 : 1);
   // Waves per SIMD the registers are sized for.
   static constexpr int WAVES_PER_EU = G <= 4 ? 2 : 1;
   static_assert(ROUNDS * KPW == kKPS, "a step is whole rounds");
-  static_assert(ROUNDS % PD == 0, "ring sets repeat within a step");
+  static_assert(ROUNDS % PD == 0 || PD % ROUNDS == 0, "ring sets repeat within U steps");
+  static constexpr int U = PD > ROUNDS ? PD / ROUNDS : 1;   // steps per pass of the loop
 };
 
 // Cross-lane reductions without the LDS crossbar (ds_bpermute, which a
@@ -236,14 +238,15 @@ struct KVRound {
 };
 
 template <int D, int G, bool FP8, bool IL>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(DecCfg<D, G>::WAVES_PER_EU)))
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(DecCfg<D, G, FP8>::WAVES_PER_EU)))
 void decode_kernel(DecodeArgs a, int parts) {
   using CT = CacheType<FP8>;
   using Chunk = typename CT::Chunk;
   using Elem = typename CT::Elem;
-  using Cfg = DecCfg<D, G>;
+  using Cfg = DecCfg<D, G, FP8>;
   constexpr int TPK = Cfg::TPK, KPW = Cfg::KPW, ROUNDS = Cfg::ROUNDS, PD = Cfg::PD;
   constexpr int MERGE_F = G * (D + 2);               // floats a wave leaves for the merge
+  constexpr int U = Cfg::U;
   using KV = KVRound<FP8>;
 
   // LDS rows 0..31: R(j); rows 32..63: R(32 j); then one row per wave for
@@ -365,7 +368,9 @@ void decode_kernel(DecodeArgs a, int parts) {
 
     // MASK: the step reaches past the last entry (its missing keys are
     // masked); the other steps skip the test.
-    auto step = [&](int s, auto mask_tag) YRB_INLINE {
+    // U: the step's place in a pass of U steps, which picks the ring sets.
+    auto step = [&](int s, auto u_tag, auto mask_tag) YRB_INLINE {
+      constexpr int u = decltype(u_tag)::value;
       constexpr bool MASK = decltype(mask_tag)::value;
       const int A = s * kKPS;
       const int a2 = A >> 10, b1 = (A >> 5) & 31;
@@ -407,7 +412,7 @@ void decode_kernel(DecodeArgs a, int parts) {
       }
 #pragma unroll
       for (int r = 0; r < ROUNDS; ++r) {
-        KV& kv = ring[r % PD];
+        KV& kv = ring[(u * ROUNDS + r) % PD];
         const int t = s * ROUNDS + r;
         const int j = r * KPW + kg;
         float c[8], sn[8];
@@ -471,8 +476,20 @@ void decode_kernel(DecodeArgs a, int parts) {
     // partial) the masked one, in a loop of its own so that the two bodies
     // do not share registers.
     const int s_full = max(s_begin, min(s_end, len / kKPS));
-    for (int s = s_begin; s < s_full; ++s) step(s, std::false_type{});
-    for (int s = s_full; s < s_end; ++s) step(s, std::true_type{});
+    for (int s = s_begin; s < s_full; s += U) {
+      static_for<U>([&](auto u_tag) YRB_INLINE {
+        if (s + decltype(u_tag)::value < s_full) step(s + decltype(u_tag)::value, u_tag, std::false_type{});
+      });
+    }
+    for (int s = s_full; s < s_end; ++s) {
+      if constexpr (U == 1) {
+        step(s, std::integral_constant<int, 0>{}, std::true_type{});
+      } else {
+        static_assert(U == 2, "two steps per pass at most");
+        if ((s - s_begin) & 1) step(s, std::integral_constant<int, 1>{}, std::true_type{});
+        else step(s, std::integral_constant<int, 0>{}, std::true_type{});
+      }
+    }
   }
 
   // Merge the key groups of the wave: each group's sums go to the wave's
