@@ -2,7 +2,8 @@
 """Throughput of the YaRN-RoPE blockwise attention path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-                    [--workload all|prefill|decode|ring|copy]
+                    [--workload all|prefill|gqa32k_{pi,ntk,yarn}|decode|decode_fp8|
+                                decode_gqa|decode_gqa_fp8|sink_window|ring|copy]
 
 One step is the whole prefill path on the Llama-7B-like 16k workload
 (batch 1, 32 heads, d=128, 16384 tokens, bf16, YaRN s=4 from 4096):
@@ -11,18 +12,22 @@ One step is the whole prefill path on the Llama-7B-like 16k workload
 ``value`` is algorithmic TFLOP/s of the step (4*d flop per visible
 (query, key) pair, masked pairs not counted) with inputs resident in HBM.
 
-Also measured in the same run: the sink + window decode (64 sequences x 32
-heads, cache 4 + 4096, HBM GB/s), one ring device's share (8 heads, 8 key
-blocks of 32768 at query block 7), and the fp64 oracle on the host cores
-over a bounded sample (``cpu_baseline``).  Per-kernel durations come from
-HIP events recorded on the stream the library launches on.
-Prints one JSON line.
+Also measured in the same run, each with its roofline: the 32k grouped-query
+prefill once per rescale method (PI, NTK-aware, YaRN at s=8), the sink +
+window decode (64 sequences, cache 4 + 4096) with 32 heads and with 32 query
+over 8 key/value heads, each over a bf16 and an E4M3 cache (HBM GB/s), the
+interleaved pair layout, per-pair factor tables, the prefill under the
+sink+window mask, one ring device's share (8 heads, 8 key blocks of 32768 at
+query block 7), and the fp64 oracle on the host's cores over a bounded
+sample (``cpu_baseline``).  Per-kernel durations come from HIP events
+recorded on the stream the library launches on.  Prints one JSON line.
 
 Warm-up: under sustained load the engine clock ramps up over about the
 first 50 ms (the 16k attention kernel measured 2.5 ms on its first launch
-and 1.67 ms from about the 25th on), so the default is 30 untimed steps; the
-decode and the ring share, timed after it, take their own warm-up of about
-the same length.
+and 1.67 ms from about the 25th on).  Every workload therefore runs its W
+warm-up steps and then keeps warming, ten steps at a time, until at least
+0.2 s of warm-up has passed; the line reports the steps that took
+(``warmup_steps_run``).  The timed steps are exactly K.
 """
 from __future__ import annotations
 
@@ -47,23 +52,18 @@ METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HB
 # device copy (FETCH x1.99994, WRITE x1.0).  Each figure holds only for the
 # kernel sources it was taken on: the sha256 over the listed files must match,
 # else the line reports traffic null.
+_PP = ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h")
+_DEC = ("csrc/decode.hip", "csrc/common.h")
 MEASURED_TRAFFIC = {
-    "attn_bf16_pp_kernel": {
-        "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
-        "sha256": "ce8e6c36e22a7e2c76919f55ab83bb5006d79a7ef3bcad54fbf6a901c3916ea5",
-        "fetch_kib": 1060865, "write_kib": 131091},
-    "decode_bf16_kernel": {
-        "files": ("csrc/decode.hip", "csrc/common.h"),
-        "sha256": "bb86e0e7d62bfd147d1ef7163969d9f4cb27d1676997f5cb425c4230aea4a39b",
-        "fetch_kib": 2108966, "write_kib": 512},
-    "decode_bf16_kernel_fp8": {
-        "files": ("csrc/decode.hip", "csrc/common.h"),
-        "sha256": "bb86e0e7d62bfd147d1ef7163969d9f4cb27d1676997f5cb425c4230aea4a39b",
-        "fetch_kib": 1060697, "write_kib": 512},
-    "attn_bf16_pp_kernel_window": {
-        "files": ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h"),
-        "sha256": "ce8e6c36e22a7e2c76919f55ab83bb5006d79a7ef3bcad54fbf6a901c3916ea5",
-        "fetch_kib": 733819, "write_kib": 131091},
+    "attn_bf16_pp_kernel": {"files": _PP, "sha256": None, "fetch_kib": 0, "write_kib": 0},
+    "attn_bf16_pp_kernel_gqa_prefill_32k_pi8": {"files": _PP, "sha256": None, "fetch_kib": 0, "write_kib": 0},
+    "attn_bf16_pp_kernel_gqa_prefill_32k_ntk8": {"files": _PP, "sha256": None, "fetch_kib": 0, "write_kib": 0},
+    "attn_bf16_pp_kernel_gqa_prefill_32k_yarn8": {"files": _PP, "sha256": None, "fetch_kib": 0, "write_kib": 0},
+    "attn_bf16_pp_kernel_window": {"files": _PP, "sha256": None, "fetch_kib": 0, "write_kib": 0},
+    "decode_kernel": {"files": _DEC, "sha256": None, "fetch_kib": 0, "write_kib": 0},
+    "decode_kernel_fp8": {"files": _DEC, "sha256": None, "fetch_kib": 0, "write_kib": 0},
+    "decode_kernel_gqa": {"files": _DEC, "sha256": None, "fetch_kib": 0, "write_kib": 0},
+    "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": None, "fetch_kib": 0, "write_kib": 0},
 }
 FETCH_FACTOR, WRITE_FACTOR = 1.99994, 1.0
 
@@ -110,11 +110,36 @@ def _upload(shape, seed):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def run_prefill(steps: int, warmup: int):
+# The engine clock ramps up over about the first 50 ms of sustained load, so
+# warm-up goes on past the W steps asked for until this much time has run.
+WARMUP_MIN_S = 0.2
+
+
+def warm(fn, warmup: int, min_s: float = WARMUP_MIN_S) -> int:
+    """Run fn() `warmup` times, then more, in tens, until `min_s` seconds of
+    warm-up have passed (synchronised).  Returns the number of calls made."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(warmup):
+        fn()
+        n += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_s:
+        for _ in range(10):
+            fn()
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def run_prefill(steps: int, warmup: int, w=None):
+    """One step of the prefill path on workload w (default the 16k one):
+    table build, K rotation, attention with Q rotated on load."""
     import torch
     from yarn_rope_blockwise_amd import api
     from yarn_rope_blockwise_amd import workloads as W
-    w = W.LLAMA_16K
+    w = w or W.LLAMA_16K
     B, S, H, D = w.batch, w.seq, w.n_q_heads, w.head_dim
     q = _upload((B, S, H, D), 0)
     k = _upload((B, S, w.n_kv_heads, D), 1)
@@ -140,9 +165,7 @@ def run_prefill(steps: int, warmup: int):
         if ev is not None:
             ev[3].record()
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    n_warm = warm(step, warmup)
     evs = [_events(4) for _ in range(steps)]
     t0, t1 = _events(2)
     torch.cuda.synchronize()
@@ -157,7 +180,7 @@ def run_prefill(steps: int, warmup: int):
     attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     flops = causal_flops(S, H, D, B)
     return dict(total_ms=total_ms, ms_per_step=total_ms / steps, tables_ms=tab_ms,
-                rope_k_ms=rope_ms, attn_ms=attn_ms, flops=flops,
+                rope_k_ms=rope_ms, attn_ms=attn_ms, flops=flops, warmup_steps_run=n_warm,
                 k_bytes=2 * k.numel() * 2 + S * D * 4)
 
 
@@ -188,8 +211,7 @@ def run_sink_window_prefill(steps: int, warmup: int, n_sink: int = 4, window: in
         api.attn_prefill_sink_window(q, k_rot, v, scale, n_sink, window, cos_sin=tab, out=out,
                                      workspace=ws)
 
-    for _ in range(warmup):
-        call()
+    warm(call, warmup)
     t0, t1 = _events(2)
     torch.cuda.synchronize()
     t0.record()
@@ -202,50 +224,42 @@ def run_sink_window_prefill(steps: int, warmup: int, n_sink: int = 4, window: in
     return dict(ms=ms, flops=flops, n_sink=n_sink, window=window)
 
 
-def run_decode(steps: int, warmup: int):
+def run_gqa32k(steps: int, warmup: int, kinds=None):
+    """The 32k grouped-query prefill (32 query / 8 key-value heads, base 5e5,
+    s = 8 from 4096) once per rescale method (PI, NTK-aware, YaRN): the same
+    inputs, each method's own tables and softmax scale; the step as for the
+    16k workload (table build, K rotation, attention)."""
+    from yarn_rope_blockwise_amd import workloads as W
+    kinds = kinds or (W.PI, W.NTK, W.YARN)
+    out = {}
+    for kind in kinds:
+        w = W.GQA_32K[kind]
+        log(f"gqa 32k prefill, {w.name}")
+        out[w.name] = run_prefill(steps, warmup, w)
+    return out
+
+
+def run_decode(steps: int, warmup: int, n_q_heads=None, n_kv_heads=None, fp8: bool = False):
+    """The sink + window decode (64 sequences, 4 + 4096 cache), timed over
+    back-to-back launches: bf16 cache through attn_decode_sink_window, or
+    E4M3 codes with per-(sequence, head) scales through
+    attn_decode_sink_window_fp8; head counts default to the workload's."""
     import torch
     from yarn_rope_blockwise_amd import api, synth
     from yarn_rope_blockwise_amd import workloads as W
     w = W.SINK_DECODE
+    Hq = n_q_heads or w.n_q_heads
+    Hkv = n_kv_heads or w.n_kv_heads
     C = w.n_sink + w.window
-    q = _upload((w.batch, w.n_q_heads, w.head_dim), 0)
-    kc = _upload((w.batch, w.n_kv_heads, C, w.head_dim), 1)
-    vc = _upload((w.batch, w.n_kv_heads, C, w.head_dim), 2)
-    lens = torch.full((w.batch,), C, dtype=torch.int32, device="cuda")
-    rh = torch.from_numpy(synth.ring_heads(w.batch, w.window)).cuda()
-    tab, _, af = api.rope_tables_build(api.RopeConfig.of(w.rope), C)
-    scale = af / np.sqrt(w.head_dim)
-    out = torch.empty_like(q)
-    for _ in range(warmup):
-        api.attn_decode_sink_window(q, kc, vc, lens, w.n_sink, w.window, tab, scale, rh, out)
-    torch.cuda.synchronize()
-    # Back-to-back launches between two events: the host queues calls faster
-    # than the GPU runs them, so no launch waits on the host (events around
-    # each call would also time the host's call overhead while the GPU idles).
-    ev = _events(2)
-    ev[0].record()
-    for _ in range(steps):
-        api.attn_decode_sink_window(q, kc, vc, lens, w.n_sink, w.window, tab, scale, rh, out)
-    ev[1].record()
-    torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / steps
-    kv_bytes = 2 * kc.numel() * 2
-    other = q.numel() * 2 * 2 + lens.numel() * 4 * 2
-    return dict(ms=ms, bytes=kv_bytes + other, kv_bytes=kv_bytes)
-
-
-def run_decode_fp8(steps: int, warmup: int):
-    """The decode workload with E4M3 K/V caches and per-(sequence, head) scales."""
-    import torch
-    from yarn_rope_blockwise_amd import api, synth
-    from yarn_rope_blockwise_amd import workloads as W
-    w = W.SINK_DECODE
-    C = w.n_sink + w.window
-    q = _upload((w.batch, w.n_q_heads, w.head_dim), 0)
-    kc = torch.from_numpy(synth.e4m3_codes((w.batch, w.n_kv_heads, C, w.head_dim), 1)).cuda()
-    vc = torch.from_numpy(synth.e4m3_codes((w.batch, w.n_kv_heads, C, w.head_dim), 2)).cuda()
-    ks = torch.from_numpy(synth.uniform_scales((w.batch, w.n_kv_heads), 4)).cuda()
-    vs = torch.from_numpy(synth.uniform_scales((w.batch, w.n_kv_heads), 5)).cuda()
+    q = _upload((w.batch, Hq, w.head_dim), 0)
+    if fp8:
+        kc = torch.from_numpy(synth.e4m3_codes((w.batch, Hkv, C, w.head_dim), 1)).cuda()
+        vc = torch.from_numpy(synth.e4m3_codes((w.batch, Hkv, C, w.head_dim), 2)).cuda()
+        ks = torch.from_numpy(synth.uniform_scales((w.batch, Hkv), 4)).cuda()
+        vs = torch.from_numpy(synth.uniform_scales((w.batch, Hkv), 5)).cuda()
+    else:
+        kc = _upload((w.batch, Hkv, C, w.head_dim), 1)
+        vc = _upload((w.batch, Hkv, C, w.head_dim), 2)
     lens = torch.full((w.batch,), C, dtype=torch.int32, device="cuda")
     rh = torch.from_numpy(synth.ring_heads(w.batch, w.window)).cuda()
     tab, _, af = api.rope_tables_build(api.RopeConfig.of(w.rope), C)
@@ -253,11 +267,16 @@ def run_decode_fp8(steps: int, warmup: int):
     out = torch.empty_like(q)
 
     def call():
-        api.attn_decode_sink_window_fp8(q, kc, vc, lens, w.n_sink, w.window, tab, scale, rh,
-                                        out, k_scale=ks, v_scale=vs)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
+        if fp8:
+            api.attn_decode_sink_window_fp8(q, kc, vc, lens, w.n_sink, w.window, tab, scale, rh,
+                                            out, k_scale=ks, v_scale=vs)
+        else:
+            api.attn_decode_sink_window(q, kc, vc, lens, w.n_sink, w.window, tab, scale, rh, out)
+
+    warm(call, warmup)
+    # Back-to-back launches between two events: the host queues calls faster
+    # than the GPU runs them, so no launch waits on the host (events around
+    # each call would also time the host's call overhead while the GPU idles).
     ev = _events(2)
     ev[0].record()
     for _ in range(steps):
@@ -265,8 +284,8 @@ def run_decode_fp8(steps: int, warmup: int):
     ev[1].record()
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1]) / steps
-    kv_bytes = 2 * kc.numel()
-    other = q.numel() * 2 * 2 + lens.numel() * 4 * 2 + ks.numel() * 4 * 2
+    kv_bytes = 2 * kc.numel() * kc.element_size()
+    other = q.numel() * 2 * 2 + lens.numel() * 4 * 2 + (2 * w.batch * Hkv * 4 if fp8 else 0)
     return dict(ms=ms, bytes=kv_bytes + other, kv_bytes=kv_bytes)
 
 
@@ -280,9 +299,7 @@ def run_interleaved(steps: int, warmup: int):
     k = _upload((w.batch, w.seq, w.n_kv_heads, w.head_dim), 1)
     tab, _, _ = api.rope_tables_build(api.RopeConfig.of(w.rope), w.seq)
     kr = torch.empty_like(k)
-    for _ in range(warmup):
-        api.rope_apply_ex(k, tab, layout=api.LAYOUT_INTERLEAVED, out=kr)
-    torch.cuda.synchronize()
+    warm(lambda: api.rope_apply_ex(k, tab, layout=api.LAYOUT_INTERLEAVED, out=kr), warmup)
     ev = _events(2)
     ev[0].record()
     for _ in range(steps):
@@ -306,9 +323,7 @@ def run_interleaved(steps: int, warmup: int):
         api.attn_decode_sink_window_ex(q, kc, vc, lens, d.n_sink, d.window, dtab,
                                        af / np.sqrt(d.head_dim), layout=api.LAYOUT_INTERLEAVED,
                                        ring_head=rh, out=out)
-    for _ in range(3 * warmup):
-        call()
-    torch.cuda.synchronize()
+    warm(call, 3 * warmup)
     ev = _events(2)
     ev[0].record()
     for _ in range(steps):
@@ -357,9 +372,7 @@ def run_ring(steps: int, warmup: int):
         if ev is not None:
             ev[nb + 1].record()
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm(step, warmup)
     evs = [_events(nb + 2) for _ in range(steps)]
     for i in range(steps):
         step(evs[i])
@@ -379,9 +392,7 @@ def run_factor_tables(steps: int, warmup: int):
     S, D = 262144, 128
     lam = np.sort(np.random.default_rng(7).uniform(1.0, 64.0, D // 2))
     tab = torch.empty((S, D // 2, 2), dtype=torch.float32, device="cuda")
-    for _ in range(warmup):
-        api.rope_tables_build_factors(D, 1e4, lam, S, out=tab)
-    torch.cuda.synchronize()
+    warm(lambda: api.rope_tables_build_factors(D, 1e4, lam, S, out=tab), warmup)
     ev = _events(2)
     ev[0].record()
     for _ in range(steps):
@@ -404,35 +415,88 @@ def run_copy(steps: int):
     return {"copy_bytes_read": n, "copy_bytes_written": n, "launches": steps}
 
 
-def cpu_baseline(budget_s: float = 12.0):
-    """The fp64 oracle as it stands, on the 16k workload, head by head."""
+def _oracle_head(head: int, ready, go, results):
+    """One process of the CPU baseline: draw one head of the 16k prefill's
+    shape (seeded by head), wait at the barrier, run the fp64 oracle on it."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # pragma: no cover - the env vars already ask for one thread
+        pass
     from oracle import attention as A
     from oracle import rope as R
     from yarn_rope_blockwise_amd import synth
     from yarn_rope_blockwise_amd import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     w = W.LLAMA_16K
     S, D = w.seq, w.head_dim
     th = R.inv_freq(w.rope.kind, D, w.rope.base, w.rope.scale, w.rope.orig_ctx)
     sc = R.softmax_scale(w.rope.kind, w.rope.scale, D)
-    done = 0
+    qv, _ = synth.normal((1, S, 1, D), 1000 + head, "bf16")
+    kv, _ = synth.normal((1, S, 1, D), 2000 + head, "bf16")
+    vv, _ = synth.normal((1, S, 1, D), 3000 + head, "bf16")
+    ready.wait()
+    go.wait()
     t0 = time.perf_counter()
-    while done < w.n_q_heads and time.perf_counter() - t0 < budget_s:
-        qv, _ = synth.normal((1, S, 1, D), 1000 + done, "bf16")
-        kv, _ = synth.normal((1, S, 1, D), 2000 + done, "bf16")
-        vv, _ = synth.normal((1, S, 1, D), 3000 + done, "bf16")
-        A.prefill(qv, kv, vv, th, sc)
-        done += 1
-    el = time.perf_counter() - t0
-    flops = causal_flops(S, done, D)
-    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+    A.prefill(qv, kv, vv, th, sc)
+    results.put((head, time.perf_counter() - t0))
+
+
+def cpu_baseline(max_procs: int = 32):
+    """The fp64 oracle as it stands, on the 16k prefill's shape: one process
+    per core this process may run on (os.sched_getaffinity), each with BLAS
+    on one thread and one whole head (all 16384 causal rows, its own seeded
+    inputs, drawn before the clock starts).  The clock runs from the
+    barrier that releases every process to the last result."""
+    import multiprocessing as mp
+    from yarn_rope_blockwise_amd import workloads as W
+    n = max(1, min(len(os.sched_getaffinity(0)), max_procs, W.LLAMA_16K.n_q_heads))
+    ctx = mp.get_context("spawn")            # fresh interpreters: no GPU state inherited
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                            "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    ready, go = ctx.Barrier(n + 1), ctx.Barrier(n + 1)
+    results = ctx.Queue()
+    procs = [ctx.Process(target=_oracle_head, args=(h, ready, go, results)) for h in range(n)]
+    try:
+        for p_ in procs:
+            p_.start()
+        ready.wait()                          # every process has its inputs
+        go.wait()
+        t0 = time.perf_counter()
+        per = [results.get() for _ in range(n)]
+        wall = time.perf_counter() - t0
+        for p_ in procs:
+            p_.join()
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    w = W.LLAMA_16K
+    flops = causal_flops(w.seq, n, w.head_dim)
+    return {"value": round(flops / wall / 1e12, 6), "unit": "TFLOP/s", "cores": n,
             "kind": "oracle",
-            "sample": f"{done} of {w.n_q_heads} heads of the 16k prefill (all 16384 causal rows "
-                      f"each, fp64 numpy), {el:.1f} s wall incl. input generation"}
+            "sample": f"{n} of {w.n_q_heads} heads of the 16k prefill shape (all 16384 causal "
+                      f"rows each, fp64 numpy, own seeded inputs), one process per core with "
+                      f"BLAS on 1 thread; {wall:.1f} s wall from the start barrier, "
+                      f"slowest head {max(t for _, t in per):.1f} s"}
+
+
+def roofline(bound, achieved, peak, unit, kernel, traffic_key=None, **per_launch):
+    d = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4),
+         "traffic": measured_traffic(traffic_key) if traffic_key else None, "kernel": kernel}
+    d.update(per_launch)
+    return d
+
+
+def decode_entry(name, d, kernel, traffic_key):
+    gbs = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+    return {"workload": name, "ms": round(d["ms"], 4), "GB/s": round(gbs, 1),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", kernel, traffic_key,
+                                 bytes_per_launch=d["bytes"])}
 
 
 def main():
@@ -441,9 +505,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip decode and ring share")
+    ap.add_argument("--no-extras", action="store_true", help="skip everything but the 16k step")
     ap.add_argument("--workload", default="all",
-                    choices=["all", "prefill", "decode", "decode_fp8", "sink_window", "ring",
+                    choices=["all", "prefill", "gqa32k_pi", "gqa32k_ntk", "gqa32k_yarn", "decode",
+                             "decode_fp8", "decode_gqa", "decode_gqa_fp8", "sink_window", "ring",
                              "copy"],
                     help="run one workload alone (for profiling); the JSON line needs 'all'")
     args = ap.parse_args()
@@ -456,11 +521,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    from yarn_rope_blockwise_amd import workloads as W
 
+    dec_warm = max(3 * args.warmup, 10)
     if args.workload != "all":
+        gqa = lambda k: run_prefill(args.steps, args.warmup, W.GQA_32K[k])  # noqa: E731
         only = {"prefill": lambda: run_prefill(args.steps, args.warmup),
-                "decode": lambda: run_decode(args.steps, max(3 * args.warmup, 10)),
-                "decode_fp8": lambda: run_decode_fp8(args.steps, max(3 * args.warmup, 10)),
+                "gqa32k_pi": lambda: gqa(W.PI), "gqa32k_ntk": lambda: gqa(W.NTK),
+                "gqa32k_yarn": lambda: gqa(W.YARN),
+                "decode": lambda: run_decode(args.steps, dec_warm),
+                "decode_fp8": lambda: run_decode(args.steps, dec_warm, fp8=True),
+                "decode_gqa": lambda: run_decode(args.steps, dec_warm, 32, 8),
+                "decode_gqa_fp8": lambda: run_decode(args.steps, dec_warm, 32, 8, fp8=True),
                 "sink_window": lambda: run_sink_window_prefill(args.steps, args.warmup),
                 "ring": lambda: run_ring(args.steps, 2),
                 "copy": lambda: run_copy(args.steps)}[args.workload]()
@@ -480,6 +552,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": pre["warmup_steps_run"],
         "ms_per_step": round(pre["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -490,57 +563,55 @@ def main():
                    "q_heads": 32, "kv_heads": 32, "head_dim": 128, "causal": True,
                    "rope": "yarn s=4 (4096->16384), base 1e4, alpha 1, beta 32",
                    "step": "rope_tables_build + rope_apply(K) + attn_prefill_blockwise"},
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("attn_bf16_pp_kernel"),
-                     "kernel": "attn_bf16_pp_kernel", "kernel_ms": round(pre["attn_ms"], 4),
-                     "flops_per_launch": pre["flops"]},
+        "roofline": roofline("mfma", attn_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "attn_bf16_pp_kernel",
+                             "attn_bf16_pp_kernel", kernel_ms=round(pre["attn_ms"], 4),
+                             flops_per_launch=pre["flops"]),
         "step_breakdown_ms": {"rope_tables_build": round(pre["tables_ms"], 4),
                               "rope_apply_k": round(pre["rope_k_ms"], 4),
                               "attn_prefill_blockwise": round(pre["attn_ms"], 4)},
     }
     if not args.no_extras:
+        gq = run_gqa32k(max(args.steps // 2, 5), args.warmup)
+        line["gqa_prefill_32k"] = {}
+        for name, r in gq.items():
+            k_tf = r["flops"] / (r["attn_ms"] * 1e-3) / 1e12
+            line["gqa_prefill_32k"][name] = {
+                "ms_per_step": round(r["ms_per_step"], 4),
+                "TFLOP/s": round(r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12, 2),
+                "roofline": roofline("mfma", k_tf, PEAK_BF16_TFLOPS, "TFLOP/s", "attn_bf16_pp_kernel",
+                                     "attn_bf16_pp_kernel_" + name, kernel_ms=round(r["attn_ms"], 4),
+                                     flops_per_launch=r["flops"])}
         log("decode: uploading caches and timing")
-        dec = run_decode(max(args.steps, 10), max(3 * args.warmup, 10))
-        log(f"decode done: {dec['ms']:.3f} ms")
-        gbs = dec["bytes"] / (dec["ms"] * 1e-3) / 1e9
-        line["decode"] = {"workload": "sink_decode_b64_h32_4p4096", "ms": round(dec["ms"], 4),
-                          "GB/s": round(gbs, 1),
-                          "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
-                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                       "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                       "traffic": measured_traffic("decode_bf16_kernel"),
-                                       "kernel": "decode_bf16_kernel",
-                                       "bytes_per_launch": dec["bytes"]}}
-        log("decode, fp8 cache: uploading caches and timing")
-        d8 = run_decode_fp8(max(args.steps, 10), max(3 * args.warmup, 10))
-        g8 = d8["bytes"] / (d8["ms"] * 1e-3) / 1e9
-        line["decode_fp8"] = {"workload": "sink_decode_b64_h32_4p4096_e4m3", "ms": round(d8["ms"], 4),
-                              "GB/s": round(g8, 1),
-                              "roofline": {"bound": "hbm", "achieved": round(g8, 1),
-                                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                           "frac": round(g8 / PEAK_HBM_GBS, 4),
-                                           "traffic": measured_traffic("decode_bf16_kernel_fp8"),
-                                           "kernel": "decode_bf16_kernel<fp8>",
-                                           "bytes_per_launch": d8["bytes"]}}
-        il = run_interleaved(max(args.steps, 10), max(args.warmup, 10))
+        steps_d = max(args.steps, 10)
+        line["decode"] = decode_entry("sink_decode_b64_h32_4p4096", run_decode(steps_d, dec_warm),
+                                      "decode_kernel", "decode_kernel")
+        line["decode_fp8"] = decode_entry("sink_decode_b64_h32_4p4096_e4m3",
+                                          run_decode(steps_d, dec_warm, fp8=True),
+                                          "decode_kernel<fp8>", "decode_kernel_fp8")
+        line["decode_gqa"] = decode_entry("sink_decode_b64_q32_kv8_4p4096",
+                                          run_decode(steps_d, dec_warm, 32, 8),
+                                          "decode_kernel<G=4>", "decode_kernel_gqa")
+        line["decode_gqa_fp8"] = decode_entry("sink_decode_b64_q32_kv8_4p4096_e4m3",
+                                              run_decode(steps_d, dec_warm, 32, 8, fp8=True),
+                                              "decode_kernel<G=4, fp8>", "decode_kernel_gqa_fp8")
+        log(f"decode done: {line['decode']['ms']:.3f} ms, gqa {line['decode_gqa']['ms']:.3f} ms")
+        il = run_interleaved(steps_d, max(args.warmup, 10))
         line["interleaved_layout"] = {
             "rope_apply_ex_k16k": {"ms": round(il["rope_ms"], 4),
                                    "GB/s": round(il["rope_bytes"] / (il["rope_ms"] * 1e-3) / 1e9, 1)},
             "decode_ex_bf16": {"ms": round(il["dec_ms"], 4),
                                "GB/s": round(il["dec_bytes"] / (il["dec_ms"] * 1e-3) / 1e9, 1)}}
-        ft = run_factor_tables(max(args.steps, 10), 10)
+        ft = run_factor_tables(steps_d, 10)
         line["factor_tables"] = {"workload": "rope_tables_build_factors 262144 rows x 64 pairs",
                                  "ms": round(ft["ms"], 4),
                                  "GB/s": round(ft["bytes"] / (ft["ms"] * 1e-3) / 1e9, 1)}
-        sw = run_sink_window_prefill(max(args.steps, 10), args.warmup)
+        sw = run_sink_window_prefill(steps_d, args.warmup)
+        sw_tf = sw["flops"] / (sw["ms"] * 1e-3) / 1e12
         line["sink_window_prefill"] = {
             "workload": "llama7b_prefill_16k_yarn4 attention, 4 sinks + 4096 window",
-            "ms": round(sw["ms"], 4), "flops_per_launch": sw["flops"],
-            "TFLOP/s": round(sw["flops"] / (sw["ms"] * 1e-3) / 1e12, 2),
-            "frac_bf16_peak": round(sw["flops"] / (sw["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic("attn_bf16_pp_kernel_window")}
+            "ms": round(sw["ms"], 4), "TFLOP/s": round(sw_tf, 2),
+            "roofline": roofline("mfma", sw_tf, PEAK_BF16_TFLOPS, "TFLOP/s", "attn_bf16_pp_kernel<window>",
+                                 "attn_bf16_pp_kernel_window", flops_per_launch=sw["flops"])}
         log(f"sink+window prefill done: {sw['ms']:.3f} ms")
         log("ring share: uploading blocks and timing")
         ring = run_ring(max(2, args.steps // 5), 2)
@@ -550,7 +621,7 @@ def main():
                               "TFLOP/s": round(ring["flops"] / (ring["ms"] * 1e-3) / 1e12, 2),
                               "per_call_ms": ring["per_call_ms"]}
     if not args.no_cpu_baseline:
-        log("cpu baseline: fp64 oracle on a bounded sample")
+        log("cpu baseline: fp64 oracle on a bounded sample, one process per core")
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
 

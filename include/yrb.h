@@ -27,6 +27,13 @@
  *    equal to 1; the other strides are given in elements, each in
  *    [0, 2^31) (else YRB_EINVAL).  Base pointers must be 16-byte aligned and
  *    strides multiples of 16 bytes (else YRB_EALIGN).
+ *  - Sizes are int64 and every check on them is free of overflow.  A call
+ *    whose launch would exceed the dispatch limits returns YRB_EINVAL: a
+ *    dispatch counts its work-items in 32 bits (at most 2^24 - 1
+ *    workgroups of 256), so rope_tables_build needs n_pos * d/2 <= 2^32 -
+ *    256, rope_apply S < 2^24 and H < 2^27, the bf16 prefill and
+ *    accumulate ceil(S/256) * B * Hq < 2^24 (fp32: B and Hq <= 65535), and
+ *    the decode B * Hkv < 2^24; positions stay below 2^31.
  *  - dtype: YRB_BF16 (bfloat16 storage, fp32 arithmetic, bf16 MFMA for the
  *    products) or YRB_F32 (fp32 storage and arithmetic).
  *  - head_dim must be 64 or 128.

@@ -206,10 +206,13 @@ def _stream_into_cache(k_seq, v_seq, n_sink, window):
 
 
 @pytest.mark.parametrize("T", [5, 40, 64, 65, 100, 203])
-def test_decode_with_eviction_equals_masked_attention(T):
+def test_decode_with_eviction_equals_masked_attention(T, golden):
     # 14cs17 "Sliding Window + Attention Sinks": the cache is the first s
-    # tokens plus the last w; positions are re-indexed inside the cache.
-    n_sink, window, H, D = 4, 60, 2, 32
+    # tokens plus the last w; positions are re-indexed inside the cache.  The
+    # sink count is the production default of ai-ml-animation-academy
+    # "Production defaults" (golden fixture).
+    n_sink = golden("production_defaults.json")["n_sink"]
+    window, H, D = 60, 2, 32
     k_seq = _rand((T, H, D), 60 + T)
     v_seq = _rand((T, H, D), 61 + T)
     qv = _rand((H, D), 62 + T)
@@ -233,6 +236,22 @@ def test_decode_with_eviction_equals_masked_attention(T):
         p = np.exp(lg - lg.max())
         ref = (p / p.sum()) @ v_seq[kept, h]
         np.testing.assert_allclose(o[h], ref, atol=1e-12)
+
+
+def test_production_default_sinks(golden):
+    # ai-ml-animation-academy "Production defaults": 4 sink tokens stay
+    # pinned beside the sliding window.  The decode workload uses that
+    # count, and 203 tokens streamed through a cache with it leave exactly
+    # tokens 0..3 and the last `window` tokens, the sinks in slots 0..3 and
+    # the window in recency order from the ring head (14cs17 "Sliding
+    # Window + Attention Sinks").
+    n_sink = golden("production_defaults.json")["n_sink"]
+    assert n_sink == 4 and W.SINK_DECODE.n_sink == n_sink
+    window, T = 60, 203
+    tok = np.arange(T, dtype=np.float64)[:, None, None] * np.ones((1, 1, 2))
+    kc, _, L, rh = _stream_into_cache(tok, tok, n_sink, window)
+    kept = [int(kc[0, A.cache_slot(e, n_sink, window, rh), 0]) for e in range(L)]
+    assert kept == list(range(n_sink)) + list(range(T - window, T))
 
 
 def test_decode_ring_head_equals_contiguous_layout():

@@ -43,6 +43,19 @@ bool strides_nonneg(const int64_t* s, int n) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? YRB_OK : YRB_EHIP; }
 
+// Launch-size limits.  A dispatch counts its work-items in 32 bits: with
+// 256 per workgroup, at most 2^24 - 1 workgroups; the fp32 attention grid
+// puts heads and batches in its y and z extents, each below 2^16.
+constexpr int64_t kMaxBlocks = (int64_t(1) << 24) - 1;
+constexpr int64_t kMaxItems = (int64_t(1) << 32) - 256;
+constexpr int64_t kMaxYZ = 65535;
+constexpr int64_t kLim31 = int64_t(1) << 31;
+
+// a * b <= lim for a, b >= 0, without forming a product that may overflow.
+bool mul_le(int64_t a, int64_t b, int64_t lim) { return a == 0 || b <= lim / a; }
+// a + b < lim for a, b >= 0, likewise.
+bool add_lt(int64_t a, int64_t b, int64_t lim) { return a < lim && b < lim - a; }
+
 int check_config(const yrb_rope_config* c) {
   if (!c) return YRB_EINVAL;
   if (c->kind < YRB_ROPE_PLAIN || c->kind > YRB_ROPE_YARN) return YRB_EINVAL;
@@ -115,7 +128,7 @@ int rope_tables_build(const yrb_rope_config* cfg, int64_t pos0, int64_t n_pos, f
   if (pos0 < 0 || n_pos < 0) return YRB_EINVAL;
   if (n_pos > 0 && !cos_sin) return YRB_EINVAL;
   if (n_pos > 0 && !aligned16(cos_sin)) return YRB_EALIGN;
-  if (n_pos > (int64_t(1) << 40) || pos0 > (int64_t(1) << 50)) return YRB_EINVAL;
+  if (!mul_le(n_pos, cfg->head_dim / 2, kMaxItems) || pos0 > (int64_t(1) << 50)) return YRB_EINVAL;
   double th[64];
   compute_theta(cfg, th);
   const int half = cfg->head_dim / 2;
@@ -140,7 +153,7 @@ int rope_tables_build_factors(int32_t head_dim, double base, const double* facto
   if (pos0 < 0 || n_pos < 0) return YRB_EINVAL;
   if (n_pos > 0 && !cos_sin) return YRB_EINVAL;
   if (n_pos > 0 && !aligned16(cos_sin)) return YRB_EALIGN;
-  if (n_pos > (int64_t(1) << 40) || pos0 > (int64_t(1) << 50)) return YRB_EINVAL;
+  if (!mul_le(n_pos, half, kMaxItems) || pos0 > (int64_t(1) << 50)) return YRB_EINVAL;
   double th[64];
   const double d = head_dim;
   for (int i = 0; i < half; ++i) th[i] = std::pow(base, -2.0 * i / d) / factors[i];
@@ -167,13 +180,15 @@ int rope_apply_ex(const void* x, void* y, int32_t dtype, int64_t B, int64_t S, i
   if (!dim_ok(D)) return YRB_EUNSUPPORTED;
   if (B < 0 || S < 0 || H < 0 || n_table_rows < 0 || pos_offset < 0) return YRB_EINVAL;
   if (!x_strides || !y_strides) return YRB_EINVAL;
-  if (B * S * H == 0) return YRB_OK;
+  if (B == 0 || S == 0 || H == 0) return YRB_OK;
+  // one workgroup row per token (S of them), head pairs in its y extent
+  if (S > kMaxBlocks || H > kLim31 / 16) return YRB_EINVAL;
   if (!x || !y || !cos_sin) return YRB_EINVAL;
   if (!strides_nonneg(x_strides, 3) || !strides_nonneg(y_strides, 3)) return YRB_EINVAL;
   if (!aligned16(x) || !aligned16(y) || !aligned16(cos_sin)) return YRB_EALIGN;
   if (!strides_aligned(x_strides, 3, dtype) || !strides_aligned(y_strides, 3, dtype))
     return YRB_EALIGN;
-  if (!pos_ids && pos_offset + S > n_table_rows) return YRB_EINVAL;
+  if (!pos_ids && (S > n_table_rows || pos_offset > n_table_rows - S)) return YRB_EINVAL;
   yrb::RopeArgs r{};
   r.x = x;
   r.y = y;
@@ -206,8 +221,14 @@ int prefill_common(const void* q, const void* k, const void* v, void* o, int32_t
   if (causal != 0 && causal != 1) return YRB_EINVAL;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return YRB_EINVAL;
   if (!strides) return YRB_EINVAL;
-  if (B * S == 0) return YRB_OK;
+  if (B == 0 || S == 0) return YRB_OK;
   if (!q || !k || !v || !o) return YRB_EINVAL;
+  if (S >= kLim31 || Hq >= kLim31) return YRB_EINVAL;
+  // grid: bf16, one workgroup per (256-row query tile, batch, head); fp32,
+  // 64-row tiles with heads and batches in the y and z extents
+  if (dtype == YRB_BF16 ? !mul_le(B, Hq, kMaxBlocks) || !mul_le((S + 255) / 256, B * Hq, kMaxBlocks)
+                        : Hq > kMaxYZ || B > kMaxYZ)
+    return YRB_EINVAL;
   for (int t = 0; t < 4; ++t) {
     if (!strides_nonneg(strides[t], 3)) return YRB_EINVAL;
     if (!strides_aligned(strides[t], 3, dtype)) return YRB_EALIGN;
@@ -215,7 +236,6 @@ int prefill_common(const void* q, const void* k, const void* v, void* o, int32_t
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(workspace))
     return YRB_EALIGN;
-  if (S >= (int64_t(1) << 31)) return YRB_EINVAL;
   if (cos_sin) {
     if (!aligned16(cos_sin)) return YRB_EALIGN;
     if (S > n_table_rows) return YRB_EINVAL;
@@ -298,7 +318,11 @@ int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk, i
   if (!strides) return YRB_EINVAL;
   const bool fin = (flags & YRB_ACC_FINALIZE) != 0;
   if (fin && !o_strides) return YRB_EINVAL;
-  if (B * Sq == 0) return YRB_OK;
+  if (B == 0 || Sq == 0) return YRB_OK;
+  if (!add_lt(q_offset, Sq, kLim31) || !add_lt(k_offset, Sk, kLim31) || Hq >= kLim31) return YRB_EINVAL;
+  if (dtype == YRB_BF16 ? !mul_le(B, Hq, kMaxBlocks) || !mul_le((Sq + 255) / 256, B * Hq, kMaxBlocks)
+                        : Hq > kMaxYZ || B > kMaxYZ)
+    return YRB_EINVAL;
   if (!q || !o_acc || !m || !l) return YRB_EINVAL;
   if (Sk > 0 && (!k_blk || !v_blk)) return YRB_EINVAL;
   if (fin && !o_out) return YRB_EINVAL;
@@ -311,8 +335,6 @@ int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk, i
   if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o_acc) ||
       !aligned16(o_out) || !aligned16(workspace))
     return YRB_EALIGN;
-  const int64_t lim = int64_t(1) << 31;
-  if (q_offset + Sq >= lim || k_offset + Sk >= lim) return YRB_EINVAL;
   const bool future = causal && k_offset > q_offset + Sq - 1;
   if (cos_sin) {
     if (!aligned16(cos_sin)) return YRB_EALIGN;
@@ -367,10 +389,11 @@ int decode_common(int cache_dtype, bool interleaved, const void* q, const void* 
   const int64_t g = Hq / Hkv;
   if (g != 1 && g != 2 && g != 4 && g != 8) return YRB_EUNSUPPORTED;
   if (n_sink < 0 || window < 1) return YRB_EINVAL;
-  if (n_sink + window > (int64_t(1) << 31) - 1) return YRB_EINVAL;
+  if (!add_lt(n_sink, window, kLim31)) return YRB_EINVAL;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return YRB_EINVAL;
   if (!q_strides || !cache_strides || !o_strides) return YRB_EINVAL;
   if (B == 0) return YRB_OK;
+  if (!mul_le(B, Hkv, kMaxBlocks)) return YRB_EINVAL;   // at most one workgroup per (sequence, head)
   if (!q || !k_cache || !v_cache || !o || !cache_len || !cos_sin) return YRB_EINVAL;
   if (!strides_nonneg(q_strides, 2) || !strides_nonneg(cache_strides, 3) ||
       !strides_nonneg(o_strides, 2))
