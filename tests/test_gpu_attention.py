@@ -264,15 +264,21 @@ def _check_prefill_rows(w, heads, rows_per_head=40):
     return worst
 
 
+# Full-size checks: 2048 seeded rows per head (the first and last rows and
+# the tile edges among them) on four heads, each row computed by the oracle
+# on its own.
+FULL_ROWS = 2048
+
+
 def test_prefill_full_llama16k():
     require_gpu()
-    _check_prefill_rows(W.LLAMA_16K, heads=[0, 13, 31])
+    _check_prefill_rows(W.LLAMA_16K, heads=[0, 13, 22, 31], rows_per_head=FULL_ROWS)
 
 
 @pytest.mark.parametrize("kind", [W.PI, W.NTK, W.YARN], ids=["pi", "ntk", "yarn"])
 def test_prefill_full_gqa32k(kind):
     require_gpu()
-    _check_prefill_rows(W.GQA_32K[kind], heads=[0, 5, 30], rows_per_head=24)
+    _check_prefill_rows(W.GQA_32K[kind], heads=[0, 5, 17, 30], rows_per_head=FULL_ROWS)
 
 
 # ---------------------------------------------------------------------------
@@ -293,12 +299,13 @@ def _ring(w_blocks, blk, Hq, Hkv, D, dtype, rope, qi, seed_base=0):
     return tab, th, q, qv, kb, vb, kbv, vbv
 
 
-def _run_ring(q, kb, vb, tab, scale, qi, blk, order, state=None, finalize=True):
+def _run_ring(q, kb, vb, tab, scale, qi, blk, order, state=None, finalize=True, workspace=None):
     out = None
     for t, j in enumerate(order):
         last = t == len(order) - 1
         out = api.attn_block_accumulate(q, kb[j], vb[j], state, qi * blk, j * blk, scale,
-                                        cos_sin=tab, first=(t == 0), finalize=finalize and last)
+                                        cos_sin=tab, first=(t == 0), finalize=finalize and last,
+                                        workspace=workspace)
     return out
 
 
@@ -411,12 +418,12 @@ def test_accumulate_full_ring_share():
     st = api.AccState.empty(1, w.block, w.n_q_heads, w.head_dim)
     order = W.ring_order(w)
     say("attn_block_accumulate ring share 8x32768 full size")
-    o = _run_ring(q, kb, vb, tab, scale, w.q_block_index, w.block, order, st)
+    o = _run_ring(q, kb, vb, tab, scale, w.q_block_index, w.block, order, st, workspace=api.new_workspace())
     torch.cuda.synchronize()
     offs = [j * w.block for j in range(w.n_blocks)]
     worst = 0.0
-    for h in (0, 7):
-        rows = _sample_rows(w.block, 50 + h, 12)
+    for h in (0, 3, 5, 7):
+        rows = _sample_rows(w.block, 50 + h, FULL_ROWS)
         o_ref, m_ref, _, _ = A.ring_share(qv, kbv, vbv, th, scale, w.q_block_index * w.block,
                                           offs, order=order, rows=rows, heads=[h])
         worst = max(worst, max_abs(host(o[0, rows, h]), o_ref[0, :, 0]))

@@ -108,7 +108,8 @@ def test_prefill_sink_window_wide_window_is_causal_prefill():
 
 def test_prefill_sink_window_full_llama16k():
     # The 16k Llama-7B-like prefill (32 heads, d=128, YaRN s=4) with 4 sinks
-    # and a 4096-token window: sampled rows of three heads against the oracle.
+    # and a 4096-token window, launched as the bench times it (with a
+    # workspace): 512 sampled rows of four heads against the oracle.
     require_gpu()
     import torch
     w = W.LLAMA_16K
@@ -118,13 +119,14 @@ def test_prefill_sink_window_full_llama16k():
     say(f"attn_prefill_sink_window {w.name} sink={n_sink} window={window}")
     kr = api.rope_apply(k, tab)
     del k
-    o = api.attn_prefill_sink_window(q, kr, v, scale, n_sink, window, cos_sin=tab)
+    o = api.attn_prefill_sink_window(q, kr, v, scale, n_sink, window, cos_sin=tab,
+                                     workspace=api.new_workspace())
     torch.cuda.synchronize()
     edges = [0, 3, 4, 63, 64, 255, 256, window - 1, window, window + 1, window + 63, window + 64,
              w.seq // 2, w.seq - 257, w.seq - 1]
     worst = 0.0
-    for h in (0, 13, 31):
-        rows = synth.sample_rows(w.seq, 30, 2000 + h, must=edges)
+    for h in (0, 13, 22, 31):
+        rows = synth.sample_rows(w.seq, 512, 2000 + h, must=edges)
         got = host(o[0, rows, h])
         ref = A.prefill(qv, kv, vv, th, scale, rows=rows, heads=[h], n_sink=n_sink,
                         window=window)[0, :, 0]
@@ -134,7 +136,7 @@ def test_prefill_sink_window_full_llama16k():
 
 def test_prefill_sink_window_full_gqa32k():
     # The 32k GQA prefill (YaRN s=8) with 4 sinks and an 8192-token window:
-    # sampled rows of query heads from different key groups.
+    # 512 sampled rows of four query heads from different key groups.
     require_gpu()
     import torch
     w = W.GQA_32K[W.YARN]
@@ -148,8 +150,8 @@ def test_prefill_sink_window_full_gqa32k():
     torch.cuda.synchronize()
     edges = [0, 5, 255, 256, window - 1, window, window + 255, window + 256, w.seq - 1]
     worst = 0.0
-    for h in (0, w.n_q_heads // 2 + 1, w.n_q_heads - 1):
-        rows = synth.sample_rows(w.seq, 20, 3000 + h, must=edges)
+    for h in (0, 9, w.n_q_heads // 2 + 1, w.n_q_heads - 1):
+        rows = synth.sample_rows(w.seq, 512, 3000 + h, must=edges)
         got = host(o[0, rows, h])
         ref = A.prefill(qv, kv, vv, th, scale, rows=rows, heads=[h], n_sink=n_sink,
                         window=window)[0, :, 0]
