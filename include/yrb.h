@@ -56,6 +56,14 @@
 
 #include <stdint.h>
 
+/* The library is built with hidden visibility; these calls alone are
+ * exported. */
+#if defined(__GNUC__) || defined(__clang__)
+#define YRB_API __attribute__((visibility("default")))
+#else
+#define YRB_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -129,7 +137,7 @@ typedef struct yrb_rope_config {
  *   inv_freq_out   host [d/2] fp64 theta'_i, or NULL.
  *   attn_factor_out host fp64, or NULL.
  */
-int rope_tables_build(const yrb_rope_config* cfg, int64_t pos0, int64_t n_pos,
+YRB_API int rope_tables_build(const yrb_rope_config* cfg, int64_t pos0, int64_t n_pos,
                       float* cos_sin, double* inv_freq_out, double* attn_factor_out,
                       void* stream);
 
@@ -147,7 +155,7 @@ int rope_tables_build(const yrb_rope_config* cfg, int64_t pos0, int64_t n_pos,
  *                  YRB_EINVAL; nothing is launched).
  *   pos0, n_pos, cos_sin, inv_freq_out   as for rope_tables_build.
  */
-int rope_tables_build_factors(int32_t head_dim, double base, const double* factors,
+YRB_API int rope_tables_build_factors(int32_t head_dim, double base, const double* factors,
                               int64_t pos0, int64_t n_pos, float* cos_sin,
                               double* inv_freq_out, void* stream);
 
@@ -167,7 +175,7 @@ int rope_tables_build_factors(int32_t head_dim, double base, const double* facto
  *                  [0, n_table_rows) is not read: that token's output is NaN.
  * Arithmetic is fp32; bf16 results are rounded to nearest even.
  */
-int rope_apply(const void* x, void* y, int32_t dtype,
+YRB_API int rope_apply(const void* x, void* y, int32_t dtype,
                int64_t B, int64_t S, int64_t H, int64_t D,
                const int64_t x_strides[3], const int64_t y_strides[3],
                const float* cos_sin, int64_t n_table_rows,
@@ -181,7 +189,7 @@ int rope_apply(const void* x, void* y, int32_t dtype,
  * A model in the interleaved layout rotates Q and K with this call and
  * passes cos_sin = NULL to attn_prefill_blockwise / attn_block_accumulate.
  */
-int rope_apply_ex(const void* x, void* y, int32_t dtype,
+YRB_API int rope_apply_ex(const void* x, void* y, int32_t dtype,
                   int64_t B, int64_t S, int64_t H, int64_t D,
                   const int64_t x_strides[3], const int64_t y_strides[3],
                   const float* cos_sin, int64_t n_table_rows,
@@ -213,7 +221,7 @@ int rope_apply_ex(const void* x, void* y, int32_t dtype,
  * bf16: products on bf16 MFMA with fp32 accumulation; probabilities are
  * rounded to bf16 before the P V product; output rounded to nearest even.
  */
-int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o,
+YRB_API int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o,
                            int32_t dtype, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
                            int64_t D, const int64_t strides[4][3],
                            const float* cos_sin, int64_t n_table_rows,
@@ -236,7 +244,7 @@ int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o,
  *   window         >= 1; values above S act as S (plain causal).
  * dtype must be YRB_BF16 (YRB_EUNSUPPORTED otherwise); S < 2^30.
  */
-int attn_prefill_sink_window(const void* q, const void* k, const void* v, void* o,
+YRB_API int attn_prefill_sink_window(const void* q, const void* k, const void* v, void* o,
                              int32_t dtype, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
                              int64_t D, const int64_t strides[4][3],
                              const float* cos_sin, int64_t n_table_rows,
@@ -272,7 +280,7 @@ int attn_prefill_sink_window(const void* q, const void* k, const void* v, void* 
  * still initialises (FIRST) and finalises (FINALIZE) as asked.  Folding the
  * blocks in any order gives the same result up to rounding.
  */
-int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk,
+YRB_API int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk,
                           int32_t dtype, int64_t B, int64_t Sq, int64_t Sk,
                           int64_t Hq, int64_t Hkv, int64_t D,
                           const int64_t strides[3][3], int64_t q_offset, int64_t k_offset,
@@ -302,7 +310,7 @@ int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk,
  * len = 0 gives o = 0; a len or ring_head out of range gives o = NaN for
  * that sequence (nothing out of range is read).  Needs n_table_rows >= C.
  */
-int attn_decode_sink_window(const void* q, const void* k_cache, const void* v_cache, void* o,
+YRB_API int attn_decode_sink_window(const void* q, const void* k_cache, const void* v_cache, void* o,
                             int32_t dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
                             int64_t n_sink, int64_t window,
                             const int64_t q_strides[2], const int64_t cache_strides[3],
@@ -329,7 +337,7 @@ int attn_decode_sink_window(const void* q, const void* k_cache, const void* v_ca
  *   v_scale        device fp32 [B][Hkv] contiguous, or NULL (= 1).
  * A NaN code reaches the output as NaN.
  */
-int attn_decode_sink_window_fp8(const void* q, const void* k_cache, const void* v_cache, void* o,
+YRB_API int attn_decode_sink_window_fp8(const void* q, const void* k_cache, const void* v_cache, void* o,
                                 int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
                                 int64_t n_sink, int64_t window,
                                 const int64_t q_strides[2], const int64_t cache_strides[3],
@@ -348,7 +356,7 @@ int attn_decode_sink_window_fp8(const void* q, const void* k_cache, const void* 
  * and alignment follow the cache type as in the two calls above; scales are
  * ignored for bf16.
  */
-int attn_decode_sink_window_ex(const void* q, const void* k_cache, const void* v_cache, void* o,
+YRB_API int attn_decode_sink_window_ex(const void* q, const void* k_cache, const void* v_cache, void* o,
                                int32_t cache_dtype, int32_t layout,
                                int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
                                int64_t n_sink, int64_t window,
@@ -360,7 +368,7 @@ int attn_decode_sink_window_ex(const void* q, const void* k_cache, const void* v
                                float softmax_scale, void* stream);
 
 /* Human-readable name of a status code (static string). */
-const char* yrb_status_str(int status);
+YRB_API const char* yrb_status_str(int status);
 
 #ifdef __cplusplus
 }

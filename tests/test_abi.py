@@ -28,7 +28,8 @@ MISALIGNED = 0x10008
 def declared_functions():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", txt, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:YRB_API\s+)?(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", txt,
+                                 flags=re.M)))
 
 
 def test_header_declares_the_five_calls():
@@ -44,6 +45,19 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
     assert L.yrb_status_str(0) == b"ok"
     assert L.yrb_status_str(-2).startswith(b"unsupported")
+
+
+def test_library_exports_nothing_else():
+    # Built with hidden visibility: the functions the header declares are the
+    # library's only exported code; internal launchers and kernels stay local.
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("needs nm")
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    funcs = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] == "T"}
+    assert funcs == set(declared_functions()), funcs ^ set(declared_functions())
 
 
 @pytest.mark.parametrize("kind", [R.PLAIN, R.PI, R.NTK, R.YARN])

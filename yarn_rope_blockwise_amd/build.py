@@ -23,7 +23,7 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code; the compiler
 # still emits ordinary scalar fp32 and the MFMA/DS/LDS-DMA instructions.
-FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]
