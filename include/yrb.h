@@ -229,6 +229,29 @@ YRB_API int attn_prefill_blockwise(const void* q, const void* k, const void* v, 
                            void* workspace, void* stream);
 
 /*
+ * attn_prefill_blockwise_noalloc -- attn_prefill_blockwise without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The work-claim counter comes from a static device array of
+ * YRB_WORKSPACE_BYTES in the library, one copy per GPU, held until the
+ * process ends; its address on a device is looked up on the first call
+ * there.  It is the same size for every input, so no size is too large for
+ * it.  Every call on a GPU shares that GPU's copy: calls that may overlap on
+ * one GPU (two streams, or one captured graph replayed on two streams at
+ * once) race on it and may skip or repeat work items; give such callers
+ * attn_prefill_blockwise with workspaces of their own.  The counter needs
+ * no clearing between calls: any value it holds claims every item once.
+ * Arguments, results and errors otherwise as attn_prefill_blockwise; this
+ * call allocates nothing and never synchronises.  YRB_EHIP if the array's
+ * address cannot be found, YRB_EUNSUPPORTED past the 64th device.
+ */
+YRB_API int attn_prefill_blockwise_noalloc(const void* q, const void* k, const void* v, void* o,
+                                   int32_t dtype, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                   int64_t D, const int64_t strides[4][3],
+                                   const float* cos_sin, int64_t n_table_rows,
+                                   float softmax_scale, int32_t causal, float* lse, void* stream);
+
+/*
  * attn_prefill_sink_window -- attn_prefill_blockwise under the attention-sink
  * plus sliding-window mask, the prefill counterpart of the decode cache
  * ([C] "Sliding Window + Attention Sinks": the first s tokens and the last w

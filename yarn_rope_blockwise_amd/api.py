@@ -22,7 +22,7 @@ LAYOUT_HALF, LAYOUT_INTERLEAVED = 0, 1
 ACC_FIRST, ACC_FINALIZE = 1, 2
 WORKSPACE_BYTES = 64      # YRB_WORKSPACE_BYTES
 EXPORTS = ("rope_tables_build", "rope_tables_build_factors", "rope_apply", "attn_prefill_blockwise",
-           "attn_prefill_sink_window",
+           "attn_prefill_blockwise_noalloc", "attn_prefill_sink_window",
            "attn_block_accumulate", "attn_decode_sink_window", "attn_decode_sink_window_fp8",
            "rope_apply_ex", "attn_decode_sink_window_ex", "yrb_status_str")
 
@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_blockwise.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64,
                                              _i64, _i64p, _vp, _i64, ctypes.c_float, _i32, _vp,
                                              _vp, _vp]
+        L.attn_prefill_blockwise_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64,
+                                                     _i64, _i64, _i64p, _vp, _i64, ctypes.c_float,
+                                                     _i32, _vp, _vp]
         L.attn_prefill_sink_window.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64,
                                                _i64, _i64p, _vp, _i64, ctypes.c_float, _i64, _i64,
                                                _vp, _vp, _vp]
@@ -263,6 +266,25 @@ def attn_prefill_blockwise(q, k, v, softmax_scale: float, cos_sin=None, causal: 
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), B, S, Hq, Hkv, D, strides,
         _ptr(cos_sin), n_rows, float(softmax_scale), int(bool(causal)), _ptr(lse),
         _ptr(workspace), _stream()))
+    return out
+
+
+def attn_prefill_blockwise_noalloc(q, k, v, softmax_scale: float, cos_sin=None,
+                                   causal: bool = True, out=None, lse=None):
+    """attn_prefill_blockwise with the claim counter in the library's static
+    per-GPU array instead of a workspace (for callers that cannot allocate;
+    calls that overlap on one GPU race on it).  ``out`` must be given when
+    the caller cannot allocate it here."""
+    import torch
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    strides = _arr(_bsh_strides(q) + _bsh_strides(k) + _bsh_strides(v) + _bsh_strides(out))
+    n_rows = 0 if cos_sin is None else cos_sin.shape[0]
+    _check("attn_prefill_blockwise_noalloc", lib().attn_prefill_blockwise_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), B, S, Hq, Hkv, D, strides,
+        _ptr(cos_sin), n_rows, float(softmax_scale), int(bool(causal)), _ptr(lse), _stream()))
     return out
 
 
