@@ -49,23 +49,32 @@ METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HB
 
 # HBM bytes per launch from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE,
 # KiB per dispatch), scaled by what the same counters read for a plain 1 GiB
-# device copy (FETCH x1.99994, WRITE x1.0).  Each figure holds only for the
+# device copy (FETCH x1.99996, WRITE x1.0).  Each figure holds only for the
 # kernel sources it was taken on: the sha256 over the listed files must match,
 # else the line reports traffic null.
 _PP = ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h")
 _DEC = ("csrc/decode.hip", "csrc/common.h")
 MEASURED_TRAFFIC = {
-    "attn_bf16_pp_kernel": {"files": _PP, "sha256": None, "fetch_kib": 0, "write_kib": 0},
-    "attn_bf16_pp_kernel_gqa_prefill_32k_pi8": {"files": _PP, "sha256": None, "fetch_kib": 0, "write_kib": 0},
-    "attn_bf16_pp_kernel_gqa_prefill_32k_ntk8": {"files": _PP, "sha256": None, "fetch_kib": 0, "write_kib": 0},
-    "attn_bf16_pp_kernel_gqa_prefill_32k_yarn8": {"files": _PP, "sha256": None, "fetch_kib": 0, "write_kib": 0},
-    "attn_bf16_pp_kernel_window": {"files": _PP, "sha256": None, "fetch_kib": 0, "write_kib": 0},
-    "decode_kernel": {"files": _DEC, "sha256": None, "fetch_kib": 0, "write_kib": 0},
-    "decode_kernel_fp8": {"files": _DEC, "sha256": None, "fetch_kib": 0, "write_kib": 0},
-    "decode_kernel_gqa": {"files": _DEC, "sha256": None, "fetch_kib": 0, "write_kib": 0},
-    "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": None, "fetch_kib": 0, "write_kib": 0},
+    "attn_bf16_pp_kernel": {"files": _PP, "sha256": "168a3f1c150ce3c7df964be10ab06f3e71f38bd2cb3b0560d40e873d550a2266",
+                           "fetch_kib": 1038593, "write_kib": 131091},
+    "attn_bf16_pp_kernel_gqa_prefill_32k_pi8": {"files": _PP, "sha256": "168a3f1c150ce3c7df964be10ab06f3e71f38bd2cb3b0560d40e873d550a2266",
+                                               "fetch_kib": 1438503, "write_kib": 262182},
+    "attn_bf16_pp_kernel_gqa_prefill_32k_ntk8": {"files": _PP, "sha256": "168a3f1c150ce3c7df964be10ab06f3e71f38bd2cb3b0560d40e873d550a2266",
+                                                "fetch_kib": 1465073, "write_kib": 262182},
+    "attn_bf16_pp_kernel_gqa_prefill_32k_yarn8": {"files": _PP, "sha256": "168a3f1c150ce3c7df964be10ab06f3e71f38bd2cb3b0560d40e873d550a2266",
+                                                 "fetch_kib": 1402415, "write_kib": 262182},
+    "attn_bf16_pp_kernel_window": {"files": _PP, "sha256": "168a3f1c150ce3c7df964be10ab06f3e71f38bd2cb3b0560d40e873d550a2266",
+                                  "fetch_kib": 722197, "write_kib": 131091},
+    "decode_kernel": {"files": _DEC, "sha256": "7679fb96bda5ccc7e3d8990695a16273a33145cd91de606d82f822955caae813",
+                     "fetch_kib": 2100193, "write_kib": 512},
+    "decode_kernel_fp8": {"files": _DEC, "sha256": "7679fb96bda5ccc7e3d8990695a16273a33145cd91de606d82f822955caae813",
+                         "fetch_kib": 1053152, "write_kib": 512},
+    "decode_kernel_gqa": {"files": _DEC, "sha256": "7679fb96bda5ccc7e3d8990695a16273a33145cd91de606d82f822955caae813",
+                         "fetch_kib": 526616, "write_kib": 3072},
+    "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": "7679fb96bda5ccc7e3d8990695a16273a33145cd91de606d82f822955caae813",
+                             "fetch_kib": 263112, "write_kib": 512},
 }
-FETCH_FACTOR, WRITE_FACTOR = 1.99994, 1.0
+FETCH_FACTOR, WRITE_FACTOR = 1.99996, 1.0
 
 
 def sources_sha256(files) -> str:
