@@ -90,12 +90,17 @@ struct DecCfg {
   static constexpr int TABB = 2 * kKPS * TROWB;      // LDS bytes of R(j) and R(32 j), j < 32
   static constexpr bool ANCHOR_Q = G <= 2;           // re-anchor the query, else compose R(e) per key
   // Rounds of K/V loads in flight (register sets of the ring): a step's
-  // worth, two for an fp8 cache with one query head per key head (its
-  // chunks are half the size; measured 3-4 % faster), half of one when the
-  // per-head query and output registers leave less room.
-  static constexpr int PD = (FP8 && G == 1) ? 2 * ROUNDS : G <= 2 ? ROUNDS : (ROUNDS > 1 ? ROUNDS / 2 : 1);
-  // Waves per SIMD the registers are sized for.
-  static constexpr int WAVES_PER_EU = G <= 4 ? 2 : 1;
+  // worth, half of one when the per-head query and output registers leave
+  // less room.
+  static constexpr int PD = G <= 2 ? ROUNDS : (ROUNDS > 1 ? ROUNDS / 2 : 1);
+  // Waves per SIMD the registers are sized for: an fp8 cache with one query
+  // head per key head fits four (its key and value chunks are half the
+  // size), whose latency hiding it needs: it has twice the arithmetic per
+  // byte of a bf16 cache.
+  static constexpr int WAVES_PER_EU = (FP8 && G == 1) ? 4 : G <= 4 ? 2 : 1;
+  // Waves a launch aims at (the host splits heads into parts until it has
+  // them): every SIMD's share at that occupancy, at least two per SIMD.
+  static constexpr int64_t TARGET_WAVES = 1024 * (WAVES_PER_EU > 2 ? WAVES_PER_EU : 2);
   static_assert(ROUNDS * KPW == kKPS, "a step is whole rounds");
   static_assert(ROUNDS % PD == 0 || PD % ROUNDS == 0, "ring sets repeat within U steps");
   static constexpr int U = PD > ROUNDS ? PD / ROUNDS : 1;   // steps per pass of the loop
@@ -253,6 +258,10 @@ void decode_kernel(DecodeArgs a, int parts) {
   // its current R(1024 a).
   __shared__ __attribute__((aligned(16))) char tab_raw[Cfg::TABB + kWaves * Cfg::TROWB];
   __shared__ __attribute__((aligned(16))) float merge[kWaves][MERGE_F];
+  // ANCHOR_Q: each wave's query rotated to R(1024 a) (a the current 1024-
+  // entry block), per head and lane chunk: the step reads it rather than
+  // hold it in registers.
+  __shared__ __attribute__((aligned(16))) float qrow[kWaves][Cfg::ANCHOR_Q ? G * D : 1];
   YRB_LDS char* const tab = (YRB_LDS char*)tab_raw;
 
   const int lane = threadIdx.x & 63;
@@ -296,26 +305,28 @@ void decode_kernel(DecodeArgs a, int parts) {
   const float v_deq = (FP8 && a.v_scale) ? a.v_scale[b * a.Hkv + hk] : 1.0f;
   const float scale_log2 = a.softmax_scale * kLog2e * k_deq;
 
-  // Query of each of the G heads rotated at len - 1 and multiplied by the
-  // logit scale (log2 units), as fp32 pairs.
-  float qx[G][8], qz[G][8];
-  {
+  // Query of head g rotated at position `pos` and multiplied by the logit
+  // scale (log2 units), as fp32 pairs.
+  auto query_at = [&](int g, int pos, float (&x)[8], float (&z)[8]) {
     float c[8], s[8];
-    row_pairs<D, IL>(a.cos_sin + (int64_t)(len > 0 ? len - 1 : 0) * D, cc, c, s);
+    row_pairs<D, IL>(a.cos_sin + (int64_t)pos * D, cc, c, s);
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + b * a.qs[0] + (int64_t)(hk * G + g) * a.qs[1];
+    float qa[8], qb[8];
+    unpack8(*reinterpret_cast<const u32x4*>(qp + 8 * cc), qa);
+    unpack8(*reinterpret_cast<const u32x4*>(qp + D / 2 + 8 * cc), qb);
+    pairs_of<IL>(qa, qb, x, z);
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + b * a.qs[0] + (int64_t)(hk * G + g) * a.qs[1];
-      float qa[8], qb[8];
-      unpack8(*reinterpret_cast<const u32x4*>(qp + 8 * cc), qa);
-      unpack8(*reinterpret_cast<const u32x4*>(qp + D / 2 + 8 * cc), qb);
-      pairs_of<IL>(qa, qb, qx[g], qz[g]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        rot(qx[g][u], qz[g][u], c[u], s[u]);
-        qx[g][u] *= scale_log2;
-        qz[g][u] *= scale_log2;
-      }
+    for (int u = 0; u < 8; ++u) {
+      rot(x[u], z[u], c[u], s[u]);
+      x[u] *= scale_log2;
+      z[u] *= scale_log2;
     }
+  };
+  // Compose mode: the query at len - 1, held for the whole launch.
+  float qx[Cfg::ANCHOR_Q ? 1 : G][8], qz[Cfg::ANCHOR_Q ? 1 : G][8];
+  if constexpr (!Cfg::ANCHOR_Q) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) query_at(g, len > 0 ? len - 1 : 0, qx[g], qz[g]);
   }
 
   // Running max, sum and output per head.  The max is kept per key group
@@ -376,33 +387,57 @@ void decode_kernel(DecodeArgs a, int parts) {
       const int a2 = A >> 10, b1 = (A >> 5) & 31;
       const int jw = 2 * kKPS + wave;
       if (a2 != a_cur) {
-        float c2[8], s2[8];
-        row_pairs<D, IL>(a.cos_sin + (int64_t)(a2 << 10) * D, cc, c2, s2);
-        if (kg == 0) {
-          YRB_LDS char* row = tab + jw * Cfg::TROWB;
+        // ANCHOR_Q: R(1024 a2)^T R(len - 1) q = R(len - 1 - 1024 a2) q, into
+        // the wave's query rows; compose: R(1024 a2) into its table row.
+        if constexpr (Cfg::ANCHOR_Q) {
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const f32x4 t = {c2[2 * w], s2[2 * w], c2[2 * w + 1], s2[2 * w + 1]};
-            *reinterpret_cast<YRB_LDS f32x4*>(row + 16 * tab_phys<D>(jw, tab_chunk<D, IL>(cc, w))) = t;
+          for (int g = 0; g < G; ++g) {
+            float x[8], z[8];
+            query_at(g, len - 1 - (a2 << 10), x, z);
+            if (kg == 0) {
+              float* qr = &qrow[wave][(g * TPK + cc) * 16];
+#pragma unroll
+              for (int w = 0; w < 8; ++w) {
+                qr[w] = x[w];
+                qr[8 + w] = z[w];
+              }
+            }
+          }
+        } else {
+          float c2[8], s2[8];
+          row_pairs<D, IL>(a.cos_sin + (int64_t)(a2 << 10) * D, cc, c2, s2);
+          if (kg == 0) {
+            YRB_LDS char* row = tab + jw * Cfg::TROWB;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const f32x4 t = {c2[2 * w], s2[2 * w], c2[2 * w + 1], s2[2 * w + 1]};
+              *reinterpret_cast<YRB_LDS f32x4*>(row + 16 * tab_phys<D>(jw, tab_chunk<D, IL>(cc, w))) = t;
+            }
           }
         }
         a_cur = a2;
+        // the lanes of key group 0 wrote what every lane reads next: keep
+        // the compiler from moving those reads above the writes (a wave's
+        // LDS accesses complete in order)
+        __builtin_amdgcn_wave_barrier();
       }
-      float c2[8], s2[8], c1[8], s1[8];
-      lds_pairs<D, IL>(tab, jw, cc, c2, s2);
+      float c1[8], s1[8];
       lds_pairs<D, IL>(tab, kKPS + b1, cc, c1, s1);
       float qx_s[G][8], qz_s[G][8];   // ANCHOR_Q: the query this step's keys meet
       if constexpr (Cfg::ANCHOR_Q) {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g) {
+          const float* qr = &qrow[wave][(g * TPK + cc) * 16];
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
-            qx_s[g][w] = qx[g][w];
-            qz_s[g][w] = qz[g][w];
-            rot_t(qx_s[g][w], qz_s[g][w], c2[w], s2[w]);
+            qx_s[g][w] = qr[w];
+            qz_s[g][w] = qr[8 + w];
             rot_t(qx_s[g][w], qz_s[g][w], c1[w], s1[w]);
           }
+        }
       } else {
+        float c2[8], s2[8];
+        lds_pairs<D, IL>(tab, jw, cc, c2, s2);
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
           rc[w] = c2[w];
@@ -433,8 +468,8 @@ void decode_kernel(DecodeArgs a, int parts) {
           float acc = 0.f;
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
-            const float qxw = Cfg::ANCHOR_Q ? qx_s[g][w] : qx[g][w];
-            const float qzw = Cfg::ANCHOR_Q ? qz_s[g][w] : qz[g][w];
+            const float qxw = Cfg::ANCHOR_Q ? qx_s[g][w] : qx[Cfg::ANCHOR_Q ? 0 : g][w];
+            const float qzw = Cfg::ANCHOR_Q ? qz_s[g][w] : qz[Cfg::ANCHOR_Q ? 0 : g][w];
             acc = __builtin_fmaf(qxw, x[w], __builtin_fmaf(qzw, z[w], acc));
           }
           acc = group_sum<TPK>(acc);
@@ -573,14 +608,13 @@ void decode_kernel(DecodeArgs a, int parts) {
   }
 }
 
-// Waves that split one head's entries: enough (sequence, head, part) units
-// to give every SIMD two waves, at most 4.
-constexpr int64_t kTargetWaves = 2048;
 
 template <int D, int G, bool FP8, bool IL>
 hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
+  // Waves that split one head's entries: enough (sequence, head, part)
+  // units for the occupancy the kernel is built for, at most 4 parts.
   int parts = 1;
-  while (parts < kWaves && a.B * a.Hkv * parts < kTargetWaves) parts *= 2;
+  while (parts < kWaves && a.B * a.Hkv * parts < DecCfg<D, G, FP8>::TARGET_WAVES) parts *= 2;
   const int heads_per_wg = kWaves / parts;
   const int64_t blocks = a.B * ((a.Hkv + heads_per_wg - 1) / heads_per_wg);
   if (blocks == 0) return hipSuccess;
