@@ -33,7 +33,11 @@
  *    workgroups of 256), so rope_tables_build needs n_pos * d/2 <= 2^32 -
  *    256, rope_apply S < 2^24 and H < 2^27, the bf16 prefill and
  *    accumulate ceil(S/256) * B * Hq < 2^24 (fp32: B and Hq <= 65535), and
- *    the decode B * Hkv < 2^24; positions stay below 2^31.
+ *    the decode B * Hkv < 2^24; positions stay below 2^31.  The decode
+ *    addresses one (sequence, head)'s cache with 32-bit offsets: it needs
+ *    n_sink + window <= 2^24, the entry stride below 2^24 bytes and
+ *    (n_sink + window - 1) * entry stride + head_dim elements within 2^32
+ *    bytes (else YRB_EINVAL).
  *  - dtype: YRB_BF16 (bfloat16 storage, fp32 arithmetic, bf16 MFMA for the
  *    products) or YRB_F32 (fp32 storage and arithmetic).
  *  - head_dim must be 64 or 128.

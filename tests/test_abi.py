@@ -277,6 +277,15 @@ def test_decode_validation():
     assert _decode(k=MISALIGNED) == EALIGN
     assert _decode(cs=_strides(4 * 64 * 128, 64 * 128, 100)) == EALIGN
     assert _decode(B=0) == OK
+    # 32-bit offsets inside one (sequence, head): entries, entry stride, span.
+    # A call within the limits stops at the next check (a misaligned query).
+    assert _decode(sink=1, win=(1 << 24) - 1, rows=1 << 24, cs=_strides(0, 0, 0), q=MISALIGNED) == EALIGN
+    assert _decode(sink=2, win=(1 << 24) - 1, rows=1 << 25, cs=_strides(0, 0, 0)) == EINVAL
+    assert _decode(cs=_strides(0, 0, (1 << 23) - 8), q=MISALIGNED) == EALIGN
+    assert _decode(cs=_strides(0, 0, 1 << 23)) == EINVAL                 # 2^24 bytes per entry
+    # 2^14 entries of 2^18 bytes: the last byte at 2^32 - 2^18 + 255; one entry more passes 2^32
+    assert _decode(win=(1 << 14) - 4, rows=1 << 15, cs=_strides(0, 0, 1 << 17), q=MISALIGNED) == EALIGN
+    assert _decode(win=(1 << 14) - 3, rows=1 << 15, cs=_strides(0, 0, 1 << 17)) == EINVAL
 
 
 def _decode_fp8(**over):

@@ -6,7 +6,7 @@ from oracle import attention as A
 from oracle import rope as R
 from yarn_rope_blockwise_amd import api, synth
 from yarn_rope_blockwise_amd import workloads as W
-from tests.gpu_helpers import BF16_TOL, draw, host, max_abs, require_gpu, say
+from tests.gpu_helpers import BF16_TOL, dev_tensor, draw, host, max_abs, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -241,6 +241,68 @@ def test_decode_fp8_nan_code_reaches_output():
     torch.cuda.synchronize()
     got = host(o)
     assert np.isnan(got[0, 1, 5]) and not np.isnan(got[0, 0]).any()
+
+
+def test_decode_fp8_nan_key_code_reaches_output():
+    # A NaN code in a visible key row makes that head's logit, and so its
+    # whole output, NaN; the other head is untouched.
+    require_gpu()
+    import torch
+    n_sink, window, D = 4, 60, 128
+    C = n_sink + window
+    rope = W.Rope(W.PLAIN, D, 1e4, 1.0, 4096)
+    tab, th, scale, (qv, kv, vv), q, dv = _fp8_case(1, 2, 2, D, n_sink, window, [C], None, rope,
+                                                    seed=91)
+    dv["k"][0, 1, 10, 5] = 0xFF
+    say("attn_decode_sink_window_fp8 NaN key code")
+    o = api.attn_decode_sink_window_fp8(q, dv["k"], dv["v"], dv["lens"], n_sink, window, tab,
+                                        scale, k_scale=dv["ks"], v_scale=dv["vs"])
+    torch.cuda.synchronize()
+    got = host(o)
+    assert np.isnan(got[0, 1]).all() and not np.isnan(got[0, 0]).any()
+
+
+@pytest.mark.parametrize("G,D,IL", [(1, 128, False), (1, 64, False), (2, 128, True), (4, 128, False),
+                                    (8, 64, True)])
+def test_decode_fp8_every_code(G, D, IL):
+    # Every non-NaN E4M3 code, subnormals and the largest included: each of
+    # the 16 (sequence, key head) pairs draws its K and V codes from one
+    # exponent field, with scales that bring its values to about 0.5 .. 0.94,
+    # so every field is decoded at full relative weight; the queries are
+    # multiplied by 8 (exact) so that the softmax is peaked and the output
+    # follows the logits closely.
+    require_gpu()
+    import torch
+    from oracle import fp8
+    B, Hkv, n_sink, window = 2, 8, 4, 300
+    Hq, C = Hkv * G, n_sink + window
+    fields = np.arange(16).reshape(B, Hkv)
+    rope = W.Rope(W.YARN, D, 1e4, 4.0, 128)
+    tab, th, _ = api.rope_tables_build(api.RopeConfig.of(rope), C)
+    qv0, _ = draw((B, Hq, D), 95, "bf16")
+    qv = qv0 * 8.0
+    q = dev_tensor(qv, synth.bf16_bits_from_f32(qv.astype(np.float32)), "bf16")
+    kc = synth.e4m3_codes_banded((B, Hkv, C, D), 96, fields)
+    vc = synth.e4m3_codes_banded((B, Hkv, C, D), 97, fields[::-1])
+    band = lambda f: (2.0 ** (7 - np.maximum(f, 1)) * 0.5).astype(np.float32)
+    ks, vs = band(fields), band(fields[::-1])
+    kv = fp8.e4m3_decode(kc) * ks.astype(np.float64)[:, :, None, None]
+    vv = fp8.e4m3_decode(vc) * vs.astype(np.float64)[:, :, None, None]
+    rh = np.array([17, window - 1], np.int32)
+    scale = R.softmax_scale(rope.kind, rope.scale, D)
+    say(f"attn_decode_sink_window_ex fp8 every code G={G} D={D} IL={IL}")
+    o = api.attn_decode_sink_window_ex(
+        q, torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda(),
+        torch.tensor([C, C], dtype=torch.int32, device="cuda"), n_sink, window, tab, scale,
+        ring_head=torch.from_numpy(rh).cuda(), k_scale=torch.from_numpy(ks).cuda(),
+        v_scale=torch.from_numpy(vs).cuda(),
+        layout=api.LAYOUT_INTERLEAVED if IL else api.LAYOUT_HALF)
+    torch.cuda.synchronize()
+    got = host(o)
+    ref = A.decode_sink_window(qv, kv, vv, th, scale, n_sink, window, [C, C], rh,
+                               layout="interleaved" if IL else "half")
+    err = max_abs(got, ref)
+    assert err <= BF16_TOL, err
 
 
 @pytest.mark.parametrize("fp8", [False, True])

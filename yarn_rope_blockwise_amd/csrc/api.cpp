@@ -401,6 +401,14 @@ int decode_common(int cache_dtype, bool interleaved, const void* q, const void* 
   const int64_t cache_q = cache_dtype == yrb::kFP8E4M3 ? 16 : 8;   // elements per 16 bytes
   for (int i = 0; i < 3; ++i)
     if (cache_strides[i] % cache_q != 0) return YRB_EALIGN;
+  // The kernel addresses a (sequence, head)'s cache with 32-bit offsets from
+  // one base: an entry index and the entry stride in bytes below 2^24 (one
+  // 24-bit product), the farthest byte below 2^32.
+  const int64_t esz = cache_dtype == yrb::kFP8E4M3 ? 1 : 2;
+  const int64_t kLim24 = int64_t(1) << 24;
+  if (n_sink + window > kLim24 || cache_strides[2] * esz >= kLim24 ||
+      (n_sink + window - 1) * cache_strides[2] * esz + D * esz > int64_t(0xFFFFFFFF))
+    return YRB_EINVAL;
   if (!strides_aligned(q_strides, 2, dtype) || !strides_aligned(o_strides, 2, dtype)) return YRB_EALIGN;
   if (!aligned16(q) || !aligned16(o) || !aligned16(k_cache) || !aligned16(v_cache) ||
       !aligned16(cos_sin))

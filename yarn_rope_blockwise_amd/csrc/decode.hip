@@ -33,6 +33,13 @@
 //    instead, q'.k' = (R(32 b)^T R(1024 a)^T q') . (R(j) k); with more, it
 //    forms R(e) per key, once for all the key's heads.  Reading a table row
 //    per key and head would move as many bytes as K and V together.
+//  * An fp8 (E4M3) cache row is d bytes: each lane reads a 16-byte chunk
+//    of it, so one load instruction covers whole rows (HBM serves
+//    half-lines markedly slower), and for the half-split layout the lanes
+//    of a key trade halves of their chunks so that each holds 8 complete
+//    pairs.
+//  * A lane addresses its head's cache with a 32-bit offset (one 24-bit
+//    multiply) from a wave-uniform base; the host bounds the span.
 //  * Online softmax in the exp2 domain, the logit scale folded into the
 //    query.  The running max is kept per key group (the lanes that share a
 //    key agree on it), and a group moves its reference only when a key
@@ -86,9 +93,13 @@ struct DecCfg {
   static constexpr int ROUNDS = kKPS / KPW;          // rounds per step of 32 positions
   static constexpr int RPG = 16 / TPK;               // key rows per 16 lanes of an LDS read
   static constexpr int LOG_RPG = RPG == 2 ? 1 : 2;
-  static constexpr int TROWB = 4 * D;                // bytes of a table row (d/2 pairs of (cos, sin))
-  static constexpr int TABB = 2 * kKPS * TROWB;      // LDS bytes of R(j) and R(32 j), j < 32
+  static constexpr int TROWB = 4 * D;                // bytes of an fp32 table row (d/2 pairs of (cos, sin))
+  // LDS table: rows R(j) and R(32 j) (j < 32), then one row per wave for its
+  // R(1024 a).
   static constexpr bool ANCHOR_Q = G <= 2;           // re-anchor the query, else compose R(e) per key
+  static constexpr int ROW_32 = kKPS;                // row of R(32 j): ROW_32 + j
+  static constexpr int ROW_W = ROW_32 + kKPS;        // row of wave w's R(1024 a): ROW_W + w
+  static constexpr int TAB_BYTES = (ROW_W + kWaves) * TROWB;
   // Rounds of K/V loads in flight (register sets of the ring): a step's
   // worth, half of one when the per-head query and output registers leave
   // less room.
@@ -163,19 +174,49 @@ __device__ __forceinline__ int tab_phys(int j, int k) {
   return k ^ ((j & (C::RPG - 1)) | (((k >> 4) & 1) << C::LOG_RPG));
 }
 
-// Chunk index (within a table row) of a lane's pair couple w < 4 (its pairs
-// 2w, 2w+1): half-split, pairs 8cc .. 8cc+7; interleaved (IL), pairs
-// 4cc .. 4cc+3 then d/4 + 4cc .. +3.
-template <int D, bool IL>
-__device__ __forceinline__ int tab_chunk(int cc, int w) {
-  if constexpr (!IL) return 4 * cc + w;
-  return w < 2 ? 2 * cc + w : D / 8 + 2 * cc + (w - 2);
-}
+// Which 8 pairs lane cc (of the D/16 lanes that share a key) holds, and
+// where its query and output chunks (8 elements each) sit.
+//  * bf16 cache: the lane reads two 16-byte chunks per key, at elements 8cc
+//    and d/2 + 8cc: half-split, pairs 8cc .. 8cc+7; interleaved, pairs
+//    4cc .. 4cc+3 and d/4 + 4cc .. +3.  Each load instruction covers whole
+//    128-byte halves of the key rows.
+//  * fp8 cache: a row of codes is d bytes, so chunks at 8cc and d/2 + 8cc
+//    would be 8 bytes each and a load instruction would cover half-lines,
+//    which HBM serves markedly slower (a streaming probe of this cache
+//    shape: 5.75-5.97 TB/s for half-lines against 6.75-6.94 for whole
+//    rows).  So the lane reads the 16-byte chunk cc of the row: interleaved,
+//    pairs 8cc .. 8cc+7 complete; half-split, the first TPK/2 lanes hold
+//    first elements and the others their partners, in mirror order (lane
+//    TPK-1-c holds the partners of lane c's), and the two trade halves so
+//    that lane c takes pairs 16c .. 16c+7 and lane TPK-1-c pairs
+//    16c+8 .. 16c+15.  Outputs: elements 16cc .. 16cc+15.
+template <int D, bool FP8, bool IL>
+struct LaneMap {
+  static constexpr int TPK = D / 16;
+  // pair index of the lane's u-th pair (u < 8)
+  __device__ static int pair(int cc, int u) {
+    if constexpr (!FP8) {
+      if constexpr (!IL) return 8 * cc + u;
+      return u < 4 ? 4 * cc + u : D / 4 + 4 * cc + (u - 4);
+    } else {
+      if constexpr (IL) return 8 * cc + u;
+      return cc < TPK / 2 ? 16 * cc + u : 16 * (TPK - 1 - cc) + 8 + u;
+    }
+  }
+  // 16-byte table chunk (2 pairs) of the lane's pairs 2w, 2w+1
+  __device__ static int tchunk(int cc, int w) { return pair(cc, 2 * w) / 2; }
+  // the lane's two query chunks (elements), read as pairs_of<IL> takes them
+  __device__ static int q_a(int cc) { return FP8 ? (IL ? 16 * cc : pair(cc, 0)) : 8 * cc; }
+  __device__ static int q_b(int cc) { return FP8 ? (IL ? 16 * cc + 8 : D / 2 + pair(cc, 0)) : D / 2 + 8 * cc; }
+  // the elements of o_lo and o_hi (8 each)
+  __device__ static int o_a(int cc) { return FP8 ? 16 * cc : 8 * cc; }
+  __device__ static int o_b(int cc) { return FP8 ? 16 * cc + 8 : D / 2 + 8 * cc; }
+};
 
-// The 8 pairs of one lane from its two chunks a, b (8 values each, at
-// elements 8cc and d/2 + 8cc in either layout): half-split, a the first
-// elements and b their partners; interleaved, a holds pairs 4cc .. 4cc+3
-// and b pairs d/4 + 4cc .. +3, each pair two adjacent values.
+// The 8 pairs of one lane from its two query chunks a, b (8 values each):
+// half-split, a the first elements and b their partners; interleaved, a
+// holds pairs 0..3 of the lane and b pairs 4..7, each pair two adjacent
+// values.
 template <bool IL>
 __device__ __forceinline__ void pairs_of(const float (&a)[8], const float (&b)[8], float (&x)[8],
                                          float (&z)[8]) {
@@ -193,23 +234,23 @@ __device__ __forceinline__ void pairs_of(const float (&a)[8], const float (&b)[8
 
 // (cos, sin) of the lane's 8 pairs: from a table row in global memory, or
 // from LDS row j (swizzled).
-template <int D, bool IL>
+template <class LM>
 __device__ __forceinline__ void row_pairs(const float* row, int cc, float (&c)[8], float (&s)[8]) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const f32x4 t = *reinterpret_cast<const f32x4*>(row + 4 * tab_chunk<D, IL>(cc, w));
+    const f32x4 t = *reinterpret_cast<const f32x4*>(row + 4 * LM::tchunk(cc, w));
     c[2 * w] = t[0];
     s[2 * w] = t[1];
     c[2 * w + 1] = t[2];
     s[2 * w + 1] = t[3];
   }
 }
-template <int D, bool IL>
+template <int D, class LM>
 __device__ __forceinline__ void lds_pairs(const YRB_LDS char* tab, int j, int cc, float (&c)[8], float (&s)[8]) {
   const YRB_LDS char* row = tab + j * DecCfg<D, 1>::TROWB;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const f32x4 t = *reinterpret_cast<const YRB_LDS f32x4*>(row + 16 * tab_phys<D>(j, tab_chunk<D, IL>(cc, w)));
+    const f32x4 t = *reinterpret_cast<const YRB_LDS f32x4*>(row + 16 * tab_phys<D>(j, LM::tchunk(cc, w)));
     c[2 * w] = t[0];
     s[2 * w] = t[1];
     c[2 * w + 1] = t[2];
@@ -235,33 +276,45 @@ __device__ __forceinline__ void add_angle(float& c, float& s, float c2, float s2
   s = s * c2 + c0 * s2;
 }
 
-// K/V chunks of one round for one lane, and whether its key counts.
+// K/V chunks of one round for one lane, and whether its key counts: bf16,
+// the two chunks of K and of V; fp8, one 16-byte chunk of each row.
 template <bool FP8>
 struct KVRound {
-  typename CacheType<FP8>::Chunk klo, khi, vlo, vhi;
+  u32x4 klo, khi, vlo, vhi;
   bool ok;
 };
+template <>
+struct KVRound<true> {
+  u32x4 k, v;
+  bool ok;
+};
+
+// Mirror within the lanes of a key (lane c <-> TPK-1-c): row_half_mirror for
+// 8 lanes, quad_perm [3, 2, 1, 0] for 4.
+template <int TPK>
+__device__ __forceinline__ unsigned key_mirror(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, TPK == 8 ? kDppHalfMirror : 0x1B, 0xF, 0xF, false);
+}
 
 template <int D, int G, bool FP8, bool IL>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(DecCfg<D, G, FP8>::WAVES_PER_EU)))
 void decode_kernel(DecodeArgs a, int parts) {
   using CT = CacheType<FP8>;
-  using Chunk = typename CT::Chunk;
   using Elem = typename CT::Elem;
   using Cfg = DecCfg<D, G, FP8>;
   constexpr int TPK = Cfg::TPK, KPW = Cfg::KPW, ROUNDS = Cfg::ROUNDS, PD = Cfg::PD;
   constexpr int MERGE_F = G * (D + 2);               // floats a wave leaves for the merge
   constexpr int U = Cfg::U;
+  constexpr bool AQ = Cfg::ANCHOR_Q;
   using KV = KVRound<FP8>;
+  using LM = LaneMap<D, FP8, IL>;
 
-  // LDS rows 0..31: R(j); rows 32..63: R(32 j); then one row per wave for
-  // its current R(1024 a).
-  __shared__ __attribute__((aligned(16))) char tab_raw[Cfg::TABB + kWaves * Cfg::TROWB];
+  __shared__ __attribute__((aligned(16))) char tab_raw[Cfg::TAB_BYTES];
   __shared__ __attribute__((aligned(16))) float merge[kWaves][MERGE_F];
-  // ANCHOR_Q: each wave's query rotated to R(1024 a) (a the current 1024-
-  // entry block), per head and lane chunk: the step reads it rather than
-  // hold it in registers.
-  __shared__ __attribute__((aligned(16))) float qrow[kWaves][Cfg::ANCHOR_Q ? G * D : 1];
+  // AQ: each wave's query rotated to R(1024 a) (a the current 1024-entry
+  // block), per head and lane chunk: the step reads it rather than hold it
+  // in registers.
+  __shared__ __attribute__((aligned(16))) float qrow[kWaves][AQ ? G * D : 1];
   YRB_LDS char* const tab = (YRB_LDS char*)tab_raw;
 
   const int lane = threadIdx.x & 63;
@@ -286,11 +339,11 @@ void decode_kernel(DecodeArgs a, int parts) {
 
   // R(j) and R(32 j), j < 32, into LDS (rows past the cache are never used:
   // clamped).
-  for (int idx = threadIdx.x; idx < 2 * kKPS * (D / 4); idx += kWaves * 64) {
-    const int j = idx / (D / 4), k = idx % (D / 4);
-    const int pos = j < kKPS ? j : kKPS * (j - kKPS);
+  for (int idx = threadIdx.x; idx < Cfg::ROW_W * (D / 4); idx += kWaves * 64) {
+    const int row = idx / (D / 4), k = idx % (D / 4);
+    const int pos = row < Cfg::ROW_32 ? row : kKPS * (row - Cfg::ROW_32);
     const f32x4 t = *reinterpret_cast<const f32x4*>(a.cos_sin + (int64_t)min(pos, C - 1) * D + 4 * k);
-    *reinterpret_cast<YRB_LDS f32x4*>(tab + j * Cfg::TROWB + 16 * tab_phys<D>(j, k)) = t;
+    *reinterpret_cast<YRB_LDS f32x4*>(tab + row * Cfg::TROWB + 16 * tab_phys<D>(row, k)) = t;
   }
 
   // This wave's steps: the head's ceil(len / 32) steps split over the parts.
@@ -305,16 +358,21 @@ void decode_kernel(DecodeArgs a, int parts) {
   const float v_deq = (FP8 && a.v_scale) ? a.v_scale[b * a.Hkv + hk] : 1.0f;
   const float scale_log2 = a.softmax_scale * kLog2e * k_deq;
 
+  const __bf16* qhead = reinterpret_cast<const __bf16*>(a.q) + b * a.qs[0] + (int64_t)(hk * G) * a.qs[1];
+  auto load_q = [&](int g, float (&x)[8], float (&z)[8]) {
+    const __bf16* qp = qhead + (int64_t)g * a.qs[1];
+    float qa[8], qb[8];
+    unpack8(*reinterpret_cast<const u32x4*>(qp + LM::q_a(cc)), qa);
+    unpack8(*reinterpret_cast<const u32x4*>(qp + LM::q_b(cc)), qb);
+    pairs_of<IL>(qa, qb, x, z);
+  };
+
   // Query of head g rotated at position `pos` and multiplied by the logit
   // scale (log2 units), as fp32 pairs.
   auto query_at = [&](int g, int pos, float (&x)[8], float (&z)[8]) {
     float c[8], s[8];
-    row_pairs<D, IL>(a.cos_sin + (int64_t)pos * D, cc, c, s);
-    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + b * a.qs[0] + (int64_t)(hk * G + g) * a.qs[1];
-    float qa[8], qb[8];
-    unpack8(*reinterpret_cast<const u32x4*>(qp + 8 * cc), qa);
-    unpack8(*reinterpret_cast<const u32x4*>(qp + D / 2 + 8 * cc), qb);
-    pairs_of<IL>(qa, qb, x, z);
+    row_pairs<LM>(a.cos_sin + (int64_t)pos * D, cc, c, s);
+    load_q(g, x, z);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       rot(x[u], z[u], c[u], s[u]);
@@ -323,8 +381,8 @@ void decode_kernel(DecodeArgs a, int parts) {
     }
   };
   // Compose mode: the query at len - 1, held for the whole launch.
-  float qx[Cfg::ANCHOR_Q ? 1 : G][8], qz[Cfg::ANCHOR_Q ? 1 : G][8];
-  if constexpr (!Cfg::ANCHOR_Q) {
+  float qx[AQ ? 1 : G][8], qz[AQ ? 1 : G][8];
+  if constexpr (!AQ) {
 #pragma unroll
     for (int g = 0; g < G; ++g) query_at(g, len > 0 ? len - 1 : 0, qx[g], qz[g]);
   }
@@ -341,24 +399,41 @@ void decode_kernel(DecodeArgs a, int parts) {
     for (int u = 0; u < 8; ++u) o_lo[g][u] = o_hi[g][u] = 0.f;
   }
 
-  const Elem* kb = reinterpret_cast<const Elem*>(a.k) + b * a.cs[0] + hk * a.cs[1];
-  const Elem* vb = reinterpret_cast<const Elem*>(a.v) + b * a.cs[0] + hk * a.cs[1];
+  // The head's cache in bytes from a wave-uniform base; within it a lane's
+  // chunk sits at a 32-bit offset (the host keeps an entry index and the
+  // entry stride below 2^24 bytes, and their product below 2^32).
+  const int64_t head_off = (b * a.cs[0] + hk * a.cs[1]) * (int64_t)sizeof(Elem);
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + head_off;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + head_off;
+  const unsigned row_bytes = (unsigned)(a.cs[2] * (int64_t)sizeof(Elem));
+  // bf16: chunks at elements 8cc and d/2 + 8cc (16 bytes each); fp8: K's
+  // chunk of the row (mirror order for the partners, half-split), V's chunk cc
+  const unsigned lane_off = 16u * cc;
+  const unsigned k_off = (FP8 && !IL && cc >= TPK / 2) ? D / 2 + 16u * (TPK - 1 - cc) : lane_off;
+  constexpr unsigned HALF_OFF = D / 2 * sizeof(Elem);
+  const int ring_shift = rh - n_sink;
 
   // Round t covers positions t KPW .. t KPW + KPW - 1; this lane's key is
   // entry e = t KPW + kg, in its slot: sinks first, then the ring buffer
-  // (the window offset and the head are both below `window`, so one
-  // conditional subtract takes their sum mod window).
+  // (past the sinks, e - n_sink + ring_head lies in [0, 2 window), and the
+  // unsigned min of it and of it less window is its value mod window).
   auto load_round = [&](int t, KV& kv) {
     const int e = t * KPW + kg;
     kv.ok = e < len;
-    const int d = rh + e - n_sink;
-    const int slot = e >= len ? 0 : e < n_sink ? e : n_sink + (d >= window ? d - window : d);
-    const Elem* kp = kb + (int64_t)slot * a.cs[2];
-    const Elem* vp = vb + (int64_t)slot * a.cs[2];
-    kv.klo = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(kp + 8 * cc));
-    kv.khi = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(kp + D / 2 + 8 * cc));
-    kv.vlo = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(vp + 8 * cc));
-    kv.vhi = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(vp + D / 2 + 8 * cc));
+    const int d = e + ring_shift;
+    const unsigned dw = min((unsigned)d, (unsigned)(d - window));
+    const int slot = !kv.ok ? 0 : e < n_sink ? e : n_sink + (int)dw;
+    const unsigned off = __umul24((unsigned)slot, row_bytes);
+    const unsigned vo = off + lane_off;
+    if constexpr (FP8) {
+      kv.k = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (off + k_off)));
+      kv.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + vo));
+    } else {
+      kv.klo = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + vo));
+      kv.khi = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + vo + HALF_OFF));
+      kv.vlo = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + vo));
+      kv.vhi = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + vo + HALF_OFF));
+    }
   };
 
   __syncthreads();   // the tables are in LDS
@@ -372,8 +447,7 @@ void decode_kernel(DecodeArgs a, int parts) {
 
     // Entry e = 1024 a2 + 32 b1 + j: R(e) = R(1024 a2) R(32 b1) R(j).  The
     // row of R(1024 a2) changes every 32 steps: it comes from global memory
-    // into the wave's LDS row (entry 2 kKPS + wave of the table's rows, the
-    // lanes of key group 0 writing it).
+    // into the wave's LDS row (the lanes of key group 0 writing it).
     int a_cur = -1;
     float rc[8], rs[8];              // compose: R(1024 a2 + 32 b1)
 
@@ -385,11 +459,11 @@ void decode_kernel(DecodeArgs a, int parts) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int A = s * kKPS;
       const int a2 = A >> 10, b1 = (A >> 5) & 31;
-      const int jw = 2 * kKPS + wave;
+      const int jw = Cfg::ROW_W + wave;
       if (a2 != a_cur) {
-        // ANCHOR_Q: R(1024 a2)^T R(len - 1) q = R(len - 1 - 1024 a2) q, into
-        // the wave's query rows; compose: R(1024 a2) into its table row.
-        if constexpr (Cfg::ANCHOR_Q) {
+        // AQ: R(1024 a2)^T R(len - 1) q = R(len - 1 - 1024 a2) q, into the
+        // wave's query rows; compose: R(1024 a2) into its table row.
+        if constexpr (AQ) {
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             float x[8], z[8];
@@ -405,13 +479,13 @@ void decode_kernel(DecodeArgs a, int parts) {
           }
         } else {
           float c2[8], s2[8];
-          row_pairs<D, IL>(a.cos_sin + (int64_t)(a2 << 10) * D, cc, c2, s2);
+          row_pairs<LM>(a.cos_sin + (int64_t)(a2 << 10) * D, cc, c2, s2);
           if (kg == 0) {
             YRB_LDS char* row = tab + jw * Cfg::TROWB;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
               const f32x4 t = {c2[2 * w], s2[2 * w], c2[2 * w + 1], s2[2 * w + 1]};
-              *reinterpret_cast<YRB_LDS f32x4*>(row + 16 * tab_phys<D>(jw, tab_chunk<D, IL>(cc, w))) = t;
+              *reinterpret_cast<YRB_LDS f32x4*>(row + 16 * tab_phys<D>(jw, LM::tchunk(cc, w))) = t;
             }
           }
         }
@@ -422,9 +496,9 @@ void decode_kernel(DecodeArgs a, int parts) {
         __builtin_amdgcn_wave_barrier();
       }
       float c1[8], s1[8];
-      lds_pairs<D, IL>(tab, kKPS + b1, cc, c1, s1);
-      float qx_s[G][8], qz_s[G][8];   // ANCHOR_Q: the query this step's keys meet
-      if constexpr (Cfg::ANCHOR_Q) {
+      lds_pairs<D, LM>(tab, Cfg::ROW_32 + b1, cc, c1, s1);
+      float qx_s[AQ ? G : 1][8], qz_s[AQ ? G : 1][8];   // AQ: the query this step's keys meet
+      if constexpr (AQ) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float* qr = &qrow[wave][(g * TPK + cc) * 16];
@@ -437,7 +511,7 @@ void decode_kernel(DecodeArgs a, int parts) {
         }
       } else {
         float c2[8], s2[8];
-        lds_pairs<D, IL>(tab, jw, cc, c2, s2);
+        lds_pairs<D, LM>(tab, jw, cc, c2, s2);
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
           rc[w] = c2[w];
@@ -450,30 +524,59 @@ void decode_kernel(DecodeArgs a, int parts) {
         KV& kv = ring[(u * ROUNDS + r) % PD];
         const int t = s * ROUNDS + r;
         const int j = r * KPW + kg;
+        // fp8: the lane's 8 pairs of codes.  Interleaved, its chunk as it
+        // came; half-split, the first-element lanes keep their chunk's first
+        // 8 codes and trade the last 8 for their mirror lane's first 8
+        // partners, which keeps its last 8.
+        u32x2 klo8, khi8;
+        if constexpr (FP8) {
+          if constexpr (IL) {
+            klo8 = u32x2{kv.k[0], kv.k[1]};
+            khi8 = u32x2{kv.k[2], kv.k[3]};
+          } else {
+            const bool first = cc < TPK / 2;
+            const unsigned r0 = key_mirror<TPK>(first ? kv.k[2] : kv.k[0]);
+            const unsigned r1 = key_mirror<TPK>(first ? kv.k[3] : kv.k[1]);
+            klo8 = first ? u32x2{kv.k[0], kv.k[1]} : u32x2{r0, r1};
+            khi8 = first ? u32x2{r0, r1} : u32x2{kv.k[2], kv.k[3]};
+          }
+        }
         float c[8], sn[8];
-        lds_pairs<D, IL>(tab, j, cc, c, sn);
-        if constexpr (!Cfg::ANCHOR_Q) {
+        lds_pairs<D, LM>(tab, j, cc, c, sn);
+        if constexpr (!AQ) {
 #pragma unroll
           for (int w = 0; w < 8; ++w) add_angle(c[w], sn[w], rc[w], rs[w]);
         }
+        // Logit of the lane's key with each head (log2 units), partial over
+        // the lane's 8 pairs.
+        float acc[G];
         float ka[8], kb2[8], x[8], z[8];
-        CT::unpack(kv.klo, ka);
-        CT::unpack(kv.khi, kb2);
+        if constexpr (FP8) {
+          CT::unpack(klo8, ka);
+          CT::unpack(khi8, kb2);
+        } else {
+          CT::unpack(kv.klo, ka);
+          CT::unpack(kv.khi, kb2);
+        }
         pairs_of<IL>(ka, kb2, x, z);
 #pragma unroll
         for (int w = 0; w < 8; ++w) rot(x[w], z[w], c[w], sn[w]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const float qxw = AQ ? qx_s[AQ ? g : 0][w] : qx[AQ ? 0 : g][w];
+            const float qzw = AQ ? qz_s[AQ ? g : 0][w] : qz[AQ ? 0 : g][w];
+            sum = __builtin_fmaf(qxw, x[w], __builtin_fmaf(qzw, z[w], sum));
+          }
+          acc[g] = sum;
+        }
         float p[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          float acc = 0.f;
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            const float qxw = Cfg::ANCHOR_Q ? qx_s[g][w] : qx[Cfg::ANCHOR_Q ? 0 : g][w];
-            const float qzw = Cfg::ANCHOR_Q ? qz_s[g][w] : qz[Cfg::ANCHOR_Q ? 0 : g][w];
-            acc = __builtin_fmaf(qxw, x[w], __builtin_fmaf(qzw, z[w], acc));
-          }
-          acc = group_sum<TPK>(acc);
-          const float sc = (!MASK || kv.ok) ? acc : -INFINITY;
+          float sc = group_sum<TPK>(acc[g]);
+          sc = (!MASK || kv.ok) ? sc : -INFINITY;
           // a group's reference moves when its key beats it by more than
           // the threshold: rare once every group has seen a few keys
           const bool grow = sc > m[g] + kDecTau;
@@ -494,8 +597,13 @@ void decode_kernel(DecodeArgs a, int parts) {
         // P V (a slot without an entry adds 0: its raw words are zeroed,
         // whatever the cache holds there, NaN codes included)
         float v1[8], v2[8];
-        CT::unpack((!MASK || kv.ok) ? kv.vlo : Chunk{}, v1);
-        CT::unpack((!MASK || kv.ok) ? kv.vhi : Chunk{}, v2);
+        if constexpr (FP8) {
+          CT::unpack((!MASK || kv.ok) ? u32x2{kv.v[0], kv.v[1]} : u32x2{}, v1);
+          CT::unpack((!MASK || kv.ok) ? u32x2{kv.v[2], kv.v[3]} : u32x2{}, v2);
+        } else {
+          CT::unpack((!MASK || kv.ok) ? kv.vlo : u32x4{}, v1);
+          CT::unpack((!MASK || kv.ok) ? kv.vhi : u32x4{}, v2);
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -556,8 +664,8 @@ void decode_kernel(DecodeArgs a, int parts) {
       oh[w] = bad_seq ? __builtin_nanf("") : hi[w] * inv;
     }
     __bf16* op = reinterpret_cast<__bf16*>(a.o) + b * a.os[0] + (int64_t)(hk * G + g) * a.os[1];
-    *reinterpret_cast<u32x4*>(op + 8 * cc) = pack8(ol);
-    *reinterpret_cast<u32x4*>(op + D / 2 + 8 * cc) = pack8(oh);
+    *reinterpret_cast<u32x4*>(op + LM::o_a(cc)) = pack8(ol);
+    *reinterpret_cast<u32x4*>(op + LM::o_b(cc)) = pack8(oh);
   };
 
   if (parts == 1) {
@@ -569,7 +677,8 @@ void decode_kernel(DecodeArgs a, int parts) {
 
   // Merge the parts of each head: every wave leaves (m, l, o) in LDS, then
   // the wave of part 0 rescales the parts to their common max and adds.
-  // merge[wave]: per head, m and l, then o (8cc + w, d/2 + 8cc + w).
+  // merge[wave]: per head, m and l, then o by element (the lane's o_lo and o_hi
+  // elements as LaneMap places them).
   if (kg == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -580,8 +689,8 @@ void decode_kernel(DecodeArgs a, int parts) {
       }
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        mg[2 + 8 * cc + w] = o_lo[g][w];
-        mg[2 + D / 2 + 8 * cc + w] = o_hi[g][w];
+        mg[2 + LM::o_a(cc) + w] = o_lo[g][w];
+        mg[2 + LM::o_b(cc) + w] = o_hi[g][w];
       }
     }
   }
@@ -600,8 +709,8 @@ void decode_kernel(DecodeArgs a, int parts) {
       lsum += wt * mg[1];
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        lo[w] += wt * mg[2 + 8 * cc + w];
-        hi[w] += wt * mg[2 + D / 2 + 8 * cc + w];
+        lo[w] += wt * mg[2 + LM::o_a(cc) + w];
+        hi[w] += wt * mg[2 + LM::o_b(cc) + w];
       }
     }
     store(g, lsum, lo, hi);

@@ -85,6 +85,20 @@ def e4m3_codes(shape, seed: int) -> np.ndarray:
     return (sign << 7) | (exp << 3) | man
 
 
+def e4m3_codes_banded(shape, seed: int, exp_fields) -> np.ndarray:
+    """Random 8-bit E4M3 codes whose exponent field is fixed per leading
+    index pair: exp_fields[b][h] (0..15) for codes [b, h, ...]; sign and
+    mantissa random, the one NaN mantissa of field 15 excluded.  Only bit
+    patterns are drawn."""
+    rng = np.random.default_rng(seed)
+    e = np.asarray(exp_fields, np.uint8).reshape(shape[:2] + (1,) * (len(shape) - 2))
+    e = np.broadcast_to(e, shape)
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8)
+    man = rng.integers(0, 8, size=shape, dtype=np.uint8)
+    man = np.where(e == 15, man % 7, man).astype(np.uint8)
+    return (sign << 7) | (e << 3) | man
+
+
 def uniform_scales(shape, seed: int, lo: float = 0.05, hi: float = 0.5) -> np.ndarray:
     """fp32 values drawn uniformly from [lo, hi)."""
     return np.random.default_rng(seed).uniform(lo, hi, size=shape).astype(np.float32)
