@@ -157,13 +157,16 @@ __device__ __forceinline__ void offsets_from(const WaveState<D, 2>& st, Offsets&
 // a quarter: the last key index inside the keys; for each query tile, the
 // last key index visible to the lane's query row under the causal mask; the
 // end of the sink keys and the window length (both unused without a
-// window).
+// window).  Wave-uniform, in key indices: the end of the sinks and the last
+// key some row of the wave has outside its window (-1 if none).
 struct MaskInfo {
   int key_last;
   int q_last[2];
   int sink_end;
   int window;
   bool causal;
+  int sink_end_u;
+  int w_lo_u;
 };
 
 // Mask of the quarter whose first key index is kbase, for query tile X:
@@ -171,16 +174,41 @@ struct MaskInfo {
 // 4(lane/32).  A key stays if it is inside the keys, not after the row
 // (causal), and either a sink or inside the row's window; the others get
 // -inf, so P = 0.
+//
+// With a window, whether some row's window starts past the quarter's first
+// key and whether the quarter holds a sink key are wave-uniform, and each
+// case takes its cheapest exact form: with no window start inside, every key
+// is inside every row's window and the causal test alone decides (the
+// diagonal, the ragged end, and sinks alike); a window start inside and no
+// sink, one unsigned range test (e in (lo, hi]); both, the full test.
 template <bool WIN>
 __device__ __forceinline__ void mask_scores(f32x16& s, const MaskInfo& mi, int X, int kbase) {
   const int hi = (mi.causal ? min(mi.key_last, mi.q_last[X]) : mi.key_last) - kbase;
+  const bool edge = WIN && kbase <= mi.w_lo_u;       // some row's window starts inside
+  if (!edge) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int e = 8 * (j >> 2) + (j & 3);
+      s[j] = e <= hi ? s[j] : -INFINITY;
+    }
+    return;
+  }
   const int lo = mi.q_last[X] - mi.window - kbase;   // window: keys after it
   const int se = mi.sink_end - kbase;                 // sinks: keys before it
+  if (kbase >= mi.sink_end_u) {                      // no sink key
+    const int lo1 = lo + 1;
+    const unsigned width = (unsigned)max(hi - lo, 0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int e = 8 * (j >> 2) + (j & 3);
+      s[j] = (unsigned)(e - lo1) < width ? s[j] : -INFINITY;
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int e = 8 * (j >> 2) + (j & 3);
-    bool keep = e <= hi;
-    if constexpr (WIN) keep = keep && (e < se || e > lo);
+    const bool keep = e <= hi && (e < se || e > lo);
     s[j] = keep ? s[j] : -INFINITY;
   }
 }
@@ -801,6 +829,8 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
     mi.sink_end = sink_end - 4 * (lane >> 5);
     mi.window = a.window;
     mi.causal = a.causal != 0;
+    mi.sink_end_u = sink_end;
+    mi.w_lo_u = -1;
     bf16x8 kf[NDS];           // K of the next S chain
     bf16x8 vf[2][NDT];        // V of the next PV products
     bf16x8 p0[2], p1[2];
@@ -844,6 +874,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_bf16_pp_kernel(AttnArgs
     }
     const int n_full_s = __builtin_amdgcn_readfirstlane(n_full_m);
     const int w_lo_s = __builtin_amdgcn_readfirstlane(w_lo_m);
+    mi.w_lo_u = w_lo_s;
     auto masked = [&](int kt) YRB_INLINE {
       return kt >= n_full_s || (kt * BN + BN - 1 >= sink_end && kt * BN <= w_lo_s);
     };
