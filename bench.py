@@ -55,24 +55,26 @@ METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HB
 _PP = ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h")
 _DEC = ("csrc/decode.hip", "csrc/common.h")
 MEASURED_TRAFFIC = {
-    "attn_bf16_pp_kernel": {"files": _PP, "sha256": "168a3f1c150ce3c7df964be10ab06f3e71f38bd2cb3b0560d40e873d550a2266",
-                           "fetch_kib": 1038593, "write_kib": 131091},
-    "attn_bf16_pp_kernel_gqa_prefill_32k_pi8": {"files": _PP, "sha256": "168a3f1c150ce3c7df964be10ab06f3e71f38bd2cb3b0560d40e873d550a2266",
-                                               "fetch_kib": 1438503, "write_kib": 262182},
-    "attn_bf16_pp_kernel_gqa_prefill_32k_ntk8": {"files": _PP, "sha256": "168a3f1c150ce3c7df964be10ab06f3e71f38bd2cb3b0560d40e873d550a2266",
-                                                "fetch_kib": 1465073, "write_kib": 262182},
-    "attn_bf16_pp_kernel_gqa_prefill_32k_yarn8": {"files": _PP, "sha256": "168a3f1c150ce3c7df964be10ab06f3e71f38bd2cb3b0560d40e873d550a2266",
-                                                 "fetch_kib": 1402415, "write_kib": 262182},
-    "attn_bf16_pp_kernel_window": {"files": _PP, "sha256": "168a3f1c150ce3c7df964be10ab06f3e71f38bd2cb3b0560d40e873d550a2266",
-                                  "fetch_kib": 722197, "write_kib": 131091},
-    "decode_kernel": {"files": _DEC, "sha256": "7679fb96bda5ccc7e3d8990695a16273a33145cd91de606d82f822955caae813",
-                     "fetch_kib": 2100193, "write_kib": 512},
-    "decode_kernel_fp8": {"files": _DEC, "sha256": "7679fb96bda5ccc7e3d8990695a16273a33145cd91de606d82f822955caae813",
-                         "fetch_kib": 1053152, "write_kib": 512},
-    "decode_kernel_gqa": {"files": _DEC, "sha256": "7679fb96bda5ccc7e3d8990695a16273a33145cd91de606d82f822955caae813",
-                         "fetch_kib": 526616, "write_kib": 3072},
-    "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": "7679fb96bda5ccc7e3d8990695a16273a33145cd91de606d82f822955caae813",
-                             "fetch_kib": 263112, "write_kib": 512},
+    "attn_bf16_pp_kernel": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
+        "fetch_kib": 1029686, "write_kib": 131091},
+    "attn_bf16_pp_kernel_gqa_prefill_32k_pi8": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
+        "fetch_kib": 1446684, "write_kib": 262182},
+    "attn_bf16_pp_kernel_gqa_prefill_32k_ntk8": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
+        "fetch_kib": 1457459, "write_kib": 262182},
+    "attn_bf16_pp_kernel_gqa_prefill_32k_yarn8": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
+        "fetch_kib": 1366886, "write_kib": 262182},
+    "attn_bf16_pp_kernel_window": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
+        "fetch_kib": 727503, "write_kib": 131091},
+    "decode_kernel": {"files": _DEC, "sha256": "7e851774507132926fb20f4a3d966015634fe1efbb215ecf084dcbf26bddca71",
+        "fetch_kib": 2100151, "write_kib": 512},
+    "decode_kernel_fp8": {"files": _DEC, "sha256": "7e851774507132926fb20f4a3d966015634fe1efbb215ecf084dcbf26bddca71",
+        "fetch_kib": 1050503, "write_kib": 512},
+    "decode_kernel_gqa": {"files": _DEC, "sha256": "7e851774507132926fb20f4a3d966015634fe1efbb215ecf084dcbf26bddca71",
+        "fetch_kib": 526096, "write_kib": 1536},
+    "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": "7e851774507132926fb20f4a3d966015634fe1efbb215ecf084dcbf26bddca71",
+        "fetch_kib": 264133, "write_kib": 2560},
+    "attn_bf16_pp_kernel_ring": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",  # per step of 8 launches
+        "fetch_kib": 9440806, "write_kib": 1130654},
 }
 FETCH_FACTOR, WRITE_FACTOR = 1.99996, 1.0
 
@@ -625,10 +627,16 @@ def main():
         log("ring share: uploading blocks and timing")
         ring = run_ring(max(2, args.steps // 5), 2)
         log(f"ring share done: {ring['ms']:.3f} ms")
+        ring_kernel_ms = float(sum(ring["per_call_ms"]))
+        ring_tf = ring["flops"] / (ring_kernel_ms * 1e-3) / 1e12
         line["ring_share"] = {"workload": "ring_share_h8_8x32768_yarn8_qblock7",
                               "ms": round(ring["ms"], 3),
                               "TFLOP/s": round(ring["flops"] / (ring["ms"] * 1e-3) / 1e12, 2),
-                              "per_call_ms": ring["per_call_ms"]}
+                              "per_call_ms": ring["per_call_ms"],
+                              # the 8 accumulate launches of a step (the step also rotates the own block)
+                              "roofline": roofline("mfma", ring_tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                                   "attn_bf16_pp_kernel<exact> x 8", "attn_bf16_pp_kernel_ring",
+                                                   flops_per_step=ring["flops"], traffic_per="step of 8 launches")}
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on a bounded sample, one process per core")
         line["cpu_baseline"] = cpu_baseline()
