@@ -306,6 +306,54 @@ def test_decode_fp8_every_code(G, D, IL):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
+def test_decode_offsets_at_the_top_of_32_bits(fp8):
+    # One (sequence, head)'s cache spread out with an entry stride that puts
+    # its last entry's bytes just under 2^32: the kernel's lane offsets (a
+    # 24-bit product of entry and stride, plus the chunk) reach the top of
+    # their 32-bit range, as far as the host's checks allow.
+    require_gpu()
+    import torch
+    from oracle import fp8 as F
+    n_sink, window, D = 4, 2044, 128
+    C = n_sink + window
+    esz, align = (1, 16) if fp8 else (2, 8)
+    stride = ((2 ** 32 - 1 - D * esz) // ((C - 1) * esz)) // align * align
+    span = (C - 1) * stride + D
+    assert stride * esz < 2 ** 24 and span * esz <= 2 ** 32 - 1 and span * esz > 2 ** 32 - 4096
+    rope = W.Rope(W.PLAIN, D, 1e4, 1.0, 4096)
+    tab, th, _ = api.rope_tables_build(api.RopeConfig.of(rope), C)
+    qv, q = draw((1, 1, D), 120, "bf16")
+    rh = np.array([777], np.int32)
+    if fp8:
+        kc = synth.e4m3_codes((1, 1, C, D), 121)
+        vc = synth.e4m3_codes((1, 1, C, D), 122)
+        kv, vv = F.e4m3_decode(kc), F.e4m3_decode(vc)
+        small_k, small_v = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
+        dt = torch.uint8
+    else:
+        kv, small_k = draw((1, 1, C, D), 121, "bf16")
+        vv, small_v = draw((1, 1, C, D), 122, "bf16")
+        dt = torch.bfloat16
+    say(f"attn_decode_sink_window_ex, entry stride {stride} elements, span {span * esz} bytes, fp8={fp8}")
+    big_k = torch.empty(span, dtype=dt, device="cuda")
+    big_v = torch.empty(span, dtype=dt, device="cuda")
+    k = big_k.as_strided((1, 1, C, D), (0, 0, stride, 1))
+    v = big_v.as_strided((1, 1, C, D), (0, 0, stride, 1))
+    k.copy_(small_k)
+    v.copy_(small_v)
+    scale = R.softmax_scale(rope.kind, rope.scale, D)
+    o = api.attn_decode_sink_window_ex(q, k, v, torch.tensor([C], dtype=torch.int32, device="cuda"),
+                                       n_sink, window, tab, scale,
+                                       ring_head=torch.from_numpy(rh).cuda())
+    torch.cuda.synchronize()
+    got = host(o)
+    del k, v, big_k, big_v
+    torch.cuda.empty_cache()
+    ref = A.decode_sink_window(qv, kv, vv, th, scale, n_sink, window, [C], rh)
+    assert max_abs(got, ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("G,D", [(1, 128), (2, 64), (4, 64), (8, 128)])
 def test_decode_interleaved_layout(fp8, G, D):
     # Keys and the query rotated in the interleaved pair layout, bf16 or E4M3

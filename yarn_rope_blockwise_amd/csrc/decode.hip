@@ -18,9 +18,10 @@
 //    head's entries may be split over `parts` waves of one workgroup (the
 //    host picks parts so that caches with few key/value heads still fill
 //    the chip); the parts' (max, sum, output) merge through LDS at the end.
-//  * D/16 lanes share one key: each lane reads the two chunks holding
-//    pairs (i, i + d/2) for its 8 pairs (or, interleaved, adjacent pairs
-//    from the same two chunks), so the rotation is lane-local.  Loads are
+//  * D/16 lanes share one key and each holds 8 complete pairs, so the
+//    rotation is lane-local: with a bf16 cache a lane reads the two chunks
+//    holding pairs (i, i + d/2) (or, interleaved, adjacent pairs from the
+//    same two chunks); an fp8 cache is read as below.  Loads are
 //    non-temporal (the cache is far larger than L2 and MALL) and pipelined
 //    by round: a ring of register sets keeps a step's worth of rounds in
 //    flight, each set reloaded as soon as its round is folded.
@@ -58,9 +59,8 @@ constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kKPS = 32;         // cache positions per step
 constexpr float kDecTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
-// Cache element: bf16 (a 16-byte chunk holds 8 values) or fp8 E4M3 (OCP; an
-// 8-byte chunk holds 8 codes).  A lane reads two chunks per key for K and
-// two for V.
+// Cache element: bf16 (a 16-byte chunk holds 8 values) or fp8 E4M3 (OCP; 8
+// codes decode from one 8-byte half of a lane's 16-byte chunk).
 template <bool FP8>
 struct CacheType {
   using Chunk = u32x4;
