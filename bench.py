@@ -65,13 +65,13 @@ MEASURED_TRAFFIC = {
         "fetch_kib": 1366886, "write_kib": 262182},
     "attn_bf16_pp_kernel_window": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
         "fetch_kib": 727503, "write_kib": 131091},
-    "decode_kernel": {"files": _DEC, "sha256": "7e851774507132926fb20f4a3d966015634fe1efbb215ecf084dcbf26bddca71",
+    "decode_kernel": {"files": _DEC, "sha256": "3e22023e53b31807fe0a5622ffbf530b7ad649960aeec801860451dd1a2934c7",
         "fetch_kib": 2100151, "write_kib": 512},
-    "decode_kernel_fp8": {"files": _DEC, "sha256": "7e851774507132926fb20f4a3d966015634fe1efbb215ecf084dcbf26bddca71",
+    "decode_kernel_fp8": {"files": _DEC, "sha256": "3e22023e53b31807fe0a5622ffbf530b7ad649960aeec801860451dd1a2934c7",
         "fetch_kib": 1050503, "write_kib": 512},
-    "decode_kernel_gqa": {"files": _DEC, "sha256": "7e851774507132926fb20f4a3d966015634fe1efbb215ecf084dcbf26bddca71",
+    "decode_kernel_gqa": {"files": _DEC, "sha256": "3e22023e53b31807fe0a5622ffbf530b7ad649960aeec801860451dd1a2934c7",
         "fetch_kib": 526096, "write_kib": 1536},
-    "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": "7e851774507132926fb20f4a3d966015634fe1efbb215ecf084dcbf26bddca71",
+    "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": "3e22023e53b31807fe0a5622ffbf530b7ad649960aeec801860451dd1a2934c7",
         "fetch_kib": 264133, "write_kib": 2560},
     "attn_bf16_pp_kernel_ring": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",  # per step of 8 launches
         "fetch_kib": 9440806, "write_kib": 1130654},
