@@ -356,6 +356,88 @@ def test_accumulate_bf16_ring_small(qi):
     assert max_abs(host(o2), o_ref) <= BF16_TOL
 
 
+def test_prefill_fp32_d128():
+    # The fp32 storage path at d = 128 (the tiny configuration is d = 64):
+    # GQA 2:1, causal, ragged tail.
+    require_gpu()
+    import torch
+    rope = W.Rope(W.YARN, 128, 1e4, 4.0, 128)
+    tab, th, scale, (qv, kv, vv), (q, k, v) = _setup(1, 300, 2, 1, 128, "f32", rope, seed_base=130)
+    say("attn_prefill_blockwise fp32 S=300 Hq=2 Hkv=1 d=128")
+    kr = api.rope_apply(k, tab)
+    o = api.attn_prefill_blockwise(q, kr, v, scale, cos_sin=tab)
+    torch.cuda.synchronize()
+    ref = A.prefill(qv, kv, vv, th, scale)
+    assert max_abs(host(o), ref) <= F32_TOL
+
+
+def _ring_b(B, nb, blk, Hq, Hkv, D, rope, seed_base):
+    S = nb * blk
+    tab, th, _ = api.rope_tables_build(api.RopeConfig.of(rope), S)
+    qv, q = draw((B, blk, Hq, D), seed_base + 0, "bf16")
+    kv, k = draw((B, S, Hkv, D), seed_base + 1, "bf16")
+    vv, v = draw((B, S, Hkv, D), seed_base + 2, "bf16")
+    k = api.rope_apply(k, tab)
+    kb = [k[:, j * blk:(j + 1) * blk] for j in range(nb)]
+    vb = [v[:, j * blk:(j + 1) * blk] for j in range(nb)]
+    kbv = [kv[:, j * blk:(j + 1) * blk] for j in range(nb)]
+    vbv = [vv[:, j * blk:(j + 1) * blk] for j in range(nb)]
+    return tab, th, q, qv, kb, vb, kbv, vbv
+
+
+@pytest.mark.parametrize("causal,D", [(False, 64), (True, 128)])
+def test_accumulate_bf16_ring_batched(causal, D):
+    # Two sequences in the batch, three key blocks; non-causal (every block
+    # visible, none skipped) at d = 64, causal at d = 128, fed out of order.
+    require_gpu()
+    import torch
+    B, nb, blk, Hq, Hkv, qi = 2, 3, 200, 4, 2, 1
+    rope = W.Rope(W.YARN, D, 1e4, 4.0, 150)
+    tab, th, q, qv, kb, vb, kbv, vbv = _ring_b(B, nb, blk, Hq, Hkv, D, rope, 140 + D)
+    scale = R.softmax_scale(rope.kind, rope.scale, D)
+    order = [2, 0, 1]
+    st = api.AccState.empty(B, blk, Hq, D)
+    say(f"attn_block_accumulate bf16 B=2 3x200 causal={causal} d={D}")
+    o = None
+    for t, j in enumerate(order):
+        o = api.attn_block_accumulate(q, kb[j], vb[j], st, qi * blk, j * blk, scale, cos_sin=tab,
+                                      causal=causal, first=(t == 0), finalize=(t == nb - 1))
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref, _ = A.ring_share(qv, kbv, vbv, th, scale, qi * blk,
+                                          [j * blk for j in range(nb)], order=order, causal=causal)
+    assert max_abs(host(o), o_ref) <= BF16_TOL
+    np.testing.assert_allclose(host(st.m), m_ref, atol=2e-2)
+    np.testing.assert_allclose(host(st.l), l_ref, rtol=2e-2)
+
+
+def test_prefill_token_stride_past_the_fast_dma():
+    # K and V with a token stride of 2^24 elements: 64 rows of it pass 2^31
+    # bytes, so the per-tile DMA cannot use 32-bit lane offsets and every
+    # tile takes the clamped per-lane-address load (about 5.3 GB per view).
+    require_gpu()
+    import torch
+    S, Hq, Hkv, D = 160, 2, 1, 128
+    stride = 1 << 24
+    rope = W.Rope(W.YARN, D, 1e4, 4.0, 128)
+    tab, th, scale, (qv, kv, vv), (q, k, v) = _setup(1, S, Hq, Hkv, D, "bf16", rope, seed_base=150)
+    kr = api.rope_apply(k, tab)
+    span = (S - 1) * stride + Hkv * D
+    say(f"attn_prefill_blockwise K/V token stride {stride} elements, {2 * span} bytes per view")
+    big_k = torch.empty(span, dtype=torch.bfloat16, device="cuda")
+    big_v = torch.empty(span, dtype=torch.bfloat16, device="cuda")
+    ks = big_k.as_strided((1, S, Hkv, D), (0, stride, D, 1))
+    vs = big_v.as_strided((1, S, Hkv, D), (0, stride, D, 1))
+    ks.copy_(kr)
+    vs.copy_(v)
+    o = api.attn_prefill_blockwise(q, ks, vs, scale, cos_sin=tab)
+    torch.cuda.synchronize()
+    got = host(o)
+    del ks, vs, big_k, big_v
+    torch.cuda.empty_cache()
+    ref = A.prefill(qv, kv, vv, th, scale)
+    assert max_abs(got, ref) <= BF16_TOL
+
+
 def test_accumulate_rows_that_start_empty():
     # Query rows at positions 0..255 against a key block at positions
     # 100..399 (causal): rows below 100 see none of its keys while later rows
