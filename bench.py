@@ -302,7 +302,8 @@ def run_decode(steps: int, warmup: int, n_q_heads=None, n_kv_heads=None, fp8: bo
 
 def run_interleaved(steps: int, warmup: int):
     """The interleaved pair layout: rope_apply_ex on the 16k K (268 MB moved) and the
-    bf16 decode through attn_decode_sink_window_ex, each timed back to back."""
+    bf16 decode through attn_decode_sink_window_ex, each timed back to back; the
+    half-split rope_apply on the same K, timed the same way."""
     import torch
     from yarn_rope_blockwise_amd import api, synth
     from yarn_rope_blockwise_amd import workloads as W
@@ -310,14 +311,21 @@ def run_interleaved(steps: int, warmup: int):
     k = _upload((w.batch, w.seq, w.n_kv_heads, w.head_dim), 1)
     tab, _, _ = api.rope_tables_build(api.RopeConfig.of(w.rope), w.seq)
     kr = torch.empty_like(k)
-    warm(lambda: api.rope_apply_ex(k, tab, layout=api.LAYOUT_INTERLEAVED, out=kr), warmup)
-    ev = _events(2)
-    ev[0].record()
-    for _ in range(steps):
-        api.rope_apply_ex(k, tab, layout=api.LAYOUT_INTERLEAVED, out=kr)
-    ev[1].record()
-    torch.cuda.synchronize()
-    rope_ms = ev[0].elapsed_time(ev[1]) / steps
+
+    def back_to_back(fn):
+        warm(fn, warmup)
+        ev = _events(2)
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps
+
+    rope_ms = back_to_back(lambda: api.rope_apply_ex(k, tab, layout=api.LAYOUT_INTERLEAVED, out=kr))
+    # the half-split pass timed the same way (in the prefill step it is one
+    # launch between two others)
+    rope_half_ms = back_to_back(lambda: api.rope_apply(k, tab, out=kr))
     rope_bytes = 2 * k.numel() * 2 + w.seq * w.head_dim * 4
     del k, kr
     d = W.SINK_DECODE
@@ -343,7 +351,8 @@ def run_interleaved(steps: int, warmup: int):
     torch.cuda.synchronize()
     dec_ms = ev[0].elapsed_time(ev[1]) / steps
     dec_bytes = 2 * kc.numel() * 2 + q.numel() * 2 * 2 + lens.numel() * 4 * 2
-    return dict(rope_ms=rope_ms, rope_bytes=rope_bytes, dec_ms=dec_ms, dec_bytes=dec_bytes)
+    return dict(rope_ms=rope_ms, rope_half_ms=rope_half_ms, rope_bytes=rope_bytes, dec_ms=dec_ms,
+                dec_bytes=dec_bytes)
 
 
 def run_ring(steps: int, warmup: int):
@@ -610,6 +619,8 @@ def main():
         line["interleaved_layout"] = {
             "rope_apply_ex_k16k": {"ms": round(il["rope_ms"], 4),
                                    "GB/s": round(il["rope_bytes"] / (il["rope_ms"] * 1e-3) / 1e9, 1)},
+            "rope_apply_k16k_half_split": {"ms": round(il["rope_half_ms"], 4),
+                                           "GB/s": round(il["rope_bytes"] / (il["rope_half_ms"] * 1e-3) / 1e9, 1)},
             "decode_ex_bf16": {"ms": round(il["dec_ms"], 4),
                                "GB/s": round(il["dec_bytes"] / (il["dec_ms"] * 1e-3) / 1e9, 1)}}
         ft = run_factor_tables(steps_d, 10)

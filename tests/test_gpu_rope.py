@@ -76,6 +76,21 @@ def test_tables_offset_rows():
     assert max(max_abs(got[..., 0], c), max_abs(got[..., 1], s)) <= TABLE_TOL
 
 
+@pytest.mark.parametrize("d,n,pos0", [(128, 1, 0), (64, 15, 7), (128, 17, 1000003), (64, 33, 262127),
+                                      (128, 4111, 16)])
+def test_tables_ragged_row_groups(d, n, pos0):
+    # Rows are written 16 to a thread (the first from its reduced angle, the
+    # rest by angle addition): counts and offsets that cut those groups
+    # short, and positions far past the tables above, against the oracle.
+    require_gpu()
+    say(f"rope_tables_build_factors d={d} n_pos={n} pos0={pos0}")
+    lam = np.linspace(1.0, 8.0, d // 2)
+    tab, th = api.rope_tables_build_factors(d, 1e4, lam, n, pos0=pos0)
+    got = host(tab)
+    c, s = R.tables(th, pos0 + np.arange(n))
+    assert max(max_abs(got[..., 0], c), max_abs(got[..., 1], s)) <= TABLE_TOL
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_rope_apply(dtype, D):

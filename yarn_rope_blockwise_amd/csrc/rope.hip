@@ -2,14 +2,16 @@
 //
 // Tables: row r holds (cos, sin) of (pos0 + r) * theta'_i for each pair i
 // ("Context Window Scaling ..." (tecvarsity), Section 2: the 2x2 rotation by
-// m * theta_i).  The angle is formed and reduced in fp64 so that rows at
-// positions ~2^18 keep fp32 accuracy; only the final value is rounded.
+// m * theta_i).  Every 16th row's angle is formed and reduced in fp64 so
+// that rows at positions ~2^18 keep fp32 accuracy; the rows between follow
+// by angle addition in fp64; only the final values are rounded.
 //
 // Rotation: (x_i, x_{i+d/2}) -> (x_i c - x_{i+d/2} s, x_i s + x_{i+d/2} c),
 // fp32 arithmetic, bf16 results rounded to nearest even.  HBM-bound: each
 // thread moves two 16-byte halves of one row and reads its table slice
 // (shared by all heads of a token, so it stays in L2).
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 
 #include "common.h"
@@ -18,17 +20,24 @@
 namespace yrb {
 
 struct ThetaPack {
-  double t[64];
+  double t[64];   // theta'_i
+  double c[64];   // cos(theta'_i)
+  double s[64];   // sin(theta'_i)
 };
 
-// half = d/2 is 32 or 64: row and pair index by shift and mask.
+// Rows a thread writes for its pair: the first from its own reduced angle,
+// each further one by turning the row before by theta'_i.
+constexpr int kTabRows = 16;
+
+// half = d/2 is 32 or 64: pair index by mask, row group by shift.  Lanes
+// take consecutive pairs, so each store of a wave writes whole rows.
 __global__ __launch_bounds__(256) void rope_tables_kernel(ThetaPack th, int log2_half, int64_t pos0,
-                                                          int64_t total, float2* out) {
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  int64_t r = idx >> log2_half;
-  int i = (int)(idx & ((1 << log2_half) - 1));
-  const double a = (double)(pos0 + r) * th.t[i];
+                                                          int64_t n_pos, float2* out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = (int)(idx & ((1 << log2_half) - 1));
+  const int64_t r0 = (idx >> log2_half) * kTabRows;
+  if (r0 >= n_pos) return;
+  const double a = (double)(pos0 + r0) * th.t[i];
   // Reduce a modulo 2 pi in fp64 (Cody and Waite's two-constant
   // subtraction: 2 pi = P1 + P2, P1 with 33 significant bits so that k * P1
   // is exact for |k| < 2^20), then take sin/cos of the reduced angle in fp32.
@@ -50,19 +59,38 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(ThetaPack th, int log2
     s = (float)sd;
     c = (float)cd;
   }
-  out[idx] = make_float2(c, s);
+  float2* o = out + (r0 << log2_half) + i;
+  o[0] = make_float2(c, s);
+  // The next rows by angle addition, (c, s) <- (c C - s S, s C + c S) with
+  // C, S the cosine and sine of theta'_i, in fp64: a rotation keeps the
+  // first row's error (one fp32 rounding) and adds ~2^-53 a step, so every
+  // row stays within about 2^-23 of the exact value before its own
+  // rounding.
+  const int rows = (int)(n_pos - r0 < kTabRows ? n_pos - r0 : kTabRows);
+  const double C = th.c[i], S = th.s[i];
+  double cd = c, sd = s;
+  for (int j = 1; j < rows; ++j) {
+    const double cn = __builtin_fma(cd, C, -(sd * S));
+    sd = __builtin_fma(sd, C, cd * S);
+    cd = cn;
+    o[(int64_t)j << log2_half] = make_float2((float)cd, (float)sd);
+  }
 }
 
 hipError_t launch_rope_tables(const double* theta, int half, int64_t pos0, int64_t n_pos,
                               float* cos_sin, hipStream_t stream) {
   if (half != 32 && half != 64) return hipErrorInvalidValue;
-  ThetaPack th;
-  for (int i = 0; i < 64; ++i) th.t[i] = i < half ? theta[i] : 0.0;
-  int64_t total = n_pos * half;
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
+  if (n_pos == 0) return hipSuccess;
+  ThetaPack th = {};
+  for (int i = 0; i < half; ++i) {
+    th.t[i] = theta[i];
+    th.c[i] = std::cos(theta[i]);
+    th.s[i] = std::sin(theta[i]);
+  }
+  const int64_t threads = (n_pos + kTabRows - 1) / kTabRows * half;
+  const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL(rope_tables_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, th, half == 64 ? 6 : 5,
-                     pos0, total, reinterpret_cast<float2*>(cos_sin));
+                     pos0, n_pos, reinterpret_cast<float2*>(cos_sin));
   return hipGetLastError();
 }
 
