@@ -56,25 +56,25 @@ _PP = ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h")
 _DEC = ("csrc/decode.hip", "csrc/common.h")
 MEASURED_TRAFFIC = {
     "attn_bf16_pp_kernel": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
-        "fetch_kib": 1029686, "write_kib": 131091},
+        "fetch_kib": 1045318, "write_kib": 131091},
     "attn_bf16_pp_kernel_gqa_prefill_32k_pi8": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
-        "fetch_kib": 1446684, "write_kib": 262182},
+        "fetch_kib": 1428135, "write_kib": 262182},
     "attn_bf16_pp_kernel_gqa_prefill_32k_ntk8": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
-        "fetch_kib": 1457459, "write_kib": 262182},
+        "fetch_kib": 1438930, "write_kib": 262182},
     "attn_bf16_pp_kernel_gqa_prefill_32k_yarn8": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
-        "fetch_kib": 1366886, "write_kib": 262182},
+        "fetch_kib": 1390411, "write_kib": 262182},
     "attn_bf16_pp_kernel_window": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
-        "fetch_kib": 727503, "write_kib": 131091},
+        "fetch_kib": 731775, "write_kib": 131091},
     "decode_kernel": {"files": _DEC, "sha256": "3e22023e53b31807fe0a5622ffbf530b7ad649960aeec801860451dd1a2934c7",
-        "fetch_kib": 2100151, "write_kib": 512},
+        "fetch_kib": 2100150, "write_kib": 512},
     "decode_kernel_fp8": {"files": _DEC, "sha256": "3e22023e53b31807fe0a5622ffbf530b7ad649960aeec801860451dd1a2934c7",
-        "fetch_kib": 1050503, "write_kib": 512},
+        "fetch_kib": 1050492, "write_kib": 512},
     "decode_kernel_gqa": {"files": _DEC, "sha256": "3e22023e53b31807fe0a5622ffbf530b7ad649960aeec801860451dd1a2934c7",
-        "fetch_kib": 526096, "write_kib": 1536},
+        "fetch_kib": 526100, "write_kib": 1536},
     "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": "3e22023e53b31807fe0a5622ffbf530b7ad649960aeec801860451dd1a2934c7",
-        "fetch_kib": 264133, "write_kib": 2560},
+        "fetch_kib": 264135, "write_kib": 2560},
     "attn_bf16_pp_kernel_ring": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",  # per step of 8 launches
-        "fetch_kib": 9440806, "write_kib": 1130654},
+        "fetch_kib": 9303140, "write_kib": 1130655},
 }
 FETCH_FACTOR, WRITE_FACTOR = 1.99996, 1.0
 
