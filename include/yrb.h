@@ -279,6 +279,40 @@ YRB_API int attn_prefill_sink_window(const void* q, const void* k, const void* v
                              float* lse, void* workspace, void* stream);
 
 /*
+ * attn_prefill_sink_window_chunk -- attn_prefill_sink_window for one chunk
+ * of a longer sequence: the chunk's Sq queries against the sequence's first
+ * Sk keys, under the same mask and with the same tile skipping, so a long
+ * input can be prefilled chunk by chunk ([C] "Sliding Window + Attention
+ * Sinks"; [J] "Attention sinks").  Positions are the sequence's own: query
+ * s of the chunk sits at q_offset + s, key t at t; key t is visible to it
+ * iff t <= q_offset + s and (t < n_sink or t > q_offset + s - window).
+ * (A cache that evicts tokens and re-indexes positions is the decode's.)
+ *
+ *   q, o           device [B][Sq][Hq][D]   strides[0], strides[3]
+ *   k, v           device [B][Sk][Hkv][D]  strides[1], strides[2]; k
+ *                  already rotated at positions 0 .. Sk-1 (rope_apply).
+ *                  Keys past a row's position are masked; the rows of the
+ *                  chunk may see fewer keys when Sk < q_offset + Sq.
+ *                  May be NULL when Sk = 0 (every row then sees no key:
+ *                  output 0, lse -inf).
+ *   q_offset       >= 0: position of the chunk's first query.
+ *   cos_sin        NULL (q already rotated) or a table of n_table_rows >=
+ *                  q_offset + Sq rows: q is rotated on load.
+ *   lse            NULL or device [B][Hq][Sq] fp32.
+ * Other arguments as attn_prefill_sink_window; n_sink values above Sk act
+ * as Sk, windows above q_offset + Sq as q_offset + Sq.  dtype YRB_BF16
+ * only; Sk < 2^30 and q_offset + Sq < 2^30.  q_offset = 0, Sq = Sk = S is
+ * attn_prefill_sink_window.
+ */
+YRB_API int attn_prefill_sink_window_chunk(const void* q, const void* k, const void* v, void* o,
+                                           int32_t dtype, int64_t B, int64_t Sq, int64_t Sk,
+                                           int64_t Hq, int64_t Hkv, int64_t D,
+                                           const int64_t strides[4][3], int64_t q_offset,
+                                           const float* cos_sin, int64_t n_table_rows,
+                                           float softmax_scale, int64_t n_sink, int64_t window,
+                                           float* lse, void* workspace, void* stream);
+
+/*
  * attn_block_accumulate -- one ring-attention step on one device: fold the
  * key/value block that just arrived into the local query block's state
  * ([J] "Ring attention": each device accumulates its block's contribution

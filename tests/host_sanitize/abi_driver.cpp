@@ -93,6 +93,16 @@ void fixed_cases() {
                                 MIS, nullptr) == YRB_EALIGN);
   EXPECT(attn_prefill_sink_window(DEV, DEV, DEV, DEV, YRB_BF16, 1, 64, 4, 2, 128, s43, DEVF, 64, 0.1f, kMax, kMax,
                                   nullptr, nullptr, nullptr) == YRB_OK);
+  EXPECT(attn_prefill_sink_window_chunk(DEV, DEV, DEV, DEV, YRB_BF16, 1, 64, 128, 4, 2, 128, s43, 64, DEVF, 128, 0.1f,
+                                        4, 32, nullptr, nullptr, nullptr) == YRB_OK);
+  EXPECT(attn_prefill_sink_window_chunk(DEV, DEV, DEV, DEV, YRB_BF16, 1, 64, 128, 4, 2, 128, s43, 64, DEVF, 127, 0.1f,
+                                        4, 32, nullptr, nullptr, nullptr) == YRB_EINVAL);
+  EXPECT(attn_prefill_sink_window_chunk(DEV, nullptr, nullptr, DEV, YRB_BF16, 1, 64, 0, 4, 2, 128, s43, 64, DEVF, 128,
+                                        0.1f, kMax, kMax, nullptr, nullptr, nullptr) == YRB_OK);
+  EXPECT(attn_prefill_sink_window_chunk(DEV, nullptr, DEV, DEV, YRB_BF16, 1, 64, 8, 4, 2, 128, s43, 64, DEVF, 128, 0.1f,
+                                        4, 32, nullptr, nullptr, nullptr) == YRB_EINVAL);
+  EXPECT(attn_prefill_sink_window_chunk(DEV, DEV, DEV, DEV, YRB_BF16, 1, 64, 128, 4, 2, 128, s43, -1, DEVF, 128, 0.1f,
+                                        4, 32, nullptr, nullptr, nullptr) == YRB_EINVAL);
   const int64_t sq2[2] = {4 * 128, 128}, sc3[3] = {4 * 4100 * 128, 4100 * 128, 128};
   EXPECT(attn_decode_sink_window(DEV, DEV, DEV, DEV, YRB_BF16, 2, 4, 4, 128, 4, 4096, sq2, sc3, sq2,
                                  static_cast<int32_t*>(DEV), nullptr, DEVF, 4100, 0.1f, nullptr) == YRB_OK);
@@ -166,12 +176,19 @@ void sweep(int iters) {
                                  {P.stride(mul(S, Hkv, D)), P.stride(mul(Hkv, D)), P.stride(D)},
                                  {P.stride(mul(S, Hkv, D)), P.stride(mul(Hkv, D)), P.stride(D)},
                                  {P.stride(mul(S, Hq, D)), P.stride(mul(Hq, D)), P.stride(D)}};
-        if (next() & 1)
+        const int64_t pick3 = (int64_t)(next() % 3);
+        if (pick3 == 0)
           account(before, attn_prefill_sink_window(P.ptr(DEV), P.ptr(DEV), P.ptr(DEV), P.ptr(DEV), dt, B, S, Hq, Hkv, D,
                                                    s, static_cast<float*>(P.ptr(DEV)), P.size(S), P.scale(0.1f),
                                                    P.size(4), P.size(64), static_cast<float*>(P.ptr(nullptr)),
                                                    P.ptr(DEV), nullptr));
-        else
+        else if (pick3 == 1) {
+          const int64_t qo = P.size(mul(2, S)), Sk = P.size(add(qo, S));
+          account(before, attn_prefill_sink_window_chunk(P.ptr(DEV), P.ptr(DEV), P.ptr(DEV), P.ptr(DEV), dt, B, S, Sk, Hq,
+                                                         Hkv, D, s, qo, static_cast<float*>(P.ptr(DEV)),
+                                                         P.size(add(qo, S)), P.scale(0.1f), P.size(4), P.size(64),
+                                                         static_cast<float*>(P.ptr(nullptr)), P.ptr(DEV), nullptr));
+        } else
           account(before, attn_prefill_blockwise(P.ptr(DEV), P.ptr(DEV), P.ptr(DEV), P.ptr(DEV), dt, B, S, Hq, Hkv, D,
                                                  s, static_cast<float*>(P.ptr(DEV)), P.size(S), P.scale(0.1f),
                                                  P.small(1, -1, 2), static_cast<float*>(P.ptr(nullptr)),

@@ -226,6 +226,39 @@ def test_prefill_sink_window_validation():
     assert _prefill_sw(B=0, sink=1 << 40, win=1 << 40) == OK
 
 
+def _prefill_chunk(**over):
+    L = api.lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=0, B=1, Sq=64, Sk=128, Hq=4, Hkv=2, D=128,
+             strides=_strides(*([64 * 4 * 128, 4 * 128, 128] * 4)), qo=64, cs=FAKE, rows=128,
+             scale=0.1, sink=4, win=32, lse=None, ws=None)
+    a.update(over)
+    return L.attn_prefill_sink_window_chunk(a["q"], a["k"], a["v"], a["o"], a["dtype"], a["B"], a["Sq"],
+                                            a["Sk"], a["Hq"], a["Hkv"], a["D"], a["strides"], a["qo"],
+                                            a["cs"], a["rows"], ctypes.c_float(a["scale"]), a["sink"],
+                                            a["win"], a["lse"], a["ws"], None)
+
+
+def test_prefill_sink_window_chunk_validation():
+    # Every call fails before a launch (or has nothing to do); calls whose
+    # sizes pass stop at the misaligned q.
+    assert _prefill_chunk(dtype=1) == EUNSUP
+    assert _prefill_chunk(qo=-1) == EINVAL
+    assert _prefill_chunk(Sk=-1) == EINVAL
+    assert _prefill_chunk(Sq=-1) == EINVAL
+    assert _prefill_chunk(sink=-1) == EINVAL
+    assert _prefill_chunk(win=0) == EINVAL
+    assert _prefill_chunk(rows=127) == EINVAL                    # q_offset + Sq > table rows
+    assert _prefill_chunk(qo=(1 << 30) - 10, rows=1 << 31) == EINVAL
+    assert _prefill_chunk(Sk=1 << 30) == EINVAL
+    assert _prefill_chunk(k=None) == EINVAL                     # keys missing while Sk > 0
+    assert _prefill_chunk(q=MISALIGNED, k=None, v=None, Sk=0) == EALIGN   # no keys: K/V may be NULL
+    assert _prefill_chunk(q=MISALIGNED, cs=None, rows=0) == EALIGN        # q already rotated: no table
+    assert _prefill_chunk(q=MISALIGNED, sink=1 << 40, win=1 << 40) == EALIGN
+    assert _prefill_chunk(q=MISALIGNED) == EALIGN
+    assert _prefill_chunk(Sq=0) == OK
+    assert _prefill_chunk(B=0) == OK
+
+
 def _accum(**over):
     L = api.lib()
     a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=0, B=1, Sq=64, Sk=64, Hq=2, Hkv=2, D=64,

@@ -157,3 +157,95 @@ def test_prefill_sink_window_full_gqa32k():
                         window=window)[0, :, 0]
         worst = max(worst, max_abs(got, ref))
     assert worst <= BF16_TOL, worst
+
+
+# ---------------------------------------------------------------------------
+# attn_prefill_sink_window_chunk: one chunk of queries at an offset against
+# the sequence's keys, positions kept.
+# ---------------------------------------------------------------------------
+
+CHUNK_CASES = [
+    # B, Sq, Sk, q_offset, Hq, Hkv, D, n_sink, window
+    (1, 300, 1000, 700, 4, 2, 128, 4, 200),      # the last chunk of a 1000-token input
+    (1, 256, 768, 512, 2, 2, 128, 4, 129),       # tile-aligned chunk, keys ending with it
+    (2, 100, 900, 400, 4, 4, 64, 4, 64),         # keys past the chunk (masked)
+    (1, 500, 300, 200, 2, 1, 128, 70, 129),      # keys ending inside the chunk: late rows see sinks only
+    (1, 64, 5000, 4900, 2, 2, 128, 300, 257),    # several sink tiles, a long gap
+    (1, 1, 4097, 4096, 2, 2, 128, 4, 4096),      # one query, a window of exactly 4096
+]
+
+
+def _chunk_setup(B, Sq, Sk, q_offset, Hq, Hkv, D, seed):
+    rope = W.Rope(W.YARN, D, 1e4, 4.0, 128)
+    n_rows = max(q_offset + Sq, Sk, 1)
+    tab, th, _ = api.rope_tables_build(api.RopeConfig.of(rope), n_rows)
+    qv, q = draw((B, Sq, Hq, D), seed, "bf16")
+    kv, k = draw((B, Sk, Hkv, D), seed + 1, "bf16")
+    vv, v = draw((B, Sk, Hkv, D), seed + 2, "bf16")
+    scale = R.softmax_scale(rope.kind, rope.scale, D)
+    return tab, th, scale, (qv, kv, vv), (q, k, v)
+
+
+@pytest.mark.parametrize("B,Sq,Sk,q_offset,Hq,Hkv,D,n_sink,window", CHUNK_CASES)
+def test_prefill_sink_window_chunk(B, Sq, Sk, q_offset, Hq, Hkv, D, n_sink, window):
+    require_gpu()
+    import torch
+    tab, th, scale, (qv, kv, vv), (q, k, v) = _chunk_setup(B, Sq, Sk, q_offset, Hq, Hkv, D, 60 + Sq + q_offset)
+    say(f"attn_prefill_sink_window_chunk B={B} Sq={Sq} Sk={Sk} q_offset={q_offset} Hq={Hq} Hkv={Hkv} D={D} "
+        f"sink={n_sink} win={window}")
+    kr = api.rope_apply(k, tab)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    o = api.attn_prefill_sink_window_chunk(q, kr, v, scale, n_sink, window, q_offset, cos_sin=tab, lse=lse,
+                                           workspace=api.new_workspace())
+    torch.cuda.synchronize()
+    ref = A.prefill(qv, kv, vv, th, scale, q_offset=q_offset, n_sink=n_sink, window=window)
+    assert max_abs(host(o), ref) <= BF16_TOL
+    q_pos, k_pos = q_offset + np.arange(Sq), np.arange(Sk)
+    qr = R.rotate_bshd(qv, th, q_pos)
+    krr = R.rotate_bshd(kv, th, k_pos)
+    vis = A.sink_window_visible(n_sink, window)
+    lse_h = host(lse)
+    for b in range(B):
+        for h in range(Hq):
+            g = A.kv_head(h, Hq, Hkv)
+            _, m, l = A.attention_full(qr[b, :, h], krr[b, :, g], vv[b, :, g], scale, q_pos, k_pos, vis,
+                                       return_state=True)
+            assert max_abs(lse_h[b, h], m + np.log(l)) <= BF16_TOL
+
+
+def test_prefill_sink_window_chunk_without_keys():
+    # Sk = 0: every row sees no key; the output is 0 and the log-sum-exp
+    # -inf, with no key or value buffer at all.
+    require_gpu()
+    import torch
+    tab, _, scale, _, (q, _, _) = _chunk_setup(1, 33, 0, 10, 2, 2, 64, 5)
+    say("attn_prefill_sink_window_chunk Sk=0")
+    empty = torch.empty((1, 0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((1, 2, 33), dtype=torch.float32, device="cuda")
+    o = torch.full_like(q, float("nan"))
+    api.attn_prefill_sink_window_chunk(q, empty, empty, scale, 4, 16, 10, cos_sin=tab, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(o)) == 0
+    assert bool(torch.all(torch.isneginf(lse)))
+
+
+def test_prefill_sink_window_in_chunks():
+    # A 2000-token input prefilled in four uneven chunks, each against the
+    # keys up to its own end (the key and value tensors grow as the chunks
+    # arrive): every row against the oracle, and against the one-call prefill.
+    require_gpu()
+    import torch
+    S, Hq, Hkv, D, n_sink, window = 2000, 4, 2, 128, 4, 700
+    tab, th, scale, (qv, kv, vv), (q, k, v) = _chunk_setup(1, S, S, 0, Hq, Hkv, D, 321)
+    kr = api.rope_apply(k, tab)
+    say(f"attn_prefill_sink_window S={S} in one call and in four chunks")
+    whole = api.attn_prefill_sink_window(q, kr, v, scale, n_sink, window, cos_sin=tab)
+    ref = A.prefill(qv, kv, vv, th, scale, n_sink=n_sink, window=window)
+    bounds = [0, 512, 1100, 1700, S]
+    for c0, c1 in zip(bounds[:-1], bounds[1:]):
+        o = api.attn_prefill_sink_window_chunk(q[:, c0:c1], kr[:, :c1], v[:, :c1], scale, n_sink, window, c0,
+                                               cos_sin=tab)
+        torch.cuda.synchronize()
+        got = host(o)
+        assert max_abs(got, ref[:, c0:c1]) <= BF16_TOL, (c0, c1)
+        assert max_abs(got, host(whole[:, c0:c1])) <= BF16_TOL, (c0, c1)

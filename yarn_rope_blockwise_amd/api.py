@@ -22,7 +22,7 @@ LAYOUT_HALF, LAYOUT_INTERLEAVED = 0, 1
 ACC_FIRST, ACC_FINALIZE = 1, 2
 WORKSPACE_BYTES = 64      # YRB_WORKSPACE_BYTES
 EXPORTS = ("rope_tables_build", "rope_tables_build_factors", "rope_apply", "attn_prefill_blockwise",
-           "attn_prefill_blockwise_noalloc", "attn_prefill_sink_window",
+           "attn_prefill_blockwise_noalloc", "attn_prefill_sink_window", "attn_prefill_sink_window_chunk",
            "attn_block_accumulate", "attn_decode_sink_window", "attn_decode_sink_window_fp8",
            "rope_apply_ex", "attn_decode_sink_window_ex", "yrb_status_str")
 
@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_sink_window.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64,
                                                _i64, _i64p, _vp, _i64, ctypes.c_float, _i64, _i64,
                                                _vp, _vp, _vp]
+        L.attn_prefill_sink_window_chunk.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64,
+                                                     _i64, _i64, _i64p, _i64, _vp, _i64, ctypes.c_float,
+                                                     _i64, _i64, _vp, _vp, _vp]
         L.attn_block_accumulate.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64,
                                             _i64, _i64p, _i64, _i64, _vp, _i64, ctypes.c_float,
                                             _i32, _vp, _vp, _vp, _i32, _vp, _i64p, _vp, _vp]
@@ -302,6 +305,26 @@ def attn_prefill_sink_window(q, k, v, softmax_scale: float, n_sink: int, window:
     _check("attn_prefill_sink_window", lib().attn_prefill_sink_window(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), B, S, Hq, Hkv, D, strides,
         _ptr(cos_sin), n_rows, float(softmax_scale), int(n_sink), int(window), _ptr(lse),
+        _ptr(workspace), _stream()))
+    return out
+
+
+def attn_prefill_sink_window_chunk(q, k, v, softmax_scale: float, n_sink: int, window: int,
+                                   q_offset: int, cos_sin=None, out=None, lse=None, workspace=None):
+    """One chunk of a sink+window prefill: q [B,Sq,Hq,D] at positions
+    q_offset.., k/v [B,Sk,Hkv,D] at positions 0.. (k already rotated); key t
+    is visible to query position p iff t <= p and (t < n_sink or t > p -
+    window).  bf16 only."""
+    import torch
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    strides = _arr(_bsh_strides(q) + _bsh_strides(k) + _bsh_strides(v) + _bsh_strides(out))
+    n_rows = 0 if cos_sin is None else cos_sin.shape[0]
+    _check("attn_prefill_sink_window_chunk", lib().attn_prefill_sink_window_chunk(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), B, Sq, Sk, Hq, Hkv, D, strides,
+        int(q_offset), _ptr(cos_sin), n_rows, float(softmax_scale), int(n_sink), int(window), _ptr(lse),
         _ptr(workspace), _stream()))
     return out
 

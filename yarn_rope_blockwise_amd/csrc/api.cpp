@@ -209,24 +209,25 @@ int rope_apply_ex(const void* x, void* y, int32_t dtype, int64_t B, int64_t S, i
 
 namespace {
 
-// Validation and launch shared by the prefill entry points; window > 0
-// turns on the sink+window mask (bf16 pipelined kernel).
-int prefill_common(const void* q, const void* k, const void* v, void* o, int32_t dtype, int64_t B, int64_t S,
-                   int64_t Hq, int64_t Hkv, int64_t D, const int64_t strides[4][3], const float* cos_sin,
-                   int64_t n_table_rows, float softmax_scale, int32_t causal, int64_t n_sink, int64_t window,
-                   float* lse, void* workspace, void* stream) {
+// Validation and launch shared by the prefill entry points: Sq queries at
+// positions q_offset.., Sk keys at positions 0..; window > 0 turns on the
+// sink+window mask (bf16 pipelined kernel).
+int prefill_common(const void* q, const void* k, const void* v, void* o, int32_t dtype, int64_t B, int64_t Sq,
+                   int64_t Sk, int64_t q_offset, int64_t Hq, int64_t Hkv, int64_t D, const int64_t strides[4][3],
+                   const float* cos_sin, int64_t n_table_rows, float softmax_scale, int32_t causal,
+                   int64_t n_sink, int64_t window, float* lse, void* workspace, void* stream) {
   if (!dtype_ok(dtype)) return YRB_EUNSUPPORTED;
   if (!dim_ok(D)) return YRB_EUNSUPPORTED;
-  if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return YRB_EINVAL;
+  if (B < 0 || Sq < 0 || Sk < 0 || q_offset < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return YRB_EINVAL;
   if (causal != 0 && causal != 1) return YRB_EINVAL;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return YRB_EINVAL;
   if (!strides) return YRB_EINVAL;
-  if (B == 0 || S == 0) return YRB_OK;
-  if (!q || !k || !v || !o) return YRB_EINVAL;
-  if (S >= kLim31 || Hq >= kLim31) return YRB_EINVAL;
+  if (B == 0 || Sq == 0) return YRB_OK;
+  if (!q || !o || (Sk > 0 && (!k || !v))) return YRB_EINVAL;
+  if (!add_lt(q_offset, Sq, kLim31) || Sk >= kLim31 || Hq >= kLim31) return YRB_EINVAL;
   // grid: bf16, one workgroup per (256-row query tile, batch, head); fp32,
   // 64-row tiles with heads and batches in the y and z extents
-  if (dtype == YRB_BF16 ? !mul_le(B, Hq, kMaxBlocks) || !mul_le((S + 255) / 256, B * Hq, kMaxBlocks)
+  if (dtype == YRB_BF16 ? !mul_le(B, Hq, kMaxBlocks) || !mul_le((Sq + 255) / 256, B * Hq, kMaxBlocks)
                         : Hq > kMaxYZ || B > kMaxYZ)
     return YRB_EINVAL;
   for (int t = 0; t < 4; ++t) {
@@ -238,7 +239,7 @@ int prefill_common(const void* q, const void* k, const void* v, void* o, int32_t
     return YRB_EALIGN;
   if (cos_sin) {
     if (!aligned16(cos_sin)) return YRB_EALIGN;
-    if (S > n_table_rows) return YRB_EINVAL;
+    if (n_table_rows < 0 || q_offset + Sq > n_table_rows) return YRB_EINVAL;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   yrb::AttnArgs a{};
@@ -255,11 +256,11 @@ int prefill_common(const void* q, const void* k, const void* v, void* o, int32_t
   a.lse = lse;
   a.cos_sin = cos_sin;
   a.B = B;
-  a.Sq = S;
-  a.Sk = S;
+  a.Sq = Sq;
+  a.Sk = Sk;
   a.Hq = Hq;
   a.Hkv = Hkv;
-  a.q_offset = 0;
+  a.q_offset = q_offset;
   a.k_offset = 0;
   a.softmax_scale = softmax_scale;
   a.causal = causal;
@@ -282,8 +283,8 @@ int attn_prefill_blockwise(const void* q, const void* k, const void* v, void* o,
                            const int64_t strides[4][3], const float* cos_sin,
                            int64_t n_table_rows, float softmax_scale, int32_t causal, float* lse,
                            void* workspace, void* stream) {
-  return prefill_common(q, k, v, o, dtype, B, S, Hq, Hkv, D, strides, cos_sin, n_table_rows, softmax_scale,
-                        causal, 0, 0, lse, workspace, stream);
+  return prefill_common(q, k, v, o, dtype, B, S, S, 0, Hq, Hkv, D, strides, cos_sin, n_table_rows,
+                        softmax_scale, causal, 0, 0, lse, workspace, stream);
 }
 
 int attn_prefill_sink_window(const void* q, const void* k, const void* v, void* o, int32_t dtype,
@@ -291,14 +292,24 @@ int attn_prefill_sink_window(const void* q, const void* k, const void* v, void* 
                              const int64_t strides[4][3], const float* cos_sin, int64_t n_table_rows,
                              float softmax_scale, int64_t n_sink, int64_t window, float* lse,
                              void* workspace, void* stream) {
+  return attn_prefill_sink_window_chunk(q, k, v, o, dtype, B, S, S, Hq, Hkv, D, strides, 0, cos_sin, n_table_rows,
+                                        softmax_scale, n_sink, window, lse, workspace, stream);
+}
+
+int attn_prefill_sink_window_chunk(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                                   int64_t B, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv, int64_t D,
+                                   const int64_t strides[4][3], int64_t q_offset, const float* cos_sin,
+                                   int64_t n_table_rows, float softmax_scale, int64_t n_sink, int64_t window,
+                                   float* lse, void* workspace, void* stream) {
   if (dtype != YRB_BF16) return YRB_EUNSUPPORTED;
-  if (n_sink < 0 || window < 1) return YRB_EINVAL;
-  if (S >= (int64_t(1) << 30)) return YRB_EINVAL;
-  // A window of S or more reaches every earlier key: plain causal.  Sinks
-  // past S are all the keys there are.
-  return prefill_common(q, k, v, o, dtype, B, S, Hq, Hkv, D, strides, cos_sin, n_table_rows, softmax_scale,
-                        1, std::min(n_sink, S), std::min(window, std::max<int64_t>(S, 1)), lse, workspace,
-                        stream);
+  if (n_sink < 0 || window < 1 || Sq < 0 || Sk < 0 || q_offset < 0) return YRB_EINVAL;
+  if (Sk >= (int64_t(1) << 30) || !add_lt(q_offset, Sq, int64_t(1) << 30)) return YRB_EINVAL;
+  // A window reaching past position 0 from the last query sees every
+  // earlier key: plain causal.  Sinks past Sk are all the keys there are.
+  const int64_t q_end = q_offset + Sq;
+  return prefill_common(q, k, v, o, dtype, B, Sq, Sk, q_offset, Hq, Hkv, D, strides, cos_sin, n_table_rows,
+                        softmax_scale, 1, std::min(n_sink, Sk), std::min(window, std::max<int64_t>(q_end, 1)), lse,
+                        workspace, stream);
 }
 
 int attn_block_accumulate(const void* q, const void* k_blk, const void* v_blk, int32_t dtype,
