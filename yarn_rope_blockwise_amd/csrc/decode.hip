@@ -41,6 +41,12 @@
 //    pairs.
 //  * A lane addresses its head's cache with a 32-bit offset (one 24-bit
 //    multiply) from a wave-uniform base; the host bounds the span.
+//  * With 8 query heads per key head (bf16 cache, half-split pairs) the
+//    logits of a round's keys come from MFMAs instead: the lanes write
+//    their keys' rotated rows (bf16) into an LDS tile, one chain of
+//    v_mfma_f32_16x16x32_bf16 multiplies it by the 8 heads' queries, and
+//    the softmax keeps one reference per head for the whole wave; P returns
+//    to the value lanes through LDS and PV stays on the VALU.
 //  * Online softmax in the exp2 domain, the logit scale folded into the
 //    query.  The running max is kept per key group (the lanes that share a
 //    key agree on it), and a group moves its reference only when a key
@@ -306,6 +312,13 @@ void decode_kernel(DecodeArgs a, int parts) {
   constexpr int MERGE_F = G * (D + 2);               // floats a wave leaves for the merge
   constexpr int U = Cfg::U;
   constexpr bool AQ = Cfg::ANCHOR_Q;
+  // bf16 cache, half-split pairs, 8 query heads per key head: the logits of
+  // a round's keys against all the heads come from one MFMA chain over the
+  // rotated keys (bf16, through a per-wave LDS tile) instead of per-lane dot
+  // products and cross-lane sums.  (At 4 heads the chain's latency, one round
+  // at a time, costs more than the dot products it replaces.)
+  constexpr bool MF = !FP8 && !IL && G >= 8;
+  constexpr int KROWB = 2 * D + 16;                  // bytes of a key row in that tile (padded)
   using KV = KVRound<FP8>;
   using LM = LaneMap<D, FP8, IL>;
 
@@ -315,6 +328,11 @@ void decode_kernel(DecodeArgs a, int parts) {
   // block), per head and lane chunk: the step reads it rather than hold it
   // in registers.
   __shared__ __attribute__((aligned(16))) float qrow[kWaves][AQ ? G * D : 1];
+  // MF: the round's rotated keys, one bf16 row per key (the rows past the
+  // round's keys are never written and their logits never used), and the
+  // round's P by (key, head).
+  __shared__ __attribute__((aligned(16))) char ktile_raw[kWaves][MF ? 16 * KROWB : 16];
+  __shared__ __attribute__((aligned(16))) float ptile[kWaves][MF ? 16 * 16 : 4];
   YRB_LDS char* const tab = (YRB_LDS char*)tab_raw;
 
   const int lane = threadIdx.x & 63;
@@ -381,10 +399,46 @@ void decode_kernel(DecodeArgs a, int parts) {
     }
   };
   // Compose mode: the query at len - 1, held for the whole launch.
-  float qx[AQ ? 1 : G][8], qz[AQ ? 1 : G][8];
-  if constexpr (!AQ) {
+  float qx[(AQ || MF) ? 1 : G][8], qz[(AQ || MF) ? 1 : G][8];
+  if constexpr (!AQ && !MF) {
 #pragma unroll
     for (int g = 0; g < G; ++g) query_at(g, len > 0 ? len - 1 : 0, qx[g], qz[g]);
+  }
+  // MF: the query of head lane % 16 (zero past G) rotated at len - 1 and
+  // scaled, as the B operand of v_mfma_f32_16x16x32_bf16: for k-step ks the
+  // lane holds dimensions 32 ks + 8 (lane / 16) .. + 7.
+  bf16x8 qb[MF ? D / 32 : 1];
+  if constexpr (MF) {
+    const int n = lane & 15;
+    const int pos = len > 0 ? len - 1 : 0;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      float f[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) f[u] = 0.f;
+      if (n < G) {
+        const int d0 = 32 * ks + 8 * (lane >> 4);
+        const bool first = d0 < D / 2;
+        const int p0 = first ? d0 : d0 - D / 2;      // the 8 pairs p0 .. p0+7
+        const __bf16* qp = qhead + (int64_t)n * a.qs[1];
+        float xa[8], xb[8];
+        unpack8(*reinterpret_cast<const u32x4*>(qp + p0), xa);
+        unpack8(*reinterpret_cast<const u32x4*>(qp + D / 2 + p0), xb);
+        const float* row = a.cos_sin + (int64_t)pos * D + 2 * p0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(row + 4 * w);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int u = 2 * w + h;
+            float x = xa[u], z = xb[u];
+            rot(x, z, t[2 * h], t[2 * h + 1]);
+            f[u] = (first ? x : z) * scale_log2;
+          }
+        }
+      }
+      qb[ks] = __builtin_bit_cast(bf16x8, pack8(f));
+    }
   }
 
   // Running max, sum and output per head.  The max is kept per key group
@@ -547,9 +601,6 @@ void decode_kernel(DecodeArgs a, int parts) {
 #pragma unroll
           for (int w = 0; w < 8; ++w) add_angle(c[w], sn[w], rc[w], rs[w]);
         }
-        // Logit of the lane's key with each head (log2 units), partial over
-        // the lane's 8 pairs.
-        float acc[G];
         float ka[8], kb2[8], x[8], z[8];
         if constexpr (FP8) {
           CT::unpack(klo8, ka);
@@ -561,38 +612,106 @@ void decode_kernel(DecodeArgs a, int parts) {
         pairs_of<IL>(ka, kb2, x, z);
 #pragma unroll
         for (int w = 0; w < 8; ++w) rot(x[w], z[w], c[w], sn[w]);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float sum = 0.f;
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            const float qxw = AQ ? qx_s[AQ ? g : 0][w] : qx[AQ ? 0 : g][w];
-            const float qzw = AQ ? qz_s[AQ ? g : 0][w] : qz[AQ ? 0 : g][w];
-            sum = __builtin_fmaf(qxw, x[w], __builtin_fmaf(qzw, z[w], sum));
-          }
-          acc[g] = sum;
-        }
         float p[G];
+        if constexpr (MF) {
+          // The key's rotated row into the tile; then S = K Q^T for the
+          // round's keys (rows) and the heads (columns) by MFMA: the lane
+          // holds rows 4 (lane / 16) + i, i < 4, of column lane % 16.
+          YRB_LDS char* const kt = (YRB_LDS char*)ktile_raw[wave];
+          const int p0 = LM::pair(cc, 0);
+          *reinterpret_cast<YRB_LDS u32x4*>(kt + kg * KROWB + 2 * p0) = pack8(x);
+          *reinterpret_cast<YRB_LDS u32x4*>(kt + kg * KROWB + D + 2 * p0) = pack8(z);
+          f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float sc = group_sum<TPK>(acc[g]);
-          sc = (!MASK || kv.ok) ? sc : -INFINITY;
-          // a group's reference moves when its key beats it by more than
-          // the threshold: rare once every group has seen a few keys
-          const bool grow = sc > m[g] + kDecTau;
-          if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float alpha = grow ? fast_exp2(m[g] - sc) : 1.0f;   // 0 from the empty state
-            m[g] = grow ? sc : m[g];
-            l[g] *= alpha;
+          for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 af =
+                *reinterpret_cast<const YRB_LDS bf16x8*>(kt + (lane & 15) * KROWB + 64 * ks + 16 * (lane >> 4));
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qb[ks], sacc, 0, 0, 0);
+          }
+          const int n = lane & 15;
+          float sv[4], mx = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kr = 4 * (lane >> 4) + i;
+            const bool ok = kr < KPW && (!MASK || t * KPW + kr < len);
+            sv[i] = ok ? sacc[i] : -INFINITY;
+            mx = fmaxf(mx, sv[i]);
+          }
+          // the round's max for the lane's head (the lanes 16 and 32 apart
+          // hold the same head's other keys)
+          {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+          }
+          if constexpr (KPW > 8) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+          }
+          // One reference per head for the whole wave (lane g holds head
+          // g's max): it moves when the round's max beats it by more than
+          // the threshold.
+          float ml = m[0];
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float tm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), g));
+            if (tm > m[g] + kDecTau) {
+              const float alpha = fast_exp2(m[g] - tm);   // 0 from the empty state
+              m[g] = tm;
+              l[g] *= alpha;
+#pragma unroll
+              for (int w = 0; w < 8; ++w) {
+                o_lo[g][w] *= alpha;
+                o_hi[g][w] *= alpha;
+              }
+            }
+            ml = n == g ? m[g] : ml;
+          }
+          float* const pt = ptile[wave];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pt[(4 * (lane >> 4) + i) * 16 + n] = sv[i] == -INFINITY ? 0.f : fast_exp2(sv[i] - ml);
+          // P of the lane's key for every head
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            p[g] = pt[kg * 16 + g];
+            l[g] += p[g];
+          }
+        } else {
+          // Logit of the lane's key with each head (log2 units), partial
+          // over the lane's 8 pairs.
+          float acc[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float sum = 0.f;
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
-              o_lo[g][w] *= alpha;
-              o_hi[g][w] *= alpha;
+              const float qxw = AQ ? qx_s[AQ ? g : 0][w] : qx[AQ ? 0 : g][w];
+              const float qzw = AQ ? qz_s[AQ ? g : 0][w] : qz[AQ ? 0 : g][w];
+              sum = __builtin_fmaf(qxw, x[w], __builtin_fmaf(qzw, z[w], sum));
             }
+            acc[g] = sum;
           }
-          // 0 for a slot without an entry (whose group may have no reference yet)
-          p[g] = (!MASK || kv.ok) ? fast_exp2(sc - m[g]) : 0.f;
-          l[g] += p[g];
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float sc = group_sum<TPK>(acc[g]);
+            sc = (!MASK || kv.ok) ? sc : -INFINITY;
+            // a group's reference moves when its key beats it by more than
+            // the threshold: rare once every group has seen a few keys
+            const bool grow = sc > m[g] + kDecTau;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+              const float alpha = grow ? fast_exp2(m[g] - sc) : 1.0f;   // 0 from the empty state
+              m[g] = grow ? sc : m[g];
+              l[g] *= alpha;
+#pragma unroll
+              for (int w = 0; w < 8; ++w) {
+                o_lo[g][w] *= alpha;
+                o_hi[g][w] *= alpha;
+              }
+            }
+            // 0 for a slot without an entry (whose group may have no reference yet)
+            p[g] = (!MASK || kv.ok) ? fast_exp2(sc - m[g]) : 0.f;
+            l[g] += p[g];
+          }
         }
         // P V (a slot without an entry adds 0: its raw words are zeroed,
         // whatever the cache holds there, NaN codes included)
