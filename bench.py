@@ -65,14 +65,14 @@ MEASURED_TRAFFIC = {
         "fetch_kib": 1390411, "write_kib": 262182},
     "attn_bf16_pp_kernel_window": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
         "fetch_kib": 731775, "write_kib": 131091},
-    "decode_kernel": {"files": _DEC, "sha256": "3e22023e53b31807fe0a5622ffbf530b7ad649960aeec801860451dd1a2934c7",
-        "fetch_kib": 2100150, "write_kib": 512},
-    "decode_kernel_fp8": {"files": _DEC, "sha256": "3e22023e53b31807fe0a5622ffbf530b7ad649960aeec801860451dd1a2934c7",
-        "fetch_kib": 1050492, "write_kib": 512},
-    "decode_kernel_gqa": {"files": _DEC, "sha256": "3e22023e53b31807fe0a5622ffbf530b7ad649960aeec801860451dd1a2934c7",
-        "fetch_kib": 526100, "write_kib": 1536},
-    "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": "3e22023e53b31807fe0a5622ffbf530b7ad649960aeec801860451dd1a2934c7",
-        "fetch_kib": 264135, "write_kib": 2560},
+    "decode_kernel": {"files": _DEC, "sha256": "d1ae78de6032f9ab0c99778156ea1ac477ccdc94d0348416166cb03a51e34598",
+        "fetch_kib": 2100179, "write_kib": 512},
+    "decode_kernel_fp8": {"files": _DEC, "sha256": "d1ae78de6032f9ab0c99778156ea1ac477ccdc94d0348416166cb03a51e34598",
+        "fetch_kib": 1050510, "write_kib": 512},
+    "decode_kernel_gqa": {"files": _DEC, "sha256": "d1ae78de6032f9ab0c99778156ea1ac477ccdc94d0348416166cb03a51e34598",
+        "fetch_kib": 526086, "write_kib": 1536},
+    "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": "d1ae78de6032f9ab0c99778156ea1ac477ccdc94d0348416166cb03a51e34598",
+        "fetch_kib": 264138, "write_kib": 2560},
     "attn_bf16_pp_kernel_ring": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",  # per step of 8 launches
         "fetch_kib": 9303140, "write_kib": 1130655},
 }
