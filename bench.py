@@ -55,16 +55,16 @@ METRIC = "YaRN-RoPE causal prefill TFLOP/s @16k (frac bf16 peak); sink decode HB
 _PP = ("csrc/attn_pp.hip", "csrc/attn_frag.h", "csrc/common.h")
 _DEC = ("csrc/decode.hip", "csrc/common.h")
 MEASURED_TRAFFIC = {
-    "attn_bf16_pp_kernel": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
-        "fetch_kib": 1045318, "write_kib": 131091},
-    "attn_bf16_pp_kernel_gqa_prefill_32k_pi8": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
-        "fetch_kib": 1428135, "write_kib": 262182},
-    "attn_bf16_pp_kernel_gqa_prefill_32k_ntk8": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
-        "fetch_kib": 1438930, "write_kib": 262182},
-    "attn_bf16_pp_kernel_gqa_prefill_32k_yarn8": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
-        "fetch_kib": 1390411, "write_kib": 262182},
-    "attn_bf16_pp_kernel_window": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",
-        "fetch_kib": 731775, "write_kib": 131091},
+    "attn_bf16_pp_kernel": {"files": _PP, "sha256": "141d016353be8f28d00c408a954442f6e543fa7ac759020ac831322bee7703d8",
+        "fetch_kib": 1041111, "write_kib": 131091},
+    "attn_bf16_pp_kernel_gqa_prefill_32k_pi8": {"files": _PP, "sha256": "141d016353be8f28d00c408a954442f6e543fa7ac759020ac831322bee7703d8",
+        "fetch_kib": 1503660, "write_kib": 262182},
+    "attn_bf16_pp_kernel_gqa_prefill_32k_ntk8": {"files": _PP, "sha256": "141d016353be8f28d00c408a954442f6e543fa7ac759020ac831322bee7703d8",
+        "fetch_kib": 1485341, "write_kib": 262182},
+    "attn_bf16_pp_kernel_gqa_prefill_32k_yarn8": {"files": _PP, "sha256": "141d016353be8f28d00c408a954442f6e543fa7ac759020ac831322bee7703d8",
+        "fetch_kib": 1427001, "write_kib": 262182},
+    "attn_bf16_pp_kernel_window": {"files": _PP, "sha256": "141d016353be8f28d00c408a954442f6e543fa7ac759020ac831322bee7703d8",
+        "fetch_kib": 532525, "write_kib": 131082},
     "decode_kernel": {"files": _DEC, "sha256": "d1ae78de6032f9ab0c99778156ea1ac477ccdc94d0348416166cb03a51e34598",
         "fetch_kib": 2100179, "write_kib": 512},
     "decode_kernel_fp8": {"files": _DEC, "sha256": "d1ae78de6032f9ab0c99778156ea1ac477ccdc94d0348416166cb03a51e34598",
@@ -73,8 +73,8 @@ MEASURED_TRAFFIC = {
         "fetch_kib": 526086, "write_kib": 1536},
     "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": "d1ae78de6032f9ab0c99778156ea1ac477ccdc94d0348416166cb03a51e34598",
         "fetch_kib": 264138, "write_kib": 2560},
-    "attn_bf16_pp_kernel_ring": {"files": _PP, "sha256": "a118845cbd2e006d9f92528c6ddce09ca87223b5c9748bff8061762c8af57bf7",  # per step of 8 launches
-        "fetch_kib": 9303140, "write_kib": 1130655},
+    "attn_bf16_pp_kernel_ring": {"files": _PP, "sha256": "141d016353be8f28d00c408a954442f6e543fa7ac759020ac831322bee7703d8",  # per step of 8 launches
+        "fetch_kib": 9391301, "write_kib": 1130850},
 }
 FETCH_FACTOR, WRITE_FACTOR = 1.99996, 1.0
 

@@ -96,8 +96,9 @@ extern "C" {
 
 /* Bytes of the optional `workspace` of the prefill calls and
  * attn_block_accumulate: a device buffer, 16-byte aligned, that holds zeros
- * before its first use.  Given one, the last 30 % of the launch's grid
- * takes its work items from a counter there, so that the XCDs, which under
+ * before its first use.  Given one, the last part of the launch's grid
+ * (30 %; 15 % under the sink+window mask) takes its work items from a
+ * counter there, so that the XCDs, which under
  * load run at clocks a few percent apart, finish together; each call leaves
  * the workspace as it found it (zero), so one workspace serves any number
  * of calls in sequence on a stream.  Calls that may run at the same time
