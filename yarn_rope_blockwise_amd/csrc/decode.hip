@@ -46,7 +46,9 @@
 //    their keys' rotated rows (bf16) into an LDS tile, one chain of
 //    v_mfma_f32_16x16x32_bf16 multiplies it by the 8 heads' queries, and
 //    the softmax keeps one reference per head for the whole wave; P returns
-//    to the value lanes through LDS and PV stays on the VALU.
+//    to the value lanes through LDS and PV stays on the VALU.  That path
+//    reads each key's R(e) from the caller's table (L2-resident: the rows
+//    are the same for every sequence and head) rather than composing it.
 //  * Online softmax in the exp2 domain, the logit scale folded into the
 //    query.  The running max is kept per key group (the lanes that share a
 //    key agree on it), and a group moves its reference only when a key
@@ -318,6 +320,14 @@ void decode_kernel(DecodeArgs a, int parts) {
   // products and cross-lane sums.  (At 4 heads the chain's latency, one round
   // at a time, costs more than the dot products it replaces.)
   constexpr bool MF = !FP8 && !IL && G >= 8;
+  // MF: each key's R(e) is read from the caller's table (the rows of the
+  // cache positions are the same for every sequence and head, so they stay
+  // in L2) instead of composed from LDS rows.  This path is heavy on LDS
+  // (the key tile, P), and without the composition it also holds no spill.
+  // (The dot-product path measured slower with it: 0.181 -> 0.214 ms for
+  // 32 query / 8 key heads; the 4 extra loads per round cost more than the
+  // 40 VALU instructions they save.)
+  constexpr bool TROW = MF;
   constexpr int KROWB = 2 * D + 16;                  // bytes of a key row in that tile (padded)
   using KV = KVRound<FP8>;
   using LM = LaneMap<D, FP8, IL>;
@@ -357,7 +367,7 @@ void decode_kernel(DecodeArgs a, int parts) {
 
   // R(j) and R(32 j), j < 32, into LDS (rows past the cache are never used:
   // clamped).
-  for (int idx = threadIdx.x; idx < Cfg::ROW_W * (D / 4); idx += kWaves * 64) {
+  for (int idx = threadIdx.x; idx < (TROW ? 0 : Cfg::ROW_W * (D / 4)); idx += kWaves * 64) {
     const int row = idx / (D / 4), k = idx % (D / 4);
     const int pos = row < Cfg::ROW_32 ? row : kKPS * (row - Cfg::ROW_32);
     const f32x4 t = *reinterpret_cast<const f32x4*>(a.cos_sin + (int64_t)min(pos, C - 1) * D + 4 * k);
@@ -504,6 +514,18 @@ void decode_kernel(DecodeArgs a, int parts) {
     // into the wave's LDS row (the lanes of key group 0 writing it).
     int a_cur = -1;
     float rc[8], rs[8];              // compose: R(1024 a2 + 32 b1)
+    // TROW: (cos, sin) of the lane's pairs at the key position of the next
+    // round, loaded one round ahead from the caller's table (the same rows
+    // for every sequence and head, so they stay in L2).
+    // Two sets, by the parity of the round (a step is an even number of
+    // rounds), so that no copy is needed.
+    float tc[2][8], ts[2][8];
+    auto load_trow = [&](int t, int set) {
+      const int e = min(t * KPW + kg, C - 1);
+      row_pairs<LM>(a.cos_sin + (int64_t)e * D, cc, tc[set], ts[set]);
+    };
+    static_assert(ROUNDS % 2 == 0, "rounds alternate the table sets");
+    if constexpr (TROW) load_trow(t_begin, 0);
 
     // MASK: the step reaches past the last entry (its missing keys are
     // masked); the other steps skip the test.
@@ -514,7 +536,7 @@ void decode_kernel(DecodeArgs a, int parts) {
       const int A = s * kKPS;
       const int a2 = A >> 10, b1 = (A >> 5) & 31;
       const int jw = Cfg::ROW_W + wave;
-      if (a2 != a_cur) {
+      if (!TROW && a2 != a_cur) {
         // AQ: R(1024 a2)^T R(len - 1) q = R(len - 1 - 1024 a2) q, into the
         // wave's query rows; compose: R(1024 a2) into its table row.
         if constexpr (AQ) {
@@ -550,7 +572,7 @@ void decode_kernel(DecodeArgs a, int parts) {
         __builtin_amdgcn_wave_barrier();
       }
       float c1[8], s1[8];
-      lds_pairs<D, LM>(tab, Cfg::ROW_32 + b1, cc, c1, s1);
+      if constexpr (!TROW) lds_pairs<D, LM>(tab, Cfg::ROW_32 + b1, cc, c1, s1);
       float qx_s[AQ ? G : 1][8], qz_s[AQ ? G : 1][8];   // AQ: the query this step's keys meet
       if constexpr (AQ) {
 #pragma unroll
@@ -563,7 +585,7 @@ void decode_kernel(DecodeArgs a, int parts) {
             rot_t(qx_s[g][w], qz_s[g][w], c1[w], s1[w]);
           }
         }
-      } else {
+      } else if constexpr (!TROW) {
         float c2[8], s2[8];
         lds_pairs<D, LM>(tab, jw, cc, c2, s2);
 #pragma unroll
@@ -596,10 +618,18 @@ void decode_kernel(DecodeArgs a, int parts) {
           }
         }
         float c[8], sn[8];
-        lds_pairs<D, LM>(tab, j, cc, c, sn);
-        if constexpr (!AQ) {
+        if constexpr (TROW) {
 #pragma unroll
-          for (int w = 0; w < 8; ++w) add_angle(c[w], sn[w], rc[w], rs[w]);
+          for (int w = 0; w < 8; ++w) {
+            c[w] = tc[r & 1][w];
+            sn[w] = ts[r & 1][w];
+          }
+        } else {
+          lds_pairs<D, LM>(tab, j, cc, c, sn);
+          if constexpr (!AQ) {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) add_angle(c[w], sn[w], rc[w], rs[w]);
+          }
         }
         float ka[8], kb2[8], x[8], z[8];
         if constexpr (FP8) {
@@ -612,6 +642,9 @@ void decode_kernel(DecodeArgs a, int parts) {
         pairs_of<IL>(ka, kb2, x, z);
 #pragma unroll
         for (int w = 0; w < 8; ++w) rot(x[w], z[w], c[w], sn[w]);
+        // TROW: the next round's rows go out once this round's are used
+        if constexpr (TROW)
+          if (t + 1 < t_end) load_trow(t + 1, (r + 1) & 1);
         float p[G];
         if constexpr (MF) {
           // The key's rotated row into the tile; then S = K Q^T for the
