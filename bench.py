@@ -65,13 +65,13 @@ MEASURED_TRAFFIC = {
         "fetch_kib": 1427001, "write_kib": 262182},
     "attn_bf16_pp_kernel_window": {"files": _PP, "sha256": "141d016353be8f28d00c408a954442f6e543fa7ac759020ac831322bee7703d8",
         "fetch_kib": 532525, "write_kib": 131082},
-    "decode_kernel": {"files": _DEC, "sha256": "d1ae78de6032f9ab0c99778156ea1ac477ccdc94d0348416166cb03a51e34598",
+    "decode_kernel": {"files": _DEC, "sha256": "0fde804d8eb30350beb5e885fc48e14b35e8afde00d371fbfbe708ecf865a16f",
         "fetch_kib": 2100179, "write_kib": 512},
-    "decode_kernel_fp8": {"files": _DEC, "sha256": "d1ae78de6032f9ab0c99778156ea1ac477ccdc94d0348416166cb03a51e34598",
+    "decode_kernel_fp8": {"files": _DEC, "sha256": "0fde804d8eb30350beb5e885fc48e14b35e8afde00d371fbfbe708ecf865a16f",
         "fetch_kib": 1050510, "write_kib": 512},
-    "decode_kernel_gqa": {"files": _DEC, "sha256": "d1ae78de6032f9ab0c99778156ea1ac477ccdc94d0348416166cb03a51e34598",
+    "decode_kernel_gqa": {"files": _DEC, "sha256": "0fde804d8eb30350beb5e885fc48e14b35e8afde00d371fbfbe708ecf865a16f",
         "fetch_kib": 526086, "write_kib": 1536},
-    "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": "d1ae78de6032f9ab0c99778156ea1ac477ccdc94d0348416166cb03a51e34598",
+    "decode_kernel_gqa_fp8": {"files": _DEC, "sha256": "0fde804d8eb30350beb5e885fc48e14b35e8afde00d371fbfbe708ecf865a16f",
         "fetch_kib": 264138, "write_kib": 2560},
     "attn_bf16_pp_kernel_ring": {"files": _PP, "sha256": "141d016353be8f28d00c408a954442f6e543fa7ac759020ac831322bee7703d8",  # per step of 8 launches
         "fetch_kib": 9391301, "write_kib": 1130850},
