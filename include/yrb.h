@@ -14,10 +14,13 @@
  *
  * Conventions shared by every call
  *  - Every device buffer is owned by the caller.  The library allocates no
- *    memory, never synchronises and keeps no mutable state between calls:
- *    calls may be made from any thread, and calls queued on different
- *    streams may run at the same time, as long as they do not write the
- *    same buffers.  A workspace (below) counts as a written buffer.
+ *    memory, never synchronises and keeps no mutable state between calls
+ *    (one exception, attn_prefill_blockwise_noalloc, keeps its work-claim
+ *    counter in a static per-GPU array; its declaration states the rule for
+ *    overlapping calls): calls may be made from any thread, and calls
+ *    queued on different streams may run at the same time, as long as they
+ *    do not write the same buffers.  A workspace (below) counts as a written
+ *    buffer.
  *  - Work is queued on `stream` (a hipStream_t; NULL = the default stream)
  *    and completes asynchronously.  A kernel fault surfaces at the caller's
  *    next synchronisation.
